@@ -1,0 +1,157 @@
+"""Seeded synthetic inputs for decode attention over a KV cache.
+
+This module holds the workload recipes only -- shapes, value distributions,
+length mixes and seeds -- and none of the attention arithmetic.  It is the one
+module both the GPU path's tests/bench and the CPU oracle's callers share.
+
+Workloads (shapes from the pages; the pages publish no dataset, so every
+tensor is drawn from a seeded generator):
+
+* ``tiny_mqa_f32``      -- fp32, B=1, Hq=8, Hkv=1, d=64; 128 cached tokens,
+  one new token appended, then attended (129 keys).
+* ``palm_mqa_bf16``     -- PaLM-540B-like multiquery layer: 48 query heads,
+  d_head 256, one KV head, context 2048 ("Efficiently Scaling Transformer
+  Inference", sections 3.3 and 4), batch 64.
+* ``llama13b_mha_bf16`` -- LLaMA-2-13B-like multi-head layer: 40 heads of
+  d 128, no sharing ("How to Parallelize a Transformer for Training", model
+  table), batch 32, context 4096.
+* ``ragged_gqa_bf16``   -- grouped-query with 8 KV heads ("All About
+  Transformer Inference", GQA paragraph), 64 query heads of d 128, batch 128,
+  per-sequence lengths uniform on [64, 8192] (continuous batching with ragged
+  reads), keys scaled by 3 to sharpen the softmax.
+* ``longctx_mqa_bf16``  -- 32x the 2048 context of the PaLM setting: B=8,
+  T=65536, 48 query heads over one KV head of d 256.
+
+Every draw is N(0, 1) in fp32, scaled where the recipe says so, then rounded
+once to the cache dtype (round-to-nearest-even via ``Tensor.to``).  Lengths
+are drawn on a CPU generator so they do not depend on the device.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+SEED_BASE = 20261202
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str            # "f32" or "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    T: int                # attended length after the step's append (max for ragged)
+    T_cap: int            # cache capacity
+    ragged: tuple = ()    # (lo, hi) inclusive range of attended lengths, or ()
+    k_scale: float = 1.0
+    seed_index: int = 0
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.seed_index
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def scale(self) -> float:
+        return float(self.D) ** -0.5
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny_mqa_f32", "f32", 1, 8, 1, 64, 129, 160, seed_index=0),
+        Workload("palm_mqa_bf16", "bf16", 64, 48, 1, 256, 2048, 2048, seed_index=1),
+        Workload("llama13b_mha_bf16", "bf16", 32, 40, 40, 128, 4096, 4096, seed_index=2),
+        Workload("ragged_gqa_bf16", "bf16", 128, 64, 8, 128, 8192, 8192, ragged=(64, 8192),
+                 k_scale=3.0, seed_index=3),
+        Workload("longctx_mqa_bf16", "bf16", 8, 48, 1, 256, 65536, 65536, seed_index=4),
+    ]
+}
+
+
+@dataclasses.dataclass
+class Case:
+    """One decode step's inputs.
+
+    lengths0 are the cached lengths BEFORE the step's append; after the
+    append every sequence holds lengths0 + 1 tokens (the attended lengths).
+    """
+    q: torch.Tensor          # [B, Hq, D]
+    k_cache: torch.Tensor    # [B, Hkv, T_cap, D]
+    v_cache: torch.Tensor    # [B, Hkv, T_cap, D]
+    lengths0: torch.Tensor   # [B] int32
+    k_new: torch.Tensor      # [B, Hkv, D]
+    v_new: torch.Tensor      # [B, Hkv, D]
+    scale: float
+
+
+def attended_lengths(w: Workload, B: Optional[int] = None) -> torch.Tensor:
+    """Per-sequence attended lengths (after the append), int32 on the CPU."""
+    B = w.B if B is None else B
+    if w.ragged:
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 7919)
+        lo, hi = w.ragged
+        return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    return torch.full((B,), w.T, dtype=torch.int32)
+
+
+def _normal(shape, gen, device, dtype, k=1.0, chunk_elems=1 << 28):
+    """N(0,1) draws in fp32, optionally scaled, rounded once to ``dtype``."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for s in range(0, n, chunk_elems):
+        e = min(n, s + chunk_elems)
+        x = torch.randn(e - s, generator=gen, device=device, dtype=torch.float32)
+        if k != 1.0:
+            x.mul_(k)
+        flat[s:e] = x.to(dtype)
+    return out
+
+
+def make_case(B, Hq, Hkv, D, T_cap, lengths_attended, dtype, seed, device="cpu",
+              k_scale=1.0) -> Case:
+    """Seeded case of arbitrary shape.  Cache rows at or beyond the attended
+    length are filled with draws too (they must never be read)."""
+    tdt = torch.float32 if dtype in ("f32", torch.float32) else torch.bfloat16
+    lengths_attended = torch.as_tensor(lengths_attended, dtype=torch.int32).cpu()
+    assert lengths_attended.shape == (B,)
+    assert int(lengths_attended.min()) >= 1 and int(lengths_attended.max()) <= T_cap
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    q = _normal((B, Hq, D), gen, device, tdt)
+    k_cache = _normal((B, Hkv, T_cap, D), gen, device, tdt, k=k_scale)
+    v_cache = _normal((B, Hkv, T_cap, D), gen, device, tdt)
+    k_new = _normal((B, Hkv, D), gen, device, tdt, k=k_scale)
+    v_new = _normal((B, Hkv, D), gen, device, tdt)
+    lengths0 = (lengths_attended - 1).to(torch.int32).to(device)
+    return Case(q, k_cache, v_cache, lengths0, k_new, v_new, float(D) ** -0.5)
+
+
+def make_workload_case(w: Workload, device="cpu", seed: Optional[int] = None,
+                       B: Optional[int] = None) -> Case:
+    """The named workload (optionally with a smaller batch for CPU tests)."""
+    B = w.B if B is None else B
+    return make_case(B, w.Hq, w.Hkv, w.D, w.T_cap, attended_lengths(w, B), w.dtype,
+                     w.seed if seed is None else seed, device, k_scale=w.k_scale)
+
+
+def bf16_bits(t: torch.Tensor):
+    """Raw bf16 bit patterns of a tensor as a numpy uint16 array (host)."""
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def host_array(t: torch.Tensor):
+    """Host numpy view in the encoding the oracle takes (float32 or bf16 bits)."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.detach().cpu().contiguous().numpy()
