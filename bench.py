@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is the whole hot path for one decode step of one attention layer:
+append every sequence's new K/V token to its cache, then attend every query
+head over its sequence's valid prefix (split-KV partial pass + log-sum-exp
+combine).  Inputs are seeded synthetic tensors resident in HBM before the
+timed region.  Several independent cache copies are cycled so that no step
+finds its cache in the 256 MB last-level cache (as in a model whose other
+layers' caches are read in between).
+
+Prints one JSON line:
+  value        step throughput in algorithmic GB/s (K/V of the valid prefixes
+               + q + out + the appended token), whole job
+  roofline     the partial-pass kernel's algorithmic GB/s (K/V + q per launch
+               / its mean launch time, HIP events on the launch stream)
+               against the 8 TB/s HBM peak
+  cpu_baseline the fp64 CPU oracle on one full step of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "longctx_mqa_bf16"
+MIN_ROTATION_BYTES = 2 << 30  # cycle >= 2 GiB of caches per round of steps
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "multiquery_decode_attention_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partial-pass launch from committed rocprofv3 counter
+    runs, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--splits", type=int, default=0, help="force split count (0 = plan)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--cache-copies", type=int, default=0, help="0 = enough for 2 GiB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import multiquery_decode_attention_amd as kvd
+    from multiquery_decode_attention_amd import inputs, traffic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kvd.library()  # fail loudly before any work if the HIP library is missing
+
+    w = inputs.WORKLOADS[args.workload]
+    K, W = args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kv_bytes_one = traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, [w.T_cap] * w.B)
+    R = args.cache_copies or max(1, math.ceil(MIN_ROTATION_BYTES / kv_bytes_one))
+    R = min(R, K + W)
+    appends_per_copy = math.ceil((K + W) / R)
+    T_cap = w.T_cap + appends_per_copy
+    attended = inputs.attended_lengths(w)  # lengths after the first step's append
+    log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T={w.T} dtype={w.dtype}; "
+        f"{R} cache copies of {kv_bytes_one / 1e6:.0f} MB, capacity {T_cap}")
+
+    variant = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU,
+               "mfma": kvd.KVD_VARIANT_MFMA}[args.variant]
+    copies = []
+    for r in range(R):
+        case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
+                                seed=w.seed + 1000 * r, device=dev, k_scale=w.k_scale)
+        cache = kvd.KVCache(case.k_cache, case.v_cache, case.lengths0, w.Hq)
+        cache.set_variant(variant)
+        cache.set_num_splits(args.splits)
+        copies.append({"case": case, "cache": cache, "out": torch.empty_like(case.q),
+                       "len": case.lengths0.cpu().tolist()})
+    plan = copies[0]["cache"].plan()
+    log(f"plan {plan}")
+    torch.cuda.synchronize()
+
+    def step(i):
+        c = copies[i % R]
+        c["cache"].append(c["case"].k_new, c["case"].v_new)
+        c["cache"].attend(c["case"].q, out=c["out"], scale=c["case"].scale)
+        c["len"] = [min(n + 1, T_cap) for n in c["len"]]
+        return c["len"]
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    for c in copies:
+        assert c["cache"].status() == kvd.KVD_OK
+        kvd.kvdecode_timing_enable(c["cache"].handle, K)
+    torch.cuda.synchronize()
+
+    step_bytes = 0
+    partial_bytes = 0
+    flops = 0
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        L = step(i)
+        step_bytes += traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L) + \
+            traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
+        partial_bytes += traffic.partial_pass_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L)
+        flops += traffic.attend_flops(w.Hq, w.D, L)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    tp = tc = ta = 0.0
+    n_att = 0
+    for c in copies:
+        t = kvd.kvdecode_timing_read(c["cache"].handle)
+        tp += t["partial_ms"]
+        tc += t["combine_ms"]
+        ta += t["append_ms"]
+        n_att += t["n_attend"]
+        assert c["cache"].status() == kvd.KVD_OK
+    assert n_att == K, (n_att, K)
+    partial_ms = tp / K
+    ms_per_step = elapsed * 1e3 / K
+    achieved = partial_bytes / K / (partial_ms * 1e-3) / 1e9
+    value = step_bytes / elapsed / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us; partial {partial_ms * 1e3:.1f} us, combine "
+        f"{tc / K * 1e3:.1f} us, append {ta / K * 1e3:.1f} us; partial {achieved:.0f} GB/s "
+        f"({achieved / traffic.MI355X_HBM_PEAK_GBPS:.1%} of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, copies[0], T_cap)
+
+    result = {
+        "metric": "decode-attention KV-cache HBM GB/s (% of peak) and tokens/sec at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) caches and queries)",
+        "pct_of_peak": round(value / traffic.MI355X_HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(w.B * K / elapsed, 1),
+        "kernel_us": {"partial": round(partial_ms * 1e3, 2), "combine": round(tc / K * 1e3, 2),
+                      "append": round(ta / K * 1e3, 2)},
+        "attend_tflops": round(flops / K / ((tp + tc) / K * 1e-3) / 1e12, 2),
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
+                   "T": w.T, "cache_dtype": w.dtype, "num_splits": plan["num_splits"],
+                   "split_tokens": plan["split_tokens"], "variant": plan["variant"],
+                   "cache_copies": R, "seed": w.seed},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name),
+                     "kernel": "partial_mfma_kernel" if plan["variant"] == "mfma" else "partial_valu_kernel"},
+        "cpu_baseline": cpu,
+    }
+    for c in copies:
+        c["cache"].close()
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, copy, T_cap):
+    """The fp64 oracle (test infrastructure) on one full step of the same
+    workload: the first copy's cache as it now stands, attended once."""
+    import numpy as np
+    import oracle
+    from multiquery_decode_attention_amd import inputs, traffic
+
+    case = copy["case"]
+    L = np.asarray(copy["len"], dtype=np.int32)
+    threads = oracle.default_threads()
+    log(f"cpu baseline: copying {w.name} cache to host, oracle on {threads} threads")
+    k = inputs.host_array(case.k_cache)
+    v = inputs.host_array(case.v_cache)
+    q = inputs.host_array(case.q)
+    dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+    t0 = time.perf_counter()
+    oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
+    sec = time.perf_counter() - t0
+    b = traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L.tolist())
+    log(f"cpu baseline: {sec:.2f} s for one step")
+    return {"value": round(b / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full attend step of {w.name} (B={w.B}, all {w.Hq} heads, "
+                      f"{int(L.sum())} cached tokens), fp64, {sec:.2f} s",
+            "tokens_per_s": round(w.B / sec, 2)}
+
+
+if __name__ == "__main__":
+    main()

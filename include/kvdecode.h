@@ -1,0 +1,181 @@
+/*
+ * kvdecode.h -- C ABI of a single-GPU decode-attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation: during generation every sequence contributes one new token.
+ * Its key and value projections are appended to the sequence's KV cache, and
+ * its query -- one vector per query head -- attends over every cached token of
+ * that sequence.  Many query heads share one key/value head (multiquery) or a
+ * few (grouped-query); multi-head attention is the case Hq == Hkv.
+ *
+ * Passages that define it:
+ *   - "All About Transformer Inference" (How To Scale Your Model, part 7),
+ *     section "Transformer inference basics": the KV cache stores every past
+ *     token's key/value projections; generation appends the new token's
+ *     projections and computes only the new query against the cached keys.
+ *   - same page, section "Implementation: JetStream": the engine interface
+ *     (prefill produces a cache, insert places it into the generate batch,
+ *     generate emits one token per batch item and appends the single-token
+ *     KV cache).  Prefill and insert are the caller writing the cache tensors
+ *     and lengths; this library provides the generate-side append and attend.
+ *   - same page, section "Continuous batching": a KV buffer sized for a
+ *     maximum batch and context length -- here [B, Hkv, T_cap, d] with a
+ *     per-sequence valid length.
+ *   - same page, section on tricks for generation throughput: ragged HBM
+ *     reads (read only the valid prefix of each sequence) and grouped-query
+ *     attention (Hkv KV heads, each shared by Hq/Hkv query heads).
+ *   - same page, section "Sharding the KV cache": the grouped contraction --
+ *     query heads reshaped row-major into [Hkv, M] groups, contracted with
+ *     the keys over the head dimension, softmaxed over the sequence, and
+ *     contracted with the values over the sequence -- and accumulating
+ *     attention across sequence shards the way Flash Attention does.
+ *   - "Efficiently Scaling Transformer Inference", section 3.3: multiquery
+ *     attention keeps n_heads query heads and a single key/value head
+ *     shared by all of them; during generation Q, K and V hold one token per
+ *     example while the cache holds many.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *     row-major, 16-byte aligned.  The library never frees them.  A handle
+ *     stores the cache and length pointers given at creation: the caller keeps
+ *     those allocations alive until kvdecode_destroy.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  append
+ *     and attend are asynchronous on it; host-side validation happens first
+ *     and a rejected call launches nothing.
+ *   - q, k_new, v_new, out and both caches share the handle's dtype: fp32
+ *     (KVD_F32) or bfloat16 (KVD_BF16).  Arithmetic is fp32 with fp32
+ *     accumulation; bf16 outputs are rounded to nearest even.
+ *   - Return values are KVD_OK (0) or a negative kvd_status_t code.
+ *   - Calls that share one handle must be serialised by the caller (same
+ *     stream, or ordered streams): attend uses the handle's workspace.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvdecode_s* kvdecode_t;
+
+enum { KVD_F32 = 0, KVD_BF16 = 1 };
+
+typedef enum {
+    KVD_OK = 0,
+    KVD_EINVAL = -1,       /* bad argument (null, non-positive size, Hq % Hkv != 0, bad scale, unknown handle) */
+    KVD_EUNSUPPORTED = -2, /* head_dim not in {64, 128, 256}, unknown dtype, or unknown variant */
+    KVD_EALIGN = -3,       /* a pointer is not 16-byte aligned */
+    KVD_ECAPACITY = -4,    /* (from kvdecode_status) an append found a sequence already at capacity */
+    KVD_EHIP = -5,         /* a HIP runtime call or kernel launch failed */
+    KVD_ENOMEM = -6,       /* host or device allocation failed */
+    KVD_ELENGTH = -7       /* (from kvdecode_status) attend found lengths[b] outside [0, capacity] */
+} kvd_status_t;
+
+/* Kernel variants for the partial pass (kvdecode_set_variant). */
+enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2 };
+
+typedef struct {
+    int32_t batch;        /* B  >= 1                                        */
+    int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads             */
+    int32_t num_kv_heads; /* Hkv >= 1; M = Hq / Hkv query heads per KV head  */
+    int32_t head_dim;     /* d in {64, 128, 256}                             */
+    int32_t capacity;     /* T_cap >= 1: cache slots per (sequence, KV head) */
+    int32_t dtype;        /* KVD_F32 or KVD_BF16                             */
+    void* k_cache;        /* [B, Hkv, T_cap, d] keys   (device)              */
+    void* v_cache;        /* [B, Hkv, T_cap, d] values (device)              */
+    int32_t* lengths;     /* [B] valid tokens per sequence (device int32),
+                             0 <= lengths[b] <= T_cap; slots >= lengths[b]
+                             are never read and may hold anything (NaN)    */
+} kvdecode_desc_t;
+
+/*
+ * Create a handle over caller-owned cache tensors.  Validates the
+ * descriptor (KVD_EINVAL / KVD_EUNSUPPORTED / KVD_EALIGN) and makes no HIP
+ * call: the device workspace (split partials, error flag) is allocated on
+ * the first append or attend, on the device current at that call, and that
+ * device is then bound to the handle.  Later calls never allocate unless
+ * kvdecode_set_num_splits asks for more splits than any earlier plan.
+ * Limits: B <= 65535, Hkv <= 65535, T_cap <= 2^24.
+ */
+int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out);
+
+/*
+ * Append one token per sequence (the generate-side cache update).
+ * k_new, v_new: [B, Hkv, d] device, handle dtype.  For each b with
+ * lengths[b] < T_cap: K[b,g,lengths[b],:] = k_new[b,g,:] and likewise V for
+ * every KV head g (a bit copy), then lengths[b] += 1.  A sequence already at
+ * capacity is left unchanged (no write, no increment) and sets the handle's
+ * sticky error, reported by kvdecode_status as KVD_ECAPACITY.
+ */
+int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void* stream);
+
+/*
+ * Attend the new query over each sequence's valid cache prefix.
+ * q: [B, Hq, d], out: [B, Hq, d] device, handle dtype; scale finite and > 0
+ * (callers normally pass 1/sqrt(d)).  For query head h of sequence b, with
+ * KV head g = floor(h / M) and n = lengths[b]:
+ *     out[b,h,:] = sum_{t<n} softmax_t(scale * q[b,h,:] . K[b,g,t,:]) V[b,g,t,:]
+ * and out[b,h,:] = 0 when n == 0.  Lengths are read on the device at run
+ * time (no host synchronisation); a length outside [0, T_cap] is clamped
+ * into range for memory safety and sets the sticky error KVD_ELENGTH.
+ * Internally: a split-KV partial pass over (sequence, KV head, split) work
+ * units, then a log-sum-exp combine of the splits.
+ */
+int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream);
+
+/*
+ * Synchronise `stream`, then report and clear the sticky device error:
+ * KVD_OK, KVD_ECAPACITY or KVD_ELENGTH (capacity is reported first when both
+ * occurred).  Returns KVD_OK without a device call if the handle has never
+ * touched a device.
+ */
+int32_t kvdecode_status(kvdecode_t h, void* stream);
+
+/*
+ * Force the split count of the attend pass (0 restores the automatic plan).
+ * n is clamped to [1, ceil(T_cap / tile)] where tile is the kernel's token
+ * tile.  Used to check that results do not depend on the split.
+ */
+int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n);
+
+/*
+ * Choose the partial-pass kernel: KVD_VARIANT_AUTO (MFMA for bf16, VALU for
+ * fp32), KVD_VARIANT_VALU (vector-ALU kernel, any dtype) or
+ * KVD_VARIANT_MFMA (bf16 only; KVD_EUNSUPPORTED for fp32).
+ */
+int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant);
+
+/*
+ * Report the current plan: variant in use, number of splits per
+ * (sequence, KV head) and tokens per split.  Any pointer may be NULL.
+ */
+int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
+                          int32_t* split_tokens);
+
+/*
+ * Kernel timing with HIP events recorded on the call's stream around the
+ * partial and combine launches of each attend (and the append kernel).
+ * kvdecode_timing_enable(h, n) allocates n event slots (n = 0 disables and
+ * frees them); at most n attends are timed before the slots are full.
+ * kvdecode_timing_read synchronises the recorded events, returns the summed
+ * durations in milliseconds and the number of timed attends and appends,
+ * and resets the slots.  Any output pointer may be NULL.
+ */
+int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls);
+int32_t kvdecode_timing_read(kvdecode_t h, double* partial_ms, double* combine_ms,
+                             double* append_ms, int32_t* n_attend, int32_t* n_append);
+
+/* Free the handle's workspace and events; never frees caller memory.
+ * Synchronises the device the handle is bound to first. */
+int32_t kvdecode_destroy(kvdecode_t h);
+
+/* Static description of a status code. */
+const char* kvdecode_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

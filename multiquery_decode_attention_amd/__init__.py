@@ -1,0 +1,255 @@
+"""Decode attention over a KV cache (multiquery / grouped-query) for MI355X.
+
+Thin ctypes binding of ``libkvdecode.so`` (C ABI in ``include/kvdecode.h``).
+The functions carry the C names and only marshal arguments: torch tensors
+become device pointers, the current torch stream becomes the HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is no
+CPU fallback, and every entry point raises ``KvdLibraryMissing`` when the
+built library cannot be loaded.
+
+    cache = KVCache(k_cache, v_cache, lengths, num_q_heads)
+    cache.append(k_new, v_new)      # write slot lengths[b], then lengths[b] += 1
+    out = cache.attend(q)           # softmax(q K^T * scale) V over each valid prefix
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
+    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
+    "KVD_VARIANT_MFMA", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
+    "kvdecode_append", "kvdecode_attend", "kvdecode_status", "kvdecode_set_num_splits",
+    "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
+    "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
+    "LIB_PATH",
+]
+
+KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
+KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH = -4, -5, -6, -7
+KVD_F32, KVD_BF16 = 0, 1
+KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA = 0, 1, 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
+
+EXPORTS = (
+    "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_status",
+    "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
+    "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
+)
+
+
+class KvdLibraryMissing(RuntimeError):
+    """The HIP library is not built (run ``__graft_entry__.build()``)."""
+
+
+class KvdError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {kvdecode_strerror(code)} (code {code})")
+
+
+class kvdecode_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("lengths", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load libkvdecode.so once; raise KvdLibraryMissing if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KvdLibraryMissing(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.POINTER(ctypes.c_double)
+    IP = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "kvdecode_create": (I, [ctypes.POINTER(kvdecode_desc_t), ctypes.POINTER(P)]),
+        "kvdecode_append": (I, [P, P, P, P]),
+        "kvdecode_attend": (I, [P, P, P, F, P]),
+        "kvdecode_status": (I, [P, P]),
+        "kvdecode_set_num_splits": (I, [P, I]),
+        "kvdecode_set_variant": (I, [P, I]),
+        "kvdecode_get_plan": (I, [P, IP, IP, IP]),
+        "kvdecode_timing_enable": (I, [P, I]),
+        "kvdecode_timing_read": (I, [P, D, D, D, IP, IP]),
+        "kvdecode_destroy": (I, [P]),
+        "kvdecode_strerror": (ctypes.c_char_p, [I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != KVD_OK:
+        raise KvdError(rc, where)
+    return rc
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+_DT = {torch.float32: KVD_F32, torch.bfloat16: KVD_BF16}
+
+
+# --- C-ABI mirrors -----------------------------------------------------------
+
+def kvdecode_strerror(code: int) -> str:
+    return library().kvdecode_strerror(code).decode()
+
+
+def kvdecode_create(k_cache: torch.Tensor, v_cache: torch.Tensor, lengths: torch.Tensor,
+                    num_q_heads: int) -> int:
+    """Handle over caller-owned caches [B, Hkv, T_cap, d] and lengths [B] int32."""
+    for t in (k_cache, v_cache):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("caches must be contiguous [B, Hkv, T_cap, d] tensors")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match in shape and dtype")
+    if k_cache.dtype not in _DT:
+        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or lengths.shape[0] != k_cache.shape[0]:
+        raise ValueError("lengths must be an int32 [B] tensor")
+    if not (k_cache.is_cuda and v_cache.is_cuda and lengths.is_cuda):
+        raise ValueError("caches and lengths must be device tensors")
+    B, Hkv, T_cap, D = k_cache.shape
+    desc = kvdecode_desc_t(B, num_q_heads, Hkv, D, T_cap, _DT[k_cache.dtype],
+                           k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr())
+    h = ctypes.c_void_p()
+    _check(library().kvdecode_create(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create")
+    return h.value
+
+
+def kvdecode_append(h: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    _check(library().kvdecode_append(h, _ptr(k_new), _ptr(v_new), _stream_ptr(stream)),
+           "kvdecode_append")
+
+
+def kvdecode_attend(h: int, q: torch.Tensor, out: torch.Tensor, scale: float, stream=None) -> None:
+    _check(library().kvdecode_attend(h, _ptr(q), _ptr(out), float(scale), _stream_ptr(stream)),
+           "kvdecode_attend")
+
+
+def kvdecode_status(h: int, stream=None) -> int:
+    """Sync the stream and return (and clear) the sticky device status code."""
+    return library().kvdecode_status(h, _stream_ptr(stream))
+
+
+def kvdecode_set_num_splits(h: int, n: int) -> None:
+    _check(library().kvdecode_set_num_splits(h, n), "kvdecode_set_num_splits")
+
+
+def kvdecode_set_variant(h: int, variant: int) -> None:
+    _check(library().kvdecode_set_variant(h, variant), "kvdecode_set_variant")
+
+
+def kvdecode_get_plan(h: int) -> dict:
+    v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(library().kvdecode_get_plan(h, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)),
+           "kvdecode_get_plan")
+    return {"variant": {1: "valu", 2: "mfma"}.get(v.value, str(v.value)),
+            "num_splits": s.value, "split_tokens": c.value}
+
+
+def kvdecode_timing_enable(h: int, max_calls: int) -> None:
+    _check(library().kvdecode_timing_enable(h, max_calls), "kvdecode_timing_enable")
+
+
+def kvdecode_timing_read(h: int) -> dict:
+    p, c, a = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    na, nb = ctypes.c_int32(), ctypes.c_int32()
+    _check(library().kvdecode_timing_read(h, ctypes.byref(p), ctypes.byref(c), ctypes.byref(a),
+                                          ctypes.byref(na), ctypes.byref(nb)),
+           "kvdecode_timing_read")
+    return {"partial_ms": p.value, "combine_ms": c.value, "append_ms": a.value,
+            "n_attend": na.value, "n_append": nb.value}
+
+
+def kvdecode_destroy(h: int) -> None:
+    _check(library().kvdecode_destroy(h), "kvdecode_destroy")
+
+
+# --- convenience object --------------------------------------------------------
+
+class KVCache:
+    """A decode-time KV cache: caller-owned tensors plus a library handle.
+
+    k_cache, v_cache: [B, Hkv, T_cap, d] (fp32 or bf16, on the GPU);
+    lengths: [B] int32 on the GPU (valid tokens per sequence).
+    The tensors must outlive the object; ``close()`` frees the handle.
+    """
+
+    def __init__(self, k_cache, v_cache, lengths, num_q_heads: int):
+        self.k_cache, self.v_cache, self.lengths = k_cache, v_cache, lengths
+        self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
+        self.Hq = num_q_heads
+        self.dtype = k_cache.dtype
+        self.handle = kvdecode_create(k_cache, v_cache, lengths, num_q_heads)
+
+    def _check_token(self, t, heads, name):
+        if t.shape != (self.B, heads, self.D) or t.dtype != self.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{self.B}, {heads}, {self.D}] "
+                             f"{self.dtype} tensor, got {tuple(t.shape)} {t.dtype}")
+        if t.device != self.k_cache.device:
+            raise ValueError(f"{name} is on {t.device}, the cache on {self.k_cache.device}")
+
+    def append(self, k_new, v_new, stream=None):
+        self._check_token(k_new, self.Hkv, "k_new")
+        self._check_token(v_new, self.Hkv, "v_new")
+        kvdecode_append(self.handle, k_new, v_new, stream)
+
+    def attend(self, q, out=None, scale=None, stream=None):
+        self._check_token(q, self.Hq, "q")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            self._check_token(out, self.Hq, "out")
+        kvdecode_attend(self.handle, q, out, self.D ** -0.5 if scale is None else scale, stream)
+        return out
+
+    def status(self, stream=None) -> int:
+        return kvdecode_status(self.handle, stream)
+
+    def set_num_splits(self, n: int):
+        kvdecode_set_num_splits(self.handle, n)
+
+    def set_variant(self, variant: int):
+        kvdecode_set_variant(self.handle, variant)
+
+    def plan(self) -> dict:
+        return kvdecode_get_plan(self.handle)
+
+    def close(self):
+        if self.handle is not None:
+            kvdecode_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

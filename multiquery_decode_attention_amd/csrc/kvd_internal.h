@@ -1,0 +1,58 @@
+// kvd_internal.h -- launchers and shared constants of the decode-attention
+// library (internal; the public ABI is include/kvdecode.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvd {
+
+// Sticky device error bits, OR-ed into the handle's flag word.
+constexpr int ERRBIT_CAPACITY = 1;  // append found lengths[b] == T_cap
+constexpr int ERRBIT_LENGTH = 2;    // a kernel saw lengths[b] outside [0, T_cap]
+
+// Tokens per inner iteration of each partial-pass kernel.
+constexpr int MFMA_TILE = 32;
+constexpr int VALU_TILE = 64;
+
+// Query heads per MFMA head block (rows of the 16x16 output tile).
+constexpr int MFMA_HEADS = 16;
+
+// log2(e): softmax is evaluated as 2^(x*log2(e) - m) with the score scale
+// folded into one fp32 multiplier.
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct PartialArgs {
+    const void* q;          // [B, Hq, D]
+    const void* k_cache;    // [B, Hkv, T_cap, D]
+    const void* v_cache;    // [B, Hkv, T_cap, D]
+    const int32_t* lengths; // [B]
+    float* o_part;          // [B, Hq, S, D] normalised partial outputs
+    float* lse_part;        // [B, Hq, S]    base-2 log-sum-exp of each split
+    int* err;               // sticky error word
+    int B, Hq, Hkv, M, D, T_cap;
+    int chunk;              // tokens per split (multiple of the kernel tile)
+    int S;                  // splits per (sequence, KV head)
+    float scale_log2e;      // scale * log2(e)
+};
+
+struct CombineArgs {
+    const float* o_part;
+    const float* lse_part;
+    const int32_t* lengths;
+    void* out;              // [B, Hq, D]
+    int B, Hq, D, T_cap, chunk, S;
+};
+
+// Each launcher returns the hipError_t of its launch.
+hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         int32_t* lengths, int* err, int B, int Hkv, int D, int T_cap,
+                         int elem_bytes, hipStream_t stream);
+hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
+
+// Waves per work unit of the MFMA partial pass for group size M.
+inline int mfma_head_blocks(int M) { return (M + MFMA_HEADS - 1) / MFMA_HEADS; }
+
+}  // namespace kvd

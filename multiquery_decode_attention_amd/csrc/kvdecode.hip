@@ -1,0 +1,393 @@
+// kvdecode.hip -- host side of the C ABI declared in include/kvdecode.h:
+// handle lifetime, argument validation, split planning, workspace and
+// kernel launches.  No torch types cross this boundary.
+#include "../../include/kvdecode.h"
+
+#include <math.h>
+#include <stdlib.h>
+
+#include <mutex>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "kvd_internal.h"
+
+struct kvdecode_s {
+    kvdecode_desc_t d;
+    int M = 1;
+    int elem = 4;
+    int variant_req = KVD_VARIANT_AUTO;
+    int forced_splits = 0;
+
+    // Device resources (allocated on first use, on the then-current device).
+    int device = -1;
+    int* err = nullptr;
+    float* o_part = nullptr;
+    float* lse_part = nullptr;
+    int ws_splits = 0;
+
+    // Event timing.
+    int timing_cap = 0;
+    std::vector<hipEvent_t> ev_attend;  // 3 per timed attend
+    std::vector<hipEvent_t> ev_append;  // 2 per timed append
+    int n_attend = 0, n_append = 0;
+};
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_set<kvdecode_s*>& live() {
+    static std::unordered_set<kvdecode_s*> s;
+    return s;
+}
+
+bool is_live(kvdecode_s* h) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return h && live().count(h);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+    int variant;
+    int tile;
+    int splits;
+    int chunk;
+};
+
+int resolve_variant(const kvdecode_s* h) {
+    if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
+    return h->d.dtype == KVD_BF16 ? KVD_VARIANT_MFMA : KVD_VARIANT_VALU;
+}
+
+// Split planner.  The grid is (splits, KV heads, sequences); lengths live on
+// the device, so the plan is made from the capacity and splits past a
+// sequence's length exit at once.  Automatic plans aim for about 32 waves
+// per compute unit on 256 CUs when every sequence is full, and keep each
+// split long enough that the fp32 partials stay a few percent of the
+// K/V bytes the split reads (partial bytes ~ M*4 per column, K/V bytes ~
+// chunk*2*elem per column).
+Plan make_plan(const kvdecode_s* h) {
+    Plan p;
+    p.variant = resolve_variant(h);
+    p.tile = p.variant == KVD_VARIANT_MFMA ? kvd::MFMA_TILE : kvd::VALU_TILE;
+    const long long T = h->d.capacity;
+    const int max_splits = (int)((T + p.tile - 1) / p.tile);
+    int s;
+    if (h->forced_splits > 0) {
+        s = h->forced_splits;
+    } else {
+        const long long waves_per_split =
+            (long long)h->d.batch * h->d.num_kv_heads *
+            (p.variant == KVD_VARIANT_MFMA ? kvd::mfma_head_blocks(h->M) : h->M);
+        const long long target_waves = 8192;
+        s = (int)((target_waves + waves_per_split - 1) / waves_per_split);
+        // keep the partials small next to the K/V bytes of a split
+        long long min_chunk = 32LL * h->M;
+        if (min_chunk < 256) min_chunk = 256;
+        const int s_cap = (int)((T + min_chunk - 1) / min_chunk);
+        if (s > s_cap) s = s_cap;
+    }
+    if (s < 1) s = 1;
+    if (s > max_splits) s = max_splits;
+    long long chunk = (T + s - 1) / s;
+    chunk = (chunk + p.tile - 1) / p.tile * p.tile;
+    p.chunk = (int)chunk;
+    p.splits = (int)((T + chunk - 1) / chunk);
+    return p;
+}
+
+int32_t hip_fail(hipError_t e) { return e == hipErrorOutOfMemory ? KVD_ENOMEM : KVD_EHIP; }
+
+// Bind the handle to the current device on first use; later calls must run
+// with the same device current.
+int32_t ensure_device(kvdecode_s* h) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (h->device >= 0) return dev == h->device ? KVD_OK : KVD_EINVAL;
+    e = hipMalloc(reinterpret_cast<void**>(&h->err), sizeof(int));
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMemset(h->err, 0, sizeof(int));
+    if (e != hipSuccess) {
+        (void)hipFree(h->err);
+        h->err = nullptr;
+        return KVD_EHIP;
+    }
+    h->device = dev;
+    return KVD_OK;
+}
+
+int32_t ensure_workspace(kvdecode_s* h, int splits) {
+    if (splits <= h->ws_splits) return KVD_OK;
+    if (h->o_part) (void)hipFree(h->o_part);
+    if (h->lse_part) (void)hipFree(h->lse_part);
+    h->o_part = nullptr;
+    h->lse_part = nullptr;
+    h->ws_splits = 0;
+    const size_t rows = (size_t)h->d.batch * h->d.num_q_heads * (size_t)splits;
+    hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->o_part), rows * h->d.head_dim * sizeof(float));
+    if (e != hipSuccess) return hip_fail(e);
+    e = hipMalloc(reinterpret_cast<void**>(&h->lse_part), rows * sizeof(float));
+    if (e != hipSuccess) {
+        (void)hipFree(h->o_part);
+        h->o_part = nullptr;
+        return hip_fail(e);
+    }
+    h->ws_splits = splits;
+    return KVD_OK;
+}
+
+void free_events(kvdecode_s* h) {
+    for (hipEvent_t ev : h->ev_attend) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : h->ev_append) (void)hipEventDestroy(ev);
+    h->ev_attend.clear();
+    h->ev_append.clear();
+    h->n_attend = h->n_append = 0;
+}
+
+int32_t ensure_events(kvdecode_s* h) {
+    if (h->timing_cap <= 0 || !h->ev_attend.empty()) return KVD_OK;
+    h->ev_attend.resize(3 * (size_t)h->timing_cap, nullptr);
+    h->ev_append.resize(2 * (size_t)h->timing_cap, nullptr);
+    for (auto* vec : {&h->ev_attend, &h->ev_append}) {
+        for (hipEvent_t& ev : *vec) {
+            if (hipEventCreate(&ev) != hipSuccess) {
+                ev = nullptr;
+                free_events(h);
+                return KVD_EHIP;
+            }
+        }
+    }
+    return KVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvdecode_strerror(int32_t code) {
+    switch (code) {
+        case KVD_OK: return "success";
+        case KVD_EINVAL: return "invalid argument";
+        case KVD_EUNSUPPORTED: return "unsupported head_dim, dtype or variant";
+        case KVD_EALIGN: return "pointer not 16-byte aligned";
+        case KVD_ECAPACITY: return "append on a sequence already at cache capacity";
+        case KVD_EHIP: return "HIP runtime error";
+        case KVD_ENOMEM: return "out of memory";
+        case KVD_ELENGTH: return "sequence length outside [0, capacity]";
+        default: return "unknown status code";
+    }
+}
+
+int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    *out = nullptr;
+    const kvdecode_desc_t& d = *desc;
+    if (d.batch < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.capacity < 1) return KVD_EINVAL;
+    if (d.batch > 65535 || d.num_kv_heads > 65535 || d.num_q_heads > 65535) return KVD_EINVAL;
+    if (d.capacity > (1 << 24)) return KVD_EINVAL;
+    if (d.num_q_heads % d.num_kv_heads != 0) return KVD_EINVAL;
+    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return KVD_EUNSUPPORTED;
+    if (d.dtype != KVD_F32 && d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    if (!d.k_cache || !d.v_cache || !d.lengths) return KVD_EINVAL;
+    if (!aligned16(d.k_cache) || !aligned16(d.v_cache) ||
+        (reinterpret_cast<uintptr_t>(d.lengths) & 3u))
+        return KVD_EALIGN;
+    kvdecode_s* h = new (std::nothrow) kvdecode_s();
+    if (!h) return KVD_ENOMEM;
+    h->d = d;
+    h->M = d.num_q_heads / d.num_kv_heads;
+    h->elem = d.dtype == KVD_F32 ? 4 : 2;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        live().insert(h);
+    }
+    *out = h;
+    return KVD_OK;
+}
+
+int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (!k_new || !v_new) return KVD_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_EALIGN;
+    int32_t rc = ensure_device(h);
+    if (rc != KVD_OK) return rc;
+    if ((rc = ensure_events(h)) != KVD_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
+    if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
+    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->d.lengths, h->err,
+                                      h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
+                                      h->elem, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed) {
+        if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
+        ++h->n_append;
+    }
+    return KVD_OK;
+}
+
+int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (!q || !out) return KVD_EINVAL;
+    if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
+    const Plan p = make_plan(h);
+    if (p.variant == KVD_VARIANT_MFMA && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    int32_t rc = ensure_device(h);
+    if (rc != KVD_OK) return rc;
+    if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
+    if ((rc = ensure_events(h)) != KVD_OK) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    kvd::PartialArgs a;
+    a.q = q;
+    a.k_cache = h->d.k_cache;
+    a.v_cache = h->d.v_cache;
+    a.lengths = h->d.lengths;
+    a.o_part = h->o_part;
+    a.lse_part = h->lse_part;
+    a.err = h->err;
+    a.B = h->d.batch;
+    a.Hq = h->d.num_q_heads;
+    a.Hkv = h->d.num_kv_heads;
+    a.M = h->M;
+    a.D = h->d.head_dim;
+    a.T_cap = h->d.capacity;
+    a.chunk = p.chunk;
+    a.S = p.splits;
+    a.scale_log2e = scale * kvd::LOG2E;
+
+    kvd::CombineArgs c;
+    c.o_part = h->o_part;
+    c.lse_part = h->lse_part;
+    c.lengths = h->d.lengths;
+    c.out = out;
+    c.B = a.B;
+    c.Hq = a.Hq;
+    c.D = a.D;
+    c.T_cap = a.T_cap;
+    c.chunk = p.chunk;
+    c.S = p.splits;
+
+    const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
+    hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
+    if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
+    hipError_t e = p.variant == KVD_VARIANT_MFMA
+                       ? kvd::launch_partial_mfma(a, st)
+                       : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
+    e = kvd::launch_combine(c, h->d.dtype == KVD_BF16, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed) {
+        if (hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
+        ++h->n_attend;
+    }
+    return KVD_OK;
+}
+
+int32_t kvdecode_status(kvdecode_t h, void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (h->device < 0) return KVD_OK;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return KVD_EINVAL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int flag = 0;
+    if (hipMemcpyAsync(&flag, h->err, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess)
+        return KVD_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
+    if (flag) {
+        if (hipMemsetAsync(h->err, 0, sizeof(int), st) != hipSuccess) return KVD_EHIP;
+        if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
+    }
+    if (flag & kvd::ERRBIT_CAPACITY) return KVD_ECAPACITY;
+    if (flag & kvd::ERRBIT_LENGTH) return KVD_ELENGTH;
+    return KVD_OK;
+}
+
+int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
+    if (!is_live(h) || n < 0) return KVD_EINVAL;
+    h->forced_splits = n;
+    return KVD_OK;
+}
+
+int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (variant != KVD_VARIANT_AUTO && variant != KVD_VARIANT_VALU && variant != KVD_VARIANT_MFMA)
+        return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_MFMA && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    h->variant_req = variant;
+    return KVD_OK;
+}
+
+int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits, int32_t* split_tokens) {
+    if (!is_live(h)) return KVD_EINVAL;
+    const Plan p = make_plan(h);
+    if (variant) *variant = p.variant;
+    if (num_splits) *num_splits = p.splits;
+    if (split_tokens) *split_tokens = p.chunk;
+    return KVD_OK;
+}
+
+int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls) {
+    if (!is_live(h) || max_calls < 0) return KVD_EINVAL;
+    free_events(h);
+    h->timing_cap = max_calls;
+    if (h->device >= 0) return ensure_events(h);
+    return KVD_OK;
+}
+
+int32_t kvdecode_timing_read(kvdecode_t h, double* partial_ms, double* combine_ms, double* append_ms,
+                             int32_t* n_attend, int32_t* n_append) {
+    if (!is_live(h)) return KVD_EINVAL;
+    double tp = 0, tc = 0, ta = 0;
+    for (int i = 0; i < h->n_attend; ++i) {
+        float a = 0, b = 0;
+        if (hipEventSynchronize(h->ev_attend[3 * i + 2]) != hipSuccess) return KVD_EHIP;
+        if (hipEventElapsedTime(&a, h->ev_attend[3 * i], h->ev_attend[3 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&b, h->ev_attend[3 * i + 1], h->ev_attend[3 * i + 2]) != hipSuccess)
+            return KVD_EHIP;
+        tp += a;
+        tc += b;
+    }
+    for (int i = 0; i < h->n_append; ++i) {
+        float a = 0;
+        if (hipEventSynchronize(h->ev_append[2 * i + 1]) != hipSuccess) return KVD_EHIP;
+        if (hipEventElapsedTime(&a, h->ev_append[2 * i], h->ev_append[2 * i + 1]) != hipSuccess)
+            return KVD_EHIP;
+        ta += a;
+    }
+    if (partial_ms) *partial_ms = tp;
+    if (combine_ms) *combine_ms = tc;
+    if (append_ms) *append_ms = ta;
+    if (n_attend) *n_attend = h->n_attend;
+    if (n_append) *n_append = h->n_append;
+    h->n_attend = h->n_append = 0;
+    return KVD_OK;
+}
+
+int32_t kvdecode_destroy(kvdecode_t h) {
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!h || !live().count(h)) return KVD_EINVAL;
+        live().erase(h);
+    }
+    if (h->device >= 0) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        if (cur != h->device) (void)hipSetDevice(h->device);
+        (void)hipDeviceSynchronize();
+        free_events(h);
+        if (h->o_part) (void)hipFree(h->o_part);
+        if (h->lse_part) (void)hipFree(h->lse_part);
+        if (h->err) (void)hipFree(h->err);
+        if (cur >= 0 && cur != h->device) (void)hipSetDevice(cur);
+    }
+    delete h;
+    return KVD_OK;
+}
+
+}  // extern "C"

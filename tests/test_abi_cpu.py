@@ -1,0 +1,161 @@
+"""The C ABI on a host without a GPU: the library loads, exports every
+symbol the header declares, and validates arguments before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import multiquery_decode_attention_amd as kvd
+from multiquery_decode_attention_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvdecode.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvd.library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(kvdecode_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    fns = header_functions()
+    assert set(kvd.EXPORTS) == set(fns), fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kvd.LIB_PATH], capture_output=True, text=True)
+    for name in header_functions():
+        assert re.search(rf"\bT {name}$", out.stdout, re.M), name
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -8, -1):
+        assert kvd.kvdecode_strerror(code) != "unknown status code"
+    assert kvd.kvdecode_strerror(-99) == "unknown status code"
+
+
+FAKE = 0x10000  # aligned address that is never dereferenced by create()
+
+
+def make_desc(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, capacity=64, dtype=kvd.KVD_BF16,
+             k_cache=FAKE, v_cache=FAKE * 2, lengths=FAKE * 3)
+    d.update(kw)
+    return kvd.kvdecode_desc_t(**d)
+
+
+def create(lib, desc):
+    h = ctypes.c_void_p()
+    rc = lib.kvdecode_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h.value
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", 0, kvd.KVD_EINVAL), ("batch", -3, kvd.KVD_EINVAL), ("batch", 70000, kvd.KVD_EINVAL),
+    ("num_q_heads", 0, kvd.KVD_EINVAL), ("num_kv_heads", 0, kvd.KVD_EINVAL),
+    ("num_q_heads", 9, kvd.KVD_EINVAL),  # not a multiple of num_kv_heads
+    ("capacity", 0, kvd.KVD_EINVAL), ("capacity", (1 << 24) + 1, kvd.KVD_EINVAL),
+    ("head_dim", 96, kvd.KVD_EUNSUPPORTED), ("head_dim", 512, kvd.KVD_EUNSUPPORTED),
+    ("dtype", 7, kvd.KVD_EUNSUPPORTED),
+    ("k_cache", 0, kvd.KVD_EINVAL), ("v_cache", 0, kvd.KVD_EINVAL), ("lengths", 0, kvd.KVD_EINVAL),
+    ("k_cache", FAKE + 8, kvd.KVD_EALIGN), ("v_cache", FAKE + 2, kvd.KVD_EALIGN),
+    ("lengths", FAKE + 2, kvd.KVD_EALIGN),
+])
+def test_create_rejects(lib, field, value, code):
+    rc, h = create(lib, make_desc(**{field: value}))
+    assert rc == code and not h
+
+
+def test_create_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.kvdecode_create(None, ctypes.byref(h)) == kvd.KVD_EINVAL
+    assert lib.kvdecode_create(ctypes.byref(make_desc()), None) == kvd.KVD_EINVAL
+
+
+def test_handle_calls_validate_before_any_device_work(lib):
+    rc, h = create(lib, make_desc())
+    assert rc == kvd.KVD_OK and h
+    # never touched a device: status is OK without a device call
+    assert lib.kvdecode_status(h, None) == kvd.KVD_OK
+    # attend argument checks (no launch happens on rejection)
+    assert lib.kvdecode_attend(h, None, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_attend(h, FAKE, None, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_attend(h, FAKE + 4, FAKE, 1.0, None) == kvd.KVD_EALIGN
+    assert lib.kvdecode_attend(h, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.kvdecode_attend(h, FAKE, FAKE, bad, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append(h, None, FAKE, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append(h, FAKE, FAKE + 8, None) == kvd.KVD_EALIGN
+    # knobs
+    assert lib.kvdecode_set_num_splits(h, -1) == kvd.KVD_EINVAL
+    assert lib.kvdecode_set_variant(h, 9) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_VALU) == kvd.KVD_OK
+    assert lib.kvdecode_timing_enable(h, -1) == kvd.KVD_EINVAL
+    assert lib.kvdecode_timing_enable(h, 4) == kvd.KVD_OK
+    assert lib.kvdecode_timing_enable(h, 0) == kvd.KVD_OK
+    assert lib.kvdecode_destroy(h) == kvd.KVD_OK
+    # a destroyed handle is unknown to every call
+    assert lib.kvdecode_destroy(h) == kvd.KVD_EINVAL
+    assert lib.kvdecode_attend(h, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_status(h, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_destroy(None) == kvd.KVD_EINVAL
+
+
+def test_mfma_variant_needs_bf16(lib):
+    rc, h = create(lib, make_desc(dtype=kvd.KVD_F32))
+    assert rc == kvd.KVD_OK
+    assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_MFMA) == kvd.KVD_EUNSUPPORTED
+    assert kvd.kvdecode_get_plan(h)["variant"] == "valu"
+    lib.kvdecode_destroy(h)
+
+
+def plan_of(lib, **kw):
+    rc, h = create(lib, make_desc(**kw))
+    assert rc == kvd.KVD_OK
+    try:
+        return kvd.kvdecode_get_plan(h), h
+    finally:
+        pass
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_plans_cover_the_cache(lib, name):
+    w = inputs.WORKLOADS[name]
+    dt = kvd.KVD_F32 if w.dtype == "f32" else kvd.KVD_BF16
+    for forced in (0, 1, 2, 7, 10**6):
+        rc, h = create(lib, make_desc(batch=w.B, num_q_heads=w.Hq, num_kv_heads=w.Hkv, head_dim=w.D,
+                                      capacity=w.T_cap, dtype=dt))
+        assert rc == kvd.KVD_OK
+        kvd.kvdecode_set_num_splits(h, forced)
+        p = kvd.kvdecode_get_plan(h)
+        tile = 32 if p["variant"] == "mfma" else 64
+        S, C = p["num_splits"], p["split_tokens"]
+        assert C % tile == 0 and S >= 1
+        assert S * C >= w.T_cap and (S - 1) * C < w.T_cap
+        if forced:
+            assert S <= forced or S == 1
+        lib.kvdecode_destroy(h)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    code = (
+        "import multiquery_decode_attention_amd as k\n"
+        f"k.LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+        "k._lib = None\n"
+        "try:\n"
+        "    k.library()\n"
+        "except k.KvdLibraryMissing:\n"
+        "    print('missing-raised')\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "missing-raised" in r.stdout, r.stderr

@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every workload runs at full size (the launch configuration the benchmark
+times, automatic split plan) and is compared element by element with the
+fp64 oracle on the same bytes; reduced-batch variants, forced split counts,
+both partial-pass kernels and the degenerate cases run at sizes that still
+span several tiles and a ragged tail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import multiquery_decode_attention_amd as kvd
+from multiquery_decode_attention_amd import inputs
+from conftest import TOL_BF16, TOL_F32, rel_err_rows
+from gpu_helpers import gpu_step, oracle_step, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def tol_for(case):
+    return TOL_BF16 if case.q.dtype == torch.bfloat16 else TOL_F32
+
+
+def check_case(case, Hq, name, **kw):
+    say(f"{name}: B={case.q.shape[0]} Hq={Hq} Hkv={case.k_cache.shape[1]} "
+        f"T_cap={case.k_cache.shape[2]} D={case.q.shape[2]} dtype={case.q.dtype} {kw}")
+    out, kc, vc, L, status, plan = gpu_step(case, Hq, **kw)
+    say(f"{name}: gpu done, plan={plan}, status={status}")
+    ref, k2, v2, L2 = oracle_step(case, lengths=kw.get("lengths"))
+    assert status == kvd.KVD_OK
+    # append: bit-exact on the whole cache and on the lengths
+    assert np.array_equal(L.cpu().numpy(), L2)
+    assert np.array_equal(inputs.host_array(kc), k2), "K cache differs after append"
+    assert np.array_equal(inputs.host_array(vc), v2), "V cache differs after append"
+    err = rel_err_rows(to_f64(out), ref)
+    say(f"{name}: max row-relative error {err:.3e} (tol {tol_for(case):.0e})")
+    assert err <= tol_for(case), err
+    return out, ref, plan
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_workload_full_size(name):
+    """Each named workload at its full size, all outputs checked."""
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_workload_case(w, device="cuda")
+    check_case(case, w.Hq, name)
+
+
+@pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 3), ("llama13b_mha_bf16", 2),
+                                    ("ragged_gqa_bf16", 6), ("tiny_mqa_f32", 1)])
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_split_invariance(name, B, splits):
+    """Any split count gives the oracle's answer (the LSE merge is exact
+    algebra; only rounding order changes)."""
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_workload_case(w, device="cpu", B=B)
+    check_case(case, w.Hq, f"{name}/splits={splits}", splits=splits)
+
+
+@pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 2), ("ragged_gqa_bf16", 4),
+                                    ("llama13b_mha_bf16", 1)])
+def test_valu_kernel_bf16(name, B):
+    """The vector-ALU kernel as an independent second GPU path in bf16."""
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_workload_case(w, device="cpu", B=B)
+    check_case(case, w.Hq, f"{name}/valu", variant=kvd.KVD_VARIANT_VALU)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv,D", [(48, 1, 256), (8, 1, 64), (64, 8, 128), (12, 4, 128),
+                                      (80, 1, 128), (16, 16, 64), (17, 1, 256)])
+def test_shapes_and_ragged_lengths(dtype, Hq, Hkv, D):
+    """Group sizes 1..80 (one to five 16-head blocks, padded ones too),
+    every head dim, and lengths hitting 0, 1, tile edges and capacity."""
+    T_cap = 300
+    lengths = [1, 2, 31, 32, 33, 64, 65, 257, 300]  # attended lengths (after append)
+    B = len(lengths)
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, lengths, dtype, seed=Hq * 1000 + D, device="cpu")
+    check_case(case, Hq, f"shape Hq={Hq} Hkv={Hkv} D={D} {dtype}")
+
+
+def test_empty_sequences_and_poisoned_tails():
+    """len 0 gives a zero row; slots past the length hold NaN/Inf and must
+    never reach the output."""
+    B, Hq, Hkv, D, T_cap = 5, 48, 1, 256, 200
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, [1, 1, 50, 199, 200], "bf16", seed=7)
+    L0 = torch.tensor([0, 0, 49, 198, 199], dtype=torch.int32)
+    for b, n in enumerate(L0.tolist()):
+        case.k_cache[b, :, n + 1:] = float("nan")
+        case.v_cache[b, :, n + 1:] = float("inf")
+    # sequences 0 and 1: attend without appending -> one empty, checked below
+    out, _, _, L, status, _ = gpu_step(case, Hq, append=False, lengths=L0)
+    assert status == kvd.KVD_OK
+    ref, _, _, _ = oracle_step(case, append=False, lengths=L0)
+    o = to_f64(out)
+    assert np.all(o[0] == 0) and np.all(o[1] == 0)
+    assert rel_err_rows(o, ref) <= TOL_BF16
+    # with the append every sequence is non-empty
+    check_case(case, Hq, "poisoned tails + append", lengths=L0)
+
+
+def test_capacity_overflow_reported_and_harmless():
+    B, Hq, Hkv, D, T_cap = 3, 8, 2, 128, 64
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, [64, 64, 10], "bf16", seed=9)
+    L0 = torch.tensor([64, 63, 9], dtype=torch.int32)  # sequence 0 is already full
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L0)
+    assert status == kvd.KVD_ECAPACITY
+    assert L.cpu().tolist() == [64, 64, 10]
+    ref, k2, v2, L2 = oracle_step(case, lengths=L0)
+    assert L2.tolist() == [64, 64, 10]
+    assert np.array_equal(inputs.host_array(kc), k2) and np.array_equal(inputs.host_array(vc), v2)
+    assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
+
+
+def test_length_out_of_range_is_clamped_and_reported():
+    B, Hq, Hkv, D, T_cap = 2, 16, 1, 128, 96
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, [96, 40], "bf16", seed=10)
+    L_bad = torch.tensor([1000, 40], dtype=torch.int32)
+    out, _, _, _, status, _ = gpu_step(case, Hq, append=False, lengths=L_bad)
+    assert status == kvd.KVD_ELENGTH
+    ref, _, _, _ = oracle_step(case, append=False, lengths=torch.tensor([96, 40], dtype=torch.int32))
+    assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hand_worked_cases_on_gpu(dtype):
+    """The exact hand-worked fixtures, zero-padded from d=2/4 to d=64 (zero
+    columns change no dot product and give zero output columns)."""
+    import json
+    from fractions import Fraction
+    from oracle_pins import GOLDEN
+    for c in json.load(open(GOLDEN))["cases"]:
+        B, Hq, Hkv, d, T = c["B"], c["Hq"], c["Hkv"], c["D"], c["T_cap"]
+        D = 64
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        def pad(x, shape):
+            z = torch.zeros(shape, dtype=torch.float32)
+            z[..., :d] = torch.tensor(x, dtype=torch.float32)
+            return z.to(tdt)
+        q = pad(c["q"], (B, Hq, D))
+        k = pad(c["k"], (B, Hkv, T, D))
+        v = pad(c["v"], (B, Hkv, T, D))
+        L = torch.tensor(c["lengths"], dtype=torch.int32)
+        if c.get("poison_tail"):
+            for b, n in enumerate(L.tolist()):
+                k[b, :, n:] = float("nan")
+                v[b, :, n:] = float("nan")
+        scale = eval(c["scale_expr"], {"log": math.log})  # noqa: S307 (fixture-owned)
+        case = inputs.Case(q, k, v, L, torch.zeros(B, Hkv, D, dtype=tdt),
+                           torch.zeros(B, Hkv, D, dtype=tdt), scale)
+        for variant in ([kvd.KVD_VARIANT_VALU] + ([kvd.KVD_VARIANT_MFMA] if dtype == "bf16" else [])):
+            out, _, _, _, status, _ = gpu_step(case, Hq, append=False, variant=variant)
+            assert status == kvd.KVD_OK
+            got = to_f64(out)[..., :d]
+            want = np.array([[[float(Fraction(x)) for x in r] for r in hb] for hb in c["out"]])
+            tol = TOL_F32 if dtype == "f32" else TOL_BF16
+            assert rel_err_rows(got, want) <= tol, (c["id"], variant, got, want)
+            assert np.all(to_f64(out)[..., d:] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cached_decode_equals_naive_recompute(dtype):
+    """Start from an empty cache; at every step append the token's K/V and
+    attend its query.  Row i must equal full causal attention recomputed
+    from scratch over tokens 0..i ("All About Transformer Inference",
+    section "Transformer inference basics")."""
+    torch.manual_seed(5)
+    T, E, Hq, Hkv, D = 70, 96, 16, 2, 128
+    M = Hq // Hkv
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    x = torch.randn(T, E, dtype=torch.float64)
+    Wq, Wk, Wv = (torch.randn(E, n * D, dtype=torch.float64) / math.sqrt(E) for n in (Hq, Hkv, Hkv))
+    Q = (x @ Wq).view(T, Hq, D).to(tdt)
+    K = (x @ Wk).view(T, Hkv, D).to(tdt)
+    V = (x @ Wv).view(T, Hkv, D).to(tdt)
+    scale = D ** -0.5
+    # from scratch, fp64 on the CPU, on the cache-dtype values
+    Qd, Kd, Vd = Q.double(), K.double(), V.double()
+    full = torch.zeros(T, Hq, D, dtype=torch.float64)
+    mask = torch.tril(torch.ones(T, T, dtype=torch.bool))
+    for h in range(Hq):
+        S = scale * (Qd[:, h] @ Kd[:, h // M].T)
+        S = S.masked_fill(~mask, float("-inf"))
+        full[:, h] = torch.softmax(S, dim=1) @ Vd[:, h // M]
+    # cached, on the GPU
+    dev = torch.device("cuda")
+    kc = torch.full((1, Hkv, T, D), float("nan"), dtype=tdt, device=dev)
+    vc = torch.full((1, Hkv, T, D), float("nan"), dtype=tdt, device=dev)
+    L = torch.zeros(1, dtype=torch.int32, device=dev)
+    cache = kvd.KVCache(kc, vc, L, Hq)
+    rows = []
+    for i in range(T):
+        cache.append(K[i][None].to(dev).contiguous(), V[i][None].to(dev).contiguous())
+        rows.append(cache.attend(Q[i][None].to(dev).contiguous(), scale=scale))
+    assert cache.status() == kvd.KVD_OK
+    cache.close()
+    got = torch.cat(rows).double().cpu().numpy()
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert rel_err_rows(got, full.numpy()) <= tol
+    assert L.item() == T
