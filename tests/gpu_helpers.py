@@ -28,13 +28,13 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def gpu_step(case: inputs.Case, Hq: int, *, variant=None, splits=None, append=True,
              lengths=None, k_cache=None, v_cache=None):
-    """Append (optional) then attend on the GPU.  Inputs are copied to the
-    device unless already there.  Returns (out, k_cache, v_cache, lengths,
-    status, plan) as device tensors / ints."""
+    """Append (optional) then attend on the GPU, on fresh device copies of
+    the case's tensors (the case itself is never modified).  Returns (out,
+    k_cache, v_cache, lengths, status, plan)."""
     dev = torch.device("cuda")
-    kc = (k_cache if k_cache is not None else case.k_cache).to(dev).contiguous()
-    vc = (v_cache if v_cache is not None else case.v_cache).to(dev).contiguous()
-    L = (lengths if lengths is not None else case.lengths0).to(dev).to(torch.int32).contiguous()
+    kc = (k_cache if k_cache is not None else case.k_cache).to(dev, copy=True).contiguous()
+    vc = (v_cache if v_cache is not None else case.v_cache).to(dev, copy=True).contiguous()
+    L = (lengths if lengths is not None else case.lengths0).to(dev, torch.int32, copy=True).contiguous()
     cache = kvd.KVCache(kc, vc, L, Hq)
     try:
         if variant is not None:
