@@ -68,9 +68,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="force split count (0 = plan)")
-    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma", "lds"])
     ap.add_argument("--cache-copies", type=int, default=0, help="0 = enough for 2 GiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -86,6 +88,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kvd.library()  # fail loudly before any work if the HIP library is missing
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, args.steps)
 
     w = inputs.WORKLOADS[args.workload]
     K, W = args.steps, args.warmup
@@ -101,7 +105,7 @@ def main():
         f"{R} cache copies of {kv_bytes_one / 1e6:.0f} MB, capacity {T_cap}")
 
     variant = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU,
-               "mfma": kvd.KVD_VARIANT_MFMA}[args.variant]
+               "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}[args.variant]
     copies = []
     for r in range(R):
         case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
@@ -191,12 +195,30 @@ def main():
                      "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(w.name),
-                     "kernel": "partial_mfma_kernel" if plan["variant"] == "mfma" else "partial_valu_kernel"},
+                     "kernel": f"partial_{plan['variant']}_kernel"},
         "cpu_baseline": cpu,
     }
     for c in copies:
         c["cache"].close()
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(mib: int, reps: int):
+    """Plain device-to-device copies of a known size: the per-dispatch
+    FETCH_SIZE / WRITE_SIZE counters of these copies convert the counters of
+    the attention kernels into bytes."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    print(json.dumps({"calibrate_copy_bytes": n, "reps": reps,
+                      "copy_GBps_read_plus_write": round(2 * n / sec / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(w, copy, T_cap):

@@ -73,8 +73,13 @@ typedef enum {
     KVD_ELENGTH = -7       /* (from kvdecode_status) attend found lengths[b] outside [0, capacity] */
 } kvd_status_t;
 
-/* Kernel variants for the partial pass (kvdecode_set_variant). */
-enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2 };
+/* Kernel variants for the partial pass (kvdecode_set_variant).
+ *   VALU: vector-ALU kernel, fp32 or bf16, one wave per (split, query head).
+ *   MFMA: bf16 matrix-core kernel, one wave per 16 query heads, each wave
+ *         loading K/V straight into registers.
+ *   LDS:  bf16 matrix-core kernel, four waves per (split, KV head) sharing
+ *         K/V tiles staged in LDS by direct global->LDS loads. */
+enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2, KVD_VARIANT_LDS = 3 };
 
 typedef struct {
     int32_t batch;        /* B  >= 1                                        */
@@ -141,9 +146,9 @@ int32_t kvdecode_status(kvdecode_t h, void* stream);
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n);
 
 /*
- * Choose the partial-pass kernel: KVD_VARIANT_AUTO (MFMA for bf16, VALU for
- * fp32), KVD_VARIANT_VALU (vector-ALU kernel, any dtype) or
- * KVD_VARIANT_MFMA (bf16 only; KVD_EUNSUPPORTED for fp32).
+ * Choose the partial-pass kernel: KVD_VARIANT_AUTO (LDS for bf16, VALU for
+ * fp32), KVD_VARIANT_VALU (any dtype), KVD_VARIANT_MFMA or KVD_VARIANT_LDS
+ * (bf16 only; KVD_EUNSUPPORTED for fp32).
  */
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant);
 

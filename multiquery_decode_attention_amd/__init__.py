@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
-    "KVD_VARIANT_MFMA", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
+    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
     "kvdecode_append", "kvdecode_attend", "kvdecode_status", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
@@ -32,7 +32,7 @@ __all__ = [
 KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
 KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH = -4, -5, -6, -7
 KVD_F32, KVD_BF16 = 0, 1
-KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA = 0, 1, 2
+KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
 
@@ -171,7 +171,7 @@ def kvdecode_get_plan(h: int) -> dict:
     v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(library().kvdecode_get_plan(h, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)),
            "kvdecode_get_plan")
-    return {"variant": {1: "valu", 2: "mfma"}.get(v.value, str(v.value)),
+    return {"variant": {1: "valu", 2: "mfma", 3: "lds"}.get(v.value, str(v.value)),
             "num_splits": s.value, "split_tokens": c.value}
 
 

@@ -33,13 +33,22 @@ CFLAGS = [
 ]
 
 
+# Per-file extra flags.  The LDS-staged kernel keeps its matrix-core
+# accumulators in ordinary VGPRs: its rare softmax rescale multiplies them on
+# the vector ALU, and accumulators in AGPRs made the compiler copy all of
+# them between register files on every loop iteration.
+FILE_FLAGS = {
+    "kvd_partial_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

@@ -56,6 +56,8 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     }
     const size_t prow = ((size_t)b * a.Hq + h) * a.S;
     const float* lse = a.lse_part + prow;
+    // Global maximum and normaliser over all splits (lane j holds split j of
+    // each block of 64).
     float L = -INFINITY;
     for (int j = lane; j < nsplit; j += 64) L = fmaxf(L, lse[j]);
     L = wave_max(L);
@@ -65,21 +67,40 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const float inv_z = 1.f / z;
 
     const float* op = a.o_part + prow * a.D;
-    for (int v = lane; v < nvec; v += 64) {
+    // Wave-uniform loop (the weight shuffles below need every lane active);
+    // lanes past the row's last column vector only skip their loads/stores.
+    for (int v0 = 0; v0 < nvec; v0 += 64) {
+        const int v = v0 + lane;
+        const bool col_ok = v < nvec;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < nsplit; ++j) {
-            const float w = exp2f(lse[j] - L);
-            const float4 o = *reinterpret_cast<const float4*>(op + (size_t)j * a.D + 4 * v);
-            acc.x = fmaf(w, o.x, acc.x);
-            acc.y = fmaf(w, o.y, acc.y);
-            acc.z = fmaf(w, o.z, acc.z);
-            acc.w = fmaf(w, o.w, acc.w);
+        for (int j0 = 0; j0 < nsplit; j0 += 64) {
+            const int jn = min(64, nsplit - j0);
+            const float wl = lane < jn ? exp2f(lse[j0 + lane] - L) : 0.f;
+            // eight independent partial loads in flight per lane
+            for (int u0 = 0; u0 < jn; u0 += 8) {
+                float4 o[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u0 + u;
+                    o[u] = (col_ok && u0 + u < jn)
+                               ? *reinterpret_cast<const float4*>(op + (size_t)j * a.D + 4 * v)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float w = __shfl(wl, (u0 + u) & 63);
+                    acc.x = fmaf(w, o[u].x, acc.x);
+                    acc.y = fmaf(w, o[u].y, acc.y);
+                    acc.z = fmaf(w, o[u].z, acc.z);
+                    acc.w = fmaf(w, o[u].w, acc.w);
+                }
+            }
         }
         acc.x *= inv_z;
         acc.y *= inv_z;
         acc.z *= inv_z;
         acc.w *= inv_z;
-        store4(orow, obase + 4 * v, acc);
+        if (col_ok) store4(orow, obase + 4 * v, acc);
     }
 }
 

@@ -44,12 +44,32 @@ struct CombineArgs {
     int B, Hq, D, T_cap, chunk, S;
 };
 
+// Partial-pass grids are one-dimensional and split-major: block
+// L = split * units + unit.  Consecutive blocks are dealt round-robin to the
+// eight XCDs, so consecutive units of the same split land on different XCDs;
+// with ragged lengths the always-active low splits are spread evenly and
+// dispatched first, and the mostly-empty high splits come last.
+struct BlockCoord {
+    int split, unit;
+};
+__device__ __forceinline__ BlockCoord block_coord(int units) {
+    const int L = (int)blockIdx.x;
+    BlockCoord c;
+    c.split = L / units;
+    c.unit = L - c.split * units;
+    return c;
+}
+
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          int32_t* lengths, int* err, int B, int Hkv, int D, int T_cap,
                          int elem_bytes, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
+
+// Workgroups of the LDS-staged kernel resident per CU (LDS ring size bound).
+inline int lds_groups_per_cu(int D) { return D == 256 ? 1 : (D == 128 ? 2 : 3); }
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
 
 // Waves per work unit of the MFMA partial pass for group size M.

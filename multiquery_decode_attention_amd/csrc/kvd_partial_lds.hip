@@ -1,0 +1,332 @@
+// kvd_partial_lds.hip -- bf16 split-KV partial pass with LDS-shared K/V tiles.
+//
+// Work unit: (split s, KV head g, sequence b[, block of 64 query heads]) ->
+// one workgroup of 4 waves.  The group's M query heads are dealt out to the
+// four waves (ceil(M/4) each, at most 16); every wave runs the same score /
+// online-softmax / value products as the register kernel on its heads, but
+// all four read one shared copy of each 32-token K/V tile from LDS, so a tile
+// crosses HBM and the cache hierarchy once for all M heads.
+//
+// Tiles arrive through a ring of NS LDS stages filled by gfx950's direct
+// global->LDS 16-byte loads (no registers held while in flight): stage i+NS-1
+// is requested while stage i is computed, so up to NS-1 tiles per workgroup
+// are in flight.  Each wave issues D/32 loads per stage; before a stage is
+// read every wave waits for its own loads of that stage (vmcnt) and the
+// workgroup meets at a barrier, which also retires the stage read in the
+// previous iteration before it is refilled.
+//
+// LDS layout of a stage: K rows then V rows, 32 rows of D bf16 each, in
+// 16-byte chunks.  Chunk p of K row t sits at position (p + t) mod (D/8) of
+// the row, so the score operand reads (16 lanes = 16 rows, one chunk each)
+// touch 16 different bank groups; V rows are read a row at a time (16 lanes
+// = 16 consecutive chunks of one row) and are stored as they are.  Rows past
+// the split's end are loaded as copies of its last valid row and masked out
+// of the softmax.
+//
+// Softmax bookkeeping per head keeps a reference maximum m and the sum l of
+// 2^(x - m).  A tile whose scores stay below m + 8 (base 2) leaves m alone:
+// its weights are at most 2^8, far inside fp32 and bf16 range, and since the
+// sum uses the same m the normalised result is unchanged.  Only when some
+// head of the wave exceeds m + 8 are m, l and that wave's accumulators
+// rescaled, which after the first tiles almost never happens.
+//
+// Sources: as for the register kernel -- the grouped contraction and the
+// cross-shard Flash-style accumulation ("All About Transformer Inference",
+// section "Sharding the KV cache"); multiquery K/V shared by all query heads
+// and the aim of loading the cache as few times as possible ("Efficiently
+// Scaling Transformer Inference", section 3.3); base-2 softmax (same page,
+// section 3.5).  FlashDecoding++'s double-buffered shared-memory loads (the
+// blog summary of that paper) are the prior art for the staging.
+#include "kvd_mfma_common.h"
+
+namespace kvd {
+namespace {
+
+using namespace mfma;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; a compiler memory barrier
+// so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_index() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// True when the predicate holds in any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
+template <int PERW>
+__device__ __forceinline__ void wait_stage(int stages_after) {
+    switch (stages_after) {
+        case 0: wait_vm_barrier<0>(); break;
+        case 1: wait_vm_barrier<PERW>(); break;
+        case 2: wait_vm_barrier<2 * PERW>(); break;
+        case 3: wait_vm_barrier<3 * PERW>(); break;
+        case 4: wait_vm_barrier<4 * PERW>(); break;
+        default: wait_vm_barrier<5 * PERW>(); break;
+    }
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int head_groups) {
+    constexpr int CH = D / 8;                        // 16-byte chunks per row
+    constexpr int KS = D / 32;                       // k-steps of the score product
+    constexpr int NE = D / 16;                       // output column blocks per lane
+    constexpr int REGION = MFMA_TILE * D * 2;        // bytes of K (or V) per stage
+    constexpr int STAGE = 2 * REGION;
+    constexpr int PERW = STAGE / (4 * 64 * 16);      // loads per wave per stage (= D/32)
+    constexpr float TAU = 8.f;                       // rescale threshold (base-2 exponent)
+    static_assert(NS >= 2 && NS - 2 <= 5, "ring depth");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
+
+    // unit = (sequence b, KV head g, head group hg), head group fastest
+    const BlockCoord bc = block_coord(a.B * a.Hkv * head_groups);
+    const int s = bc.split;
+    const int hg = bc.unit % head_groups;
+    const int g = (bc.unit / head_groups) % a.Hkv;
+    const int b = bc.unit / (head_groups * a.Hkv);
+    int len = a.lengths[b];
+    if (len < 0 || len > a.T_cap) {
+        if (s == 0 && g == 0 && hg == 0 && threadIdx.x == 0) atomicOr(a.err, ERRBIT_LENGTH);
+        len = len < 0 ? 0 : a.T_cap;
+    }
+    const int t_begin = s * a.chunk;
+    if (t_begin >= len) return;  // whole workgroup: before any barrier
+    const int t_end = min(t_begin + a.chunk, len);
+    const int n_tiles = (t_end - t_begin + MFMA_TILE - 1) / MFMA_TILE;
+
+    const int wave = wave_index();
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, gq = lane >> 4;
+    const int mg = min(a.M - hg * 64, 64);   // heads of this workgroup
+    const int hpw = (mg + 3) / 4;             // heads per wave
+    const int hw0 = hg * 64 + wave * hpw;     // first head (within the KV group) of this wave
+    const int nh = max(0, min(hpw, mg - wave * hpw));
+    const bool head_ok = c < nh;
+
+    const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.T_cap * D;
+    const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k_cache) + slab);
+    const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + slab);
+
+    // Queries of this wave's heads: B operand of the score product.
+    u32x4_t qop[KS];
+    {
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hw0 + c) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[ks] = head_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq)
+                              : u32x4_t{0, 0, 0, 0};
+    }
+
+    // Loads of one stage: this wave's PERW loads cover LDS chunks
+    // j0 .. j0+63 with j0 = (wave*PERW + n)*64; lane -> (row t, chunk p).
+    // Byte offsets inside a tile are loop invariant.
+    uint32_t doff[PERW];
+#pragma unroll
+    for (int n = 0; n < PERW; ++n) {
+        const int j0 = (wave * PERW + n) * 64;
+        const bool is_v = j0 >= MFMA_TILE * CH;
+        const int j = (is_v ? j0 - MFMA_TILE * CH : j0) + lane;
+        const int t = j / CH;
+        const int p = is_v ? j % CH : (j - t + CH * 64) % CH;  // K: position q holds chunk q - t
+        doff[n] = (uint32_t)((t * CH + p) * 16);
+    }
+    auto issue = [&](int tile) {
+        const int t0 = t_begin + tile * MFMA_TILE;
+        unsigned char* stage = lds + (tile % NS) * STAGE;
+        if (t0 + MFMA_TILE <= t_end) {
+#pragma unroll
+            for (int n = 0; n < PERW; ++n) {
+                const int j0 = (wave * PERW + n) * 64;
+                const char* base = (j0 >= MFMA_TILE * CH ? vb : kb) + (size_t)t0 * (D * 2);
+                // (the source must reach the builtin as const void*: with a
+                // char pointer the host pass drops the kernel's launch stub)
+                __builtin_amdgcn_global_load_lds((const void*)(base + doff[n]),
+                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+            }
+        } else {
+            // last, partial tile: rows past the end re-read the last valid row
+#pragma unroll
+            for (int n = 0; n < PERW; ++n) {
+                const int j0 = (wave * PERW + n) * 64;
+                const char* base = (j0 >= MFMA_TILE * CH ? vb : kb) + (size_t)t0 * (D * 2);
+                const int t = (int)(doff[n] / (D * 2));
+                const int row = min(t, t_end - 1 - t0);
+                __builtin_amdgcn_global_load_lds((const void*)(base + (int)doff[n] + (row - t) * (D * 2)),
+                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+            }
+        }
+    };
+
+    // Per-lane LDS read offsets: K operand of k-step ks (rows c and 16+c),
+    // and V row 0 of this lane's chunk (rows advance by whole rows).
+    uint32_t koff[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int t = 16 * sb + c;
+            koff[sb][ks] = (uint32_t)((t * CH + ((4 * ks + gq + t) % CH)) * 16);
+        }
+    }
+
+    f32x4_t acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    // The prologue always requests NS-1 tiles (tiles past the split re-read
+    // its last rows and are never consumed), so the number of loads issued
+    // after the queries is a compile-time constant for the compiler's own
+    // wait on them.
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(i);
+
+    if (nh == 0) {
+        // a wave with no heads of its own still loads its share of every tile
+        for (int it = 0; it < n_tiles; ++it) {
+            wait_stage<PERW>(min(n_tiles - 1, it + NS - 2) - it);
+            if (it + NS - 1 < n_tiles) issue(it + NS - 1);
+        }
+        return;
+    }
+
+    for (int it = 0; it < n_tiles; ++it) {
+        // loads issued after tile `it`: tiles it+1 .. min(it+NS-2, n_tiles-1)
+        wait_stage<PERW>(min(n_tiles - 1, it + NS - 2) - it);
+        if (it + NS - 1 < n_tiles) issue(it + NS - 1);
+
+        const unsigned char* Kl = lds + (it % NS) * STAGE;
+        const unsigned char* Vl = Kl + REGION;
+        const int t0 = t_begin + it * MFMA_TILE;
+
+        f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(Kl + koff[0][ks]);
+            const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(Kl + koff[1][ks]);
+            sc[0] = mfma16x16x32(k0, qop[ks], sc[0]);
+            sc[1] = mfma16x16x32(k1, qop[ks], sc[1]);
+        }
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
+        if (t0 + MFMA_TILE > t_end) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (wave_any(mx > m_ref + TAU)) {
+            // raise the reference of the heads that outgrew it; rescale
+            const float m_new = mx > m_ref + TAU ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+            m_ref = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * gq + i);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[e][i] *= ai;
+            }
+        }
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
+            l_run += p[j];
+        }
+        u32x4_t pop;
+        pop[0] = pack_bf16x2(p[0], p[1]);
+        pop[1] = pack_bf16x2(p[2], p[3]);
+        pop[2] = pack_bf16x2(p[4], p[5]);
+        pop[3] = pack_bf16x2(p[6], p[7]);
+        // Value product, 128 columns (one 16-byte chunk per lane) at a time.
+        if constexpr (D >= 128) {
+#pragma unroll
+            for (int i = 0; i < D / 128; ++i) {
+                uint32_t v[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int t = slot_token(gq, j);
+                    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(Vl + (t * CH + c + 16 * i) * 16);
+                    v[j][0] = xv[0];
+                    v[j][1] = xv[1];
+                    v[j][2] = xv[2];
+                    v[j][3] = xv[3];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[8 * i + e] = mfma16x16x32(pop, v_operand(v, e), acc[8 * i + e]);
+            }
+        } else {
+            uint32_t v[8][2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const u32x2_t xv = *reinterpret_cast<const u32x2_t*>(Vl + slot_token(gq, j) * CH * 16 + c * 8);
+                v[j][0] = xv[0];
+                v[j][1] = xv[1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = mfma16x16x32(pop, v_operand(v, e), acc[e]);
+        }
+    }
+
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const size_t row0 = ((size_t)b * a.Hq + (size_t)g * a.M + hw0) * a.S + s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * gq + i;
+        const float li = __shfl(l, r);
+        if (r < nh) {
+            const float inv = 1.f / li;
+            float* orow = a.o_part + (row0 + (size_t)r * a.S) * D;
+            if constexpr (D >= 128) {
+#pragma unroll
+                for (int e = 0; e < NE; e += 4) {
+                    float4 o = make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
+                                           acc[e + 3][i] * inv);
+                    *reinterpret_cast<float4*>(orow + owned_col<D>(c, e)) = o;
+                }
+            } else {
+                float4 o = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv);
+                *reinterpret_cast<float4*>(orow + owned_col<D>(c, 0)) = o;
+            }
+        }
+    }
+    if (gq == 0 && head_ok) a.lse_part[row0 + (size_t)c * a.S] = m_ref + __builtin_log2f(l);
+}
+
+template <int D, int NS>
+hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
+    const int groups = (a.M + 63) / 64;
+    dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
+    hipLaunchKernelGGL((partial_lds_kernel<D, NS>), grid, dim3(256), 0, stream, a, groups);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 64: return launch_d<64, 6>(a, stream);
+        case 128: return launch_d<128, 4>(a, stream);
+        case 256: return launch_d<256, 5>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvd

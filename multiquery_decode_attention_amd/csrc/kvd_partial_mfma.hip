@@ -34,31 +34,12 @@
 // Transformer Inference", section 3.3; base-2 softmax, same page, section 3.5;
 // reading only each sequence's valid prefix, "All About Transformer
 // Inference", ragged-reads paragraph.
-#include "kvd_internal.h"
+#include "kvd_mfma_common.h"
 
 namespace kvd {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ inline f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-    const uint32_t l = __builtin_bit_cast(uint16_t, (__bf16)lo);
-    const uint32_t h = __builtin_bit_cast(uint16_t, (__bf16)hi);
-    return l | (h << 16);
-}
-
-// Token (row of the tile) held in k-slot j of lane group gq.  Slots 0-3 are
-// rows 4gq..4gq+3 of the first 16-token half, slots 4-7 the same rows of the
-// second half: this is where the score MFMA leaves them.
-__device__ inline int slot_token(int gq, int j) { return (j < 4 ? 0 : 12) + 4 * gq + j; }
+using namespace mfma;
 
 // Registers of one 32-token tile.
 template <int D>
@@ -81,17 +62,6 @@ __device__ inline void load_k(TileRegs<D>& r, const uint16_t* __restrict__ kb, i
         for (int ks = 0; ks < TileRegs<D>::KS; ++ks) {
             r.k[sb][ks] = ok ? *reinterpret_cast<const u32x4_t*>(p + 32 * ks) : u32x4_t{0, 0, 0, 0};
         }
-    }
-}
-
-// Columns owned by lane c: for D >= 128, 8-column pieces c, c+16, ...;
-// for D == 64, the 4 columns 4c..4c+3.
-template <int D>
-__device__ inline int owned_col(int c, int e) {
-    if constexpr (D >= 128) {
-        return 8 * (c + 16 * (e / 8)) + (e % 8);
-    } else {
-        return 4 * c + e;
     }
 }
 
@@ -134,27 +104,17 @@ __device__ inline void load_tile(TileRegs<D>& r, const uint16_t* kb, const uint1
     }
 }
 
-// B operand of the value product for column e of this lane: the 8 tokens'
-// bf16 values, two per dword, gathered with byte permutes.
-template <int D>
-__device__ inline u32x4_t v_operand(const TileRegs<D>& r, int e) {
-    const int w = e / 2;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    u32x4_t o;
-    o[0] = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], sel);
-    o[1] = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], sel);
-    o[2] = __builtin_amdgcn_perm(r.v[5][w], r.v[4][w], sel);
-    o[3] = __builtin_amdgcn_perm(r.v[7][w], r.v[6][w], sel);
-    return o;
-}
-
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, int hb_groups) {
     constexpr int KS = D / 32;
     constexpr int NE = D / 16;  // value columns per lane = output blocks
-    const int s = blockIdx.x, b = blockIdx.z;
-    const int g = blockIdx.y / hb_groups;
-    const int hb = (blockIdx.y - g * hb_groups) * NW + (int)(threadIdx.x >> 6);
+    // unit = (sequence b, KV head g, head-block group), group fastest
+    const BlockCoord bc = block_coord(a.B * a.Hkv * hb_groups);
+    const int s = bc.split;
+    const int hbg = bc.unit % hb_groups;
+    const int g = (bc.unit / hb_groups) % a.Hkv;
+    const int b = bc.unit / (hb_groups * a.Hkv);
+    const int hb = hbg * NW + (int)(threadIdx.x >> 6);
     if (hb * MFMA_HEADS >= a.M) return;  // whole wave past the group's last head
     int len = a.lengths[b];
     if (len < 0 || len > a.T_cap) {
@@ -244,7 +204,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
         pop[2] = pack_bf16x2(p[4], p[5]);
         pop[3] = pack_bf16x2(p[6], p[7]);
 #pragma unroll
-        for (int e = 0; e < NE; ++e) acc[e] = mfma16x16x32(pop, v_operand<D>(r, e), acc[e]);
+        for (int e = 0; e < NE; ++e) acc[e] = mfma16x16x32(pop, v_operand(r.v, e), acc[e]);
         if (tn < t_end) load_tile<D>(r, kb, vb, tn, t_end, c, gq, false);
     }
 
@@ -282,7 +242,7 @@ hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int hbs = mfma_head_blocks(a.M);
     const int nw = hbs < 4 ? hbs : 4;
     const int groups = (hbs + nw - 1) / nw;
-    dim3 grid(a.S, a.Hkv * groups, a.B);
+    dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
     switch (nw) {
         case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1>), grid, dim3(64), 0, stream, a, groups); break;
         case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2>), grid, dim3(128), 0, stream, a, groups); break;

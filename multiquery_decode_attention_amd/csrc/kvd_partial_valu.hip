@@ -38,7 +38,11 @@ __device__ inline float wave_sum(float v) {
 template <typename T, int D>
 __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     constexpr int DPL = D / 64;  // value columns per lane
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // unit = (sequence b, query head h), head fastest
+    const BlockCoord bc = block_coord(a.B * a.Hq);
+    const int s = bc.split;
+    const int h = bc.unit % a.Hq;
+    const int b = bc.unit / a.Hq;
     const int lane = threadIdx.x;
     int len = a.lengths[b];
     if (len < 0 || len > a.T_cap) {
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
 
 template <typename T>
 hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
-    dim3 grid(a.S, a.Hq, a.B), block(64);
+    dim3 grid((unsigned)a.S * a.B * a.Hq), block(64);
     switch (a.D) {
         case 64: hipLaunchKernelGGL((partial_valu_kernel<T, 64>), grid, block, 0, stream, a); break;
         case 128: hipLaunchKernelGGL((partial_valu_kernel<T, 128>), grid, block, 0, stream, a); break;

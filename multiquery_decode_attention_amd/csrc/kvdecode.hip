@@ -58,43 +58,86 @@ struct Plan {
 
 int resolve_variant(const kvdecode_s* h) {
     if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
-    return h->d.dtype == KVD_BF16 ? KVD_VARIANT_MFMA : KVD_VARIANT_VALU;
+    return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
 }
 
-// Split planner.  The grid is (splits, KV heads, sequences); lengths live on
-// the device, so the plan is made from the capacity and splits past a
-// sequence's length exit at once.  Automatic plans aim for about 32 waves
-// per compute unit on 256 CUs when every sequence is full, and keep each
-// split long enough that the fp32 partials stay a few percent of the
-// K/V bytes the split reads (partial bytes ~ M*4 per column, K/V bytes ~
-// chunk*2*elem per column).
+// Split planner.  The grid is (splits, KV heads [x head groups], sequences);
+// lengths live on the device, so the plan is made for full caches and splits
+// past a sequence's length exit at once.  For every candidate split count S
+// the cost model charges
+//   rounds(S) * (bytes of one split + a fixed fill cost) * resident slots
+//     + fp32 partial traffic (written by the partial pass, read by combine)
+// where rounds(S) = ceil(work units * S / resident slots): a launch whose
+// last round is partly empty wastes the rest of that round.  Among plans
+// within 2% of the cheapest, the one with most splits wins (shorter splits
+// balance ragged lengths better).
+constexpr int CUS = 256;
+
+struct Shape {
+    long long units;      // workgroups per split
+    long long slots;      // workgroups resident on the whole GPU
+};
+
+Shape shape_for(const kvdecode_s* h, int variant) {
+    const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
+    Shape sh;
+    if (variant == KVD_VARIANT_LDS) {
+        sh.units = bkv * ((h->M + 63) / 64);
+        sh.slots = (long long)CUS * kvd::lds_groups_per_cu(h->d.head_dim);
+    } else if (variant == KVD_VARIANT_MFMA) {
+        const int hb = kvd::mfma_head_blocks(h->M);
+        const int nw = hb < 4 ? hb : 4;
+        sh.units = bkv * ((hb + nw - 1) / nw);
+        const int waves_per_cu = h->d.head_dim == 256 ? 4 : (h->d.head_dim == 128 ? 8 : 16);
+        sh.slots = (long long)CUS * (waves_per_cu / nw > 0 ? waves_per_cu / nw : 1);
+    } else {
+        sh.units = bkv * h->M;
+        sh.slots = (long long)CUS * 16;
+    }
+    return sh;
+}
+
 Plan make_plan(const kvdecode_s* h) {
     Plan p;
     p.variant = resolve_variant(h);
-    p.tile = p.variant == KVD_VARIANT_MFMA ? kvd::MFMA_TILE : kvd::VALU_TILE;
+    p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
     const long long T = h->d.capacity;
     const int max_splits = (int)((T + p.tile - 1) / p.tile);
-    int s;
+    auto finish = [&](int s) {
+        if (s < 1) s = 1;
+        if (s > max_splits) s = max_splits;
+        long long chunk = (T + s - 1) / s;
+        chunk = (chunk + p.tile - 1) / p.tile * p.tile;
+        p.chunk = (int)chunk;
+        p.splits = (int)((T + chunk - 1) / chunk);
+    };
     if (h->forced_splits > 0) {
-        s = h->forced_splits;
-    } else {
-        const long long waves_per_split =
-            (long long)h->d.batch * h->d.num_kv_heads *
-            (p.variant == KVD_VARIANT_MFMA ? kvd::mfma_head_blocks(h->M) : h->M);
-        const long long target_waves = 8192;
-        s = (int)((target_waves + waves_per_split - 1) / waves_per_split);
-        // keep the partials small next to the K/V bytes of a split
-        long long min_chunk = 32LL * h->M;
-        if (min_chunk < 256) min_chunk = 256;
-        const int s_cap = (int)((T + min_chunk - 1) / min_chunk);
-        if (s > s_cap) s = s_cap;
+        finish(h->forced_splits);
+        return p;
     }
-    if (s < 1) s = 1;
-    if (s > max_splits) s = max_splits;
-    long long chunk = (T + s - 1) / s;
-    chunk = (chunk + p.tile - 1) / p.tile * p.tile;
-    p.chunk = (int)chunk;
-    p.splits = (int)((T + chunk - 1) / chunk);
+    const Shape sh = shape_for(h, p.variant);
+    const double tok_bytes = 2.0 * h->d.head_dim * h->elem;        // K+V of one token
+    const double fill = 32.0 * 1024;                              // pipeline fill per split
+    const double part_bytes = (double)h->M * (h->d.head_dim + 1) * 4 * 2;
+    double best = 0;
+    std::vector<std::pair<int, double>> cand;
+    int prev_chunk = -1;
+    for (int s = 1; s <= max_splits; ++s) {
+        long long chunk = (T + s - 1) / s;
+        chunk = (chunk + p.tile - 1) / p.tile * p.tile;
+        if (chunk == prev_chunk) continue;
+        prev_chunk = (int)chunk;
+        const int splits = (int)((T + chunk - 1) / chunk);
+        const long long rounds = (sh.units * splits + sh.slots - 1) / sh.slots;
+        const double cost = (double)rounds * (chunk * tok_bytes + fill) * sh.slots +
+                            (double)sh.units * splits * part_bytes;
+        cand.emplace_back(splits, cost);
+        if (best == 0 || cost < best) best = cost;
+    }
+    int pick = 1;
+    for (auto& c : cand)
+        if (c.second <= best * 1.02 && c.first > pick) pick = c.first;
+    finish(pick);
     return p;
 }
 
@@ -235,7 +278,7 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
     const Plan p = make_plan(h);
-    if (p.variant == KVD_VARIANT_MFMA && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    if (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
@@ -275,9 +318,9 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
     const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = p.variant == KVD_VARIANT_MFMA
-                       ? kvd::launch_partial_mfma(a, st)
-                       : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
+    hipError_t e = p.variant == KVD_VARIANT_LDS    ? kvd::launch_partial_lds(a, st)
+                   : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
+                                                   : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
     e = kvd::launch_combine(c, h->d.dtype == KVD_BF16, st);
@@ -316,9 +359,9 @@ int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
 
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
     if (!is_live(h)) return KVD_EINVAL;
-    if (variant != KVD_VARIANT_AUTO && variant != KVD_VARIANT_VALU && variant != KVD_VARIANT_MFMA)
+    if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_LDS) return KVD_EUNSUPPORTED;
+    if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
-    if (variant == KVD_VARIANT_MFMA && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
     h->variant_req = variant;
     return KVD_OK;
 }

@@ -138,7 +138,7 @@ def test_plans_cover_the_cache(lib, name):
         assert rc == kvd.KVD_OK
         kvd.kvdecode_set_num_splits(h, forced)
         p = kvd.kvdecode_get_plan(h)
-        tile = 32 if p["variant"] == "mfma" else 64
+        tile = 64 if p["variant"] == "valu" else 32
         S, C = p["num_splits"], p["split_tokens"]
         assert C % tile == 0 and S >= 1
         assert S * C >= w.T_cap and (S - 1) * C < w.T_cap

@@ -60,26 +60,36 @@ def test_split_invariance(name, B, splits):
     check_case(case, w.Hq, f"{name}/splits={splits}", splits=splits)
 
 
+VARIANTS = {"valu": kvd.KVD_VARIANT_VALU, "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
 @pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 2), ("ragged_gqa_bf16", 4),
-                                    ("llama13b_mha_bf16", 1)])
-def test_valu_kernel_bf16(name, B):
-    """The vector-ALU kernel as an independent second GPU path in bf16."""
+                                    ("llama13b_mha_bf16", 1), ("longctx_mqa_bf16", 1)])
+def test_kernel_variants_bf16(name, B, variant):
+    """Each partial-pass kernel on its own (the vector-ALU one is an
+    independent second GPU path)."""
     w = inputs.WORKLOADS[name]
     case = inputs.make_workload_case(w, device="cpu", B=B)
-    check_case(case, w.Hq, f"{name}/valu", variant=kvd.KVD_VARIANT_VALU)
+    if name == "longctx_mqa_bf16":  # keep the CPU copy small: 8192 tokens
+        case = inputs.make_case(1, w.Hq, w.Hkv, w.D, 8192, [8192], "bf16", seed=w.seed)
+    check_case(case, w.Hq, f"{name}/{variant}", variant=VARIANTS[variant])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,variant", [("bf16", "lds"), ("bf16", "mfma"), ("f32", "valu")])
 @pytest.mark.parametrize("Hq,Hkv,D", [(48, 1, 256), (8, 1, 64), (64, 8, 128), (12, 4, 128),
-                                      (80, 1, 128), (16, 16, 64), (17, 1, 256)])
-def test_shapes_and_ragged_lengths(dtype, Hq, Hkv, D):
-    """Group sizes 1..80 (one to five 16-head blocks, padded ones too),
-    every head dim, and lengths hitting 0, 1, tile edges and capacity."""
+                                      (80, 1, 128), (16, 16, 64), (17, 1, 256), (130, 2, 64)])
+def test_shapes_and_ragged_lengths(dtype, variant, Hq, Hkv, D):
+    """Group sizes 1..65 (one to five 16-head blocks, one or two 64-head
+    groups, padded ones too), every head dim, and lengths hitting 1, tile
+    edges and capacity, with a forced split count that cuts mid-sequence."""
     T_cap = 300
     lengths = [1, 2, 31, 32, 33, 64, 65, 257, 300]  # attended lengths (after append)
     B = len(lengths)
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, lengths, dtype, seed=Hq * 1000 + D, device="cpu")
-    check_case(case, Hq, f"shape Hq={Hq} Hkv={Hkv} D={D} {dtype}")
+    for splits in (0, 3):
+        check_case(case, Hq, f"shape Hq={Hq} Hkv={Hkv} D={D} {dtype} {variant} splits={splits}",
+                   variant=VARIANTS[variant], splits=splits)
 
 
 def test_empty_sequences_and_poisoned_tails():
@@ -151,7 +161,8 @@ def test_hand_worked_cases_on_gpu(dtype):
         scale = eval(c["scale_expr"], {"log": math.log})  # noqa: S307 (fixture-owned)
         case = inputs.Case(q, k, v, L, torch.zeros(B, Hkv, D, dtype=tdt),
                            torch.zeros(B, Hkv, D, dtype=tdt), scale)
-        for variant in ([kvd.KVD_VARIANT_VALU] + ([kvd.KVD_VARIANT_MFMA] if dtype == "bf16" else [])):
+        for variant in ([kvd.KVD_VARIANT_VALU] +
+                        ([kvd.KVD_VARIANT_MFMA, kvd.KVD_VARIANT_LDS] if dtype == "bf16" else [])):
             out, _, _, _, status, _ = gpu_step(case, Hq, append=False, variant=variant)
             assert status == kvd.KVD_OK
             got = to_f64(out)[..., :d]
