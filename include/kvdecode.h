@@ -140,8 +140,10 @@ int32_t kvdecode_status(kvdecode_t h, void* stream);
 
 /*
  * Force the split count of the attend pass (0 restores the automatic plan).
- * n is clamped to [1, ceil(T_cap / tile)] where tile is the kernel's token
- * tile.  Used to check that results do not depend on the split.
+ * Each sequence's cache is cut into tiles of the partial kernel (32 tokens,
+ * or 64 for the vector-ALU kernel) dealt round-robin to the splits: split s
+ * owns tiles s, s+S, s+2S, ...  n is clamped to [1, ceil(T_cap / tile)].
+ * Used to check that results do not depend on the split.
  */
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n);
 
@@ -154,7 +156,8 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant);
 
 /*
  * Report the current plan: variant in use, number of splits per
- * (sequence, KV head) and tokens per split.  Any pointer may be NULL.
+ * (sequence, KV head) and the most tokens any split holds when the cache
+ * is full.  Any pointer may be NULL.
  */
 int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
                           int32_t* split_tokens);

@@ -34,7 +34,10 @@ KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH = -4, -5, -6, -7
 KVD_F32, KVD_BF16 = 0, 1
 KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS = 0, 1, 2, 3
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
+# KVD_LIBRARY may name another build of the same library (e.g. one compiled
+# with different tuning constants); by default the in-tree build is used.
+LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libkvdecode.so")
 
 EXPORTS = (
     "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_status",

@@ -1,12 +1,12 @@
 // kvd_combine.hip -- merge the split-KV partials of each (sequence, head).
 //
-// Split j of a sequence covers tokens [j*chunk, (j+1)*chunk) of its valid
-// prefix and left its softmax-normalised output O_j and its base-2
-// log-sum-exp L_j = m_j + log2(l_j).  The full attention is the softmax over
+// Split j of a sequence covers its share of the valid prefix (the partial
+// kernel's token tiles j, j+S, ...) and left its softmax-normalised output
+// O_j and its base-2 log-sum-exp L_j = m_j + log2(l_j).  The full attention is the softmax over
 // all tokens, which factorises over the splits:
 //     out = sum_j 2^(L_j - L) O_j / sum_j 2^(L_j - L),   L = max_j L_j.
-// Only ceil(len/chunk) splits hold data; a sequence with no tokens gets a
-// zero row.  This is the accumulation across sequence shards "like Flash
+// Only min(S, ceil(len/tile)) splits hold data; a sequence with no tokens
+// gets a zero row.  This is the accumulation across sequence shards "like Flash
 // Attention" of "All About Transformer Inference", section "Sharding the KV
 // cache", carried out inside one GPU.
 //
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const int lane = threadIdx.x;
     int len = a.lengths[b];
     len = len < 0 ? 0 : (len > a.T_cap ? a.T_cap : len);
-    const int nsplit = (len + a.chunk - 1) / a.chunk;
+    const int nsplit = splits_with_data(len, a.tile, a.S);
     T* orow = static_cast<T*>(a.out);
     const size_t obase = ((size_t)b * a.Hq + h) * a.D;
     const int nvec = a.D / 4;

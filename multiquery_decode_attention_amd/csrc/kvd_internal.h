@@ -31,8 +31,8 @@ struct PartialArgs {
     float* lse_part;        // [B, Hq, S]    base-2 log-sum-exp of each split
     int* err;               // sticky error word
     int B, Hq, Hkv, M, D, T_cap;
-    int chunk;              // tokens per split (multiple of the kernel tile)
-    int S;                  // splits per (sequence, KV head)
+    int S;                  // splits per (sequence, KV head): split s owns the
+                            // kernel's token tiles s, s+S, s+2S, ...
     float scale_log2e;      // scale * log2(e)
 };
 
@@ -41,8 +41,22 @@ struct CombineArgs {
     const float* lse_part;
     const int32_t* lengths;
     void* out;              // [B, Hq, D]
-    int B, Hq, D, T_cap, chunk, S;
+    int B, Hq, D, T_cap;
+    int tile;               // tokens per tile of the partial kernel that ran
+    int S;
 };
+
+// Token tiles of a sequence are dealt round-robin to its S splits: split s
+// owns tiles s, s+S, s+2S, ...  At any moment the S workgroups of a
+// sequence stream one contiguous window of its cache (good DRAM page
+// locality, like a single sequential read), every split gets an equal share
+// of full tiles, and only the split holding the sequence's last tile sees a
+// partial one.  A sequence of n tokens has min(S, ceil(n / tile)) non-empty
+// splits.
+__device__ __forceinline__ int splits_with_data(int len, int tile, int S) {
+    const int nt = (len + tile - 1) / tile;
+    return nt < S ? nt : S;
+}
 
 // Partial-pass grids are one-dimensional and split-major: block
 // L = split * units + unit.  Consecutive blocks are dealt round-robin to the
@@ -68,7 +82,8 @@ hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stre
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
 
-// Workgroups of the LDS-staged kernel resident per CU (LDS ring size bound).
+// Workgroups of the LDS-staged kernel resident per CU (bound by the 160 KB
+// of LDS: rings of 32-token stages of 8, 16 or 32 KB for d = 64, 128, 256).
 inline int lds_groups_per_cu(int D) { return D == 256 ? 1 : (D == 128 ? 2 : 3); }
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
 

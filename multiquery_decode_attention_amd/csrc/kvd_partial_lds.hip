@@ -16,10 +16,12 @@
 // previous iteration before it is refilled.
 //
 // LDS layout of a stage: K rows then V rows, 32 rows of D bf16 each, in
-// 16-byte chunks.  Chunk p of K row t sits at position (p + t) mod (D/8) of
-// the row, so the score operand reads (16 lanes = 16 rows, one chunk each)
-// touch 16 different bank groups; V rows are read a row at a time (16 lanes
-// = 16 consecutive chunks of one row) and are stored as they are.  Rows past
+// 16-byte chunks.  Chunk p of K row t sits at position p ^ (t & SWZ) of the
+// row (SWZ = 15, or 7 for d = 64), so the score operand reads (16 lanes = 16
+// rows, one chunk each) touch 16 different bank groups while every aligned
+// group of 16 chunks -- the 256 bytes a quarter-wave loads -- stays within
+// its own two cache lines; V rows are read a row at a time (16 lanes = 16
+// consecutive chunks of one row) and are stored as they are.  Rows past
 // the split's end are loaded as copies of its last valid row and masked out
 // of the softmax.
 //
@@ -62,28 +64,33 @@ __device__ __forceinline__ int wave_index() {
 // True when the predicate holds in any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
-template <int PERW>
+// Wait until at most `stages_after` stages of this wave's loads (PERW
+// each) are still in flight, then meet the workgroup at the barrier.
+template <int PERW, int MAXA>
 __device__ __forceinline__ void wait_stage(int stages_after) {
+    static_assert(MAXA >= 0 && MAXA <= 6, "ring depth");
     switch (stages_after) {
         case 0: wait_vm_barrier<0>(); break;
-        case 1: wait_vm_barrier<PERW>(); break;
-        case 2: wait_vm_barrier<2 * PERW>(); break;
-        case 3: wait_vm_barrier<3 * PERW>(); break;
-        case 4: wait_vm_barrier<4 * PERW>(); break;
-        default: wait_vm_barrier<5 * PERW>(); break;
+        case 1: wait_vm_barrier<(MAXA >= 1) * PERW>(); break;
+        case 2: wait_vm_barrier<(MAXA >= 2) * 2 * PERW>(); break;
+        case 3: wait_vm_barrier<(MAXA >= 3) * 3 * PERW>(); break;
+        case 4: wait_vm_barrier<(MAXA >= 4) * 4 * PERW>(); break;
+        case 5: wait_vm_barrier<(MAXA >= 5) * 5 * PERW>(); break;
+        default: wait_vm_barrier<(MAXA >= 6) * 6 * PERW>(); break;
     }
 }
 
 template <int D, int NS>
 __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int head_groups) {
     constexpr int CH = D / 8;                        // 16-byte chunks per row
+    constexpr int SWZ = (CH < 16 ? CH : 16) - 1;     // K chunk swizzle mask
     constexpr int KS = D / 32;                       // k-steps of the score product
     constexpr int NE = D / 16;                       // output column blocks per lane
     constexpr int REGION = MFMA_TILE * D * 2;        // bytes of K (or V) per stage
     constexpr int STAGE = 2 * REGION;
     constexpr int PERW = STAGE / (4 * 64 * 16);      // loads per wave per stage (= D/32)
     constexpr float TAU = 8.f;                       // rescale threshold (base-2 exponent)
-    static_assert(NS >= 2 && NS - 2 <= 5, "ring depth");
+    static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
     __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
 
     // unit = (sequence b, KV head g, head group hg), head group fastest
@@ -97,10 +104,13 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         if (s == 0 && g == 0 && hg == 0 && threadIdx.x == 0) atomicOr(a.err, ERRBIT_LENGTH);
         len = len < 0 ? 0 : a.T_cap;
     }
-    const int t_begin = s * a.chunk;
-    if (t_begin >= len) return;  // whole workgroup: before any barrier
-    const int t_end = min(t_begin + a.chunk, len);
-    const int n_tiles = (t_end - t_begin + MFMA_TILE - 1) / MFMA_TILE;
+    const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
+    if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
+    const int t_end = len;
+    // this split owns the sequence's tiles s, s+S, s+2S, ...
+    const int n_tiles = (n_seq_tiles - s + a.S - 1) / a.S;
+    const int tstride = a.S * MFMA_TILE;
+    const int t_first = s * MFMA_TILE;
 
     const int wave = wave_index();
     const int lane = threadIdx.x & 63;
@@ -136,11 +146,11 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         const bool is_v = j0 >= MFMA_TILE * CH;
         const int j = (is_v ? j0 - MFMA_TILE * CH : j0) + lane;
         const int t = j / CH;
-        const int p = is_v ? j % CH : (j - t + CH * 64) % CH;  // K: position q holds chunk q - t
+        const int p = is_v ? j % CH : (j % CH) ^ (t & SWZ);  // K: position q holds chunk q ^ (t & SWZ)
         doff[n] = (uint32_t)((t * CH + p) * 16);
     }
     auto issue = [&](int tile) {
-        const int t0 = t_begin + tile * MFMA_TILE;
+        const int t0 = t_first + tile * tstride;
         unsigned char* stage = lds + (tile % NS) * STAGE;
         if (t0 + MFMA_TILE <= t_end) {
 #pragma unroll
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int t = 16 * sb + c;
-            koff[sb][ks] = (uint32_t)((t * CH + ((4 * ks + gq + t) % CH)) * 16);
+            koff[sb][ks] = (uint32_t)((t * CH + ((4 * ks + gq) ^ (t & SWZ))) * 16);
         }
     }
 
@@ -183,17 +193,17 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, l_run = 0.f;
 
-    // The prologue always requests NS-1 tiles (tiles past the split re-read
-    // its last rows and are never consumed), so the number of loads issued
-    // after the queries is a compile-time constant for the compiler's own
-    // wait on them.
+    // The prologue always requests NS-1 tiles (tiles past the split's last
+    // re-read the sequence's last row and are never consumed), so the number
+    // of loads issued after the queries is a compile-time constant for the
+    // compiler's own wait on them.
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) issue(i);
 
     if (nh == 0) {
         // a wave with no heads of its own still loads its share of every tile
         for (int it = 0; it < n_tiles; ++it) {
-            wait_stage<PERW>(min(n_tiles - 1, it + NS - 2) - it);
+            wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
             if (it + NS - 1 < n_tiles) issue(it + NS - 1);
         }
         return;
@@ -201,12 +211,12 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 
     for (int it = 0; it < n_tiles; ++it) {
         // loads issued after tile `it`: tiles it+1 .. min(it+NS-2, n_tiles-1)
-        wait_stage<PERW>(min(n_tiles - 1, it + NS - 2) - it);
+        wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
         if (it + NS - 1 < n_tiles) issue(it + NS - 1);
 
         const unsigned char* Kl = lds + (it % NS) * STAGE;
         const unsigned char* Vl = Kl + REGION;
-        const int t0 = t_begin + it * MFMA_TILE;
+        const int t0 = t_first + it * tstride;
 
         f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -320,11 +330,22 @@ hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Ring depth per head dim (stages of 32 tokens: 8, 16 and 32 KB).
+#ifndef KVD_LDS_STAGES_64
+#define KVD_LDS_STAGES_64 6
+#endif
+#ifndef KVD_LDS_STAGES_128
+#define KVD_LDS_STAGES_128 4
+#endif
+#ifndef KVD_LDS_STAGES_256
+#define KVD_LDS_STAGES_256 5
+#endif
+
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 64: return launch_d<64, 6>(a, stream);
-        case 128: return launch_d<128, 4>(a, stream);
-        case 256: return launch_d<256, 5>(a, stream);
+        case 64: return launch_d<64, KVD_LDS_STAGES_64>(a, stream);
+        case 128: return launch_d<128, KVD_LDS_STAGES_128>(a, stream);
+        case 256: return launch_d<256, KVD_LDS_STAGES_256>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -121,9 +121,10 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
         if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(a.err, ERRBIT_LENGTH);
         len = len < 0 ? 0 : a.T_cap;
     }
-    const int t_begin = s * a.chunk;
-    if (t_begin >= len) return;
-    const int t_end = min(t_begin + a.chunk, len);
+    const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
+    if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
+    const int t_end = len;
+    const int tstride = a.S * MFMA_TILE;  // this split owns tiles s, s+S, ...
 
     const int lane = threadIdx.x & 63;
     const int c = lane & 15;   // row/column index inside the 16x16 tile
@@ -153,11 +154,11 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
     float l_run = 0.f;        // this lane's share of the running sum
 
     TileRegs<D> r;
-    load_tile<D>(r, kb, vb, t_begin, t_end, c, gq, true);
-    load_tile<D>(r, kb, vb, t_begin, t_end, c, gq, false);
+    load_tile<D>(r, kb, vb, s * MFMA_TILE, t_end, c, gq, true);
+    load_tile<D>(r, kb, vb, s * MFMA_TILE, t_end, c, gq, false);
 
-    for (int t0 = t_begin; t0 < t_end; t0 += MFMA_TILE) {
-        const int tn = t0 + MFMA_TILE;
+    for (int t0 = s * MFMA_TILE; t0 < t_end; t0 += tstride) {
+        const int tn = t0 + tstride;
         f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {

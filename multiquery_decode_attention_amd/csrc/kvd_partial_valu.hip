@@ -49,9 +49,8 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         if (s == 0 && h == 0 && lane == 0) atomicOr(a.err, ERRBIT_LENGTH);
         len = len < 0 ? 0 : a.T_cap;
     }
-    const int t_begin = s * a.chunk;
-    if (t_begin >= len) return;
-    const int t_end = min(t_begin + a.chunk, len);
+    const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
+    if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
     const int g = h / a.M;  // query head h reads KV head floor(h / M)
 
     __shared__ float qs[D];
@@ -68,10 +67,11 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int t0 = t_begin; t0 < t_end; t0 += VALU_TILE) {
+    for (int tile = s; tile < n_seq_tiles; tile += a.S) {
+        const int t0 = tile * VALU_TILE;
         const int t = t0 + lane;
         float x = -INFINITY;
-        if (t < t_end) {
+        if (t < len) {
             const T* kr = kb + (size_t)t * D;
             float dot = 0.f;
 #pragma unroll 8
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         m_run = m_new;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) acc[k] *= alpha;
-        const int nt = min(VALU_TILE, t_end - t0);
+        const int nt = min(VALU_TILE, len - t0);
         for (int j = 0; j < nt; ++j) {
             const float pj = __shfl(p, j);
             const T* vr = vb + (size_t)(t0 + j) * D;

@@ -51,9 +51,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 struct Plan {
     int variant;
-    int tile;
-    int splits;
-    int chunk;
+    int tile;    // tokens per tile of the chosen partial kernel
+    int splits;  // S: split s owns tiles s, s+S, ... of each sequence
+    int chunk;   // most tokens any split holds for a full cache
 };
 
 int resolve_variant(const kvdecode_s* h) {
@@ -61,11 +61,11 @@ int resolve_variant(const kvdecode_s* h) {
     return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
 }
 
-// Split planner.  The grid is (splits, KV heads [x head groups], sequences);
+// Split planner.  The grid is splits x (sequences, KV heads [, head groups]);
 // lengths live on the device, so the plan is made for full caches and splits
-// past a sequence's length exit at once.  For every candidate split count S
-// the cost model charges
-//   rounds(S) * (bytes of one split + a fixed fill cost) * resident slots
+// with no tile of a sequence exit at once.  For every candidate split count
+// S the cost model charges
+//   rounds(S) * (bytes of the busiest split + a fixed fill cost) * slots
 //     + fp32 partial traffic (written by the partial pass, read by combine)
 // where rounds(S) = ceil(work units * S / resident slots): a launch whose
 // last round is partly empty wastes the rest of that round.  Among plans
@@ -101,15 +101,13 @@ Plan make_plan(const kvdecode_s* h) {
     Plan p;
     p.variant = resolve_variant(h);
     p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
-    const long long T = h->d.capacity;
-    const int max_splits = (int)((T + p.tile - 1) / p.tile);
-    auto finish = [&](int s) {
+    const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
+    // tiles are dealt round-robin: a split holds at most ceil(n_tiles / S)
+    auto finish = [&](long long s) {
         if (s < 1) s = 1;
-        if (s > max_splits) s = max_splits;
-        long long chunk = (T + s - 1) / s;
-        chunk = (chunk + p.tile - 1) / p.tile * p.tile;
-        p.chunk = (int)chunk;
-        p.splits = (int)((T + chunk - 1) / chunk);
+        if (s > n_tiles) s = n_tiles;
+        p.splits = (int)s;
+        p.chunk = (int)((n_tiles + s - 1) / s * p.tile);
     };
     if (h->forced_splits > 0) {
         finish(h->forced_splits);
@@ -121,17 +119,15 @@ Plan make_plan(const kvdecode_s* h) {
     const double part_bytes = (double)h->M * (h->d.head_dim + 1) * 4 * 2;
     double best = 0;
     std::vector<std::pair<int, double>> cand;
-    int prev_chunk = -1;
-    for (int s = 1; s <= max_splits; ++s) {
-        long long chunk = (T + s - 1) / s;
-        chunk = (chunk + p.tile - 1) / p.tile * p.tile;
-        if (chunk == prev_chunk) continue;
-        prev_chunk = (int)chunk;
-        const int splits = (int)((T + chunk - 1) / chunk);
-        const long long rounds = (sh.units * splits + sh.slots - 1) / sh.slots;
-        const double cost = (double)rounds * (chunk * tok_bytes + fill) * sh.slots +
-                            (double)sh.units * splits * part_bytes;
-        cand.emplace_back(splits, cost);
+    long long prev_per = -1;
+    for (long long s = 1; s <= n_tiles; ++s) {
+        const long long per = (n_tiles + s - 1) / s;  // tiles of the busiest split
+        if (per == prev_per) continue;
+        prev_per = per;
+        const long long rounds = (sh.units * s + sh.slots - 1) / sh.slots;
+        const double cost = (double)rounds * (per * p.tile * tok_bytes + fill) * sh.slots +
+                            (double)sh.units * s * part_bytes;
+        cand.emplace_back((int)s, cost);
         if (best == 0 || cost < best) best = cost;
     }
     int pick = 1;
@@ -299,7 +295,6 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
     a.M = h->M;
     a.D = h->d.head_dim;
     a.T_cap = h->d.capacity;
-    a.chunk = p.chunk;
     a.S = p.splits;
     a.scale_log2e = scale * kvd::LOG2E;
 
@@ -312,7 +307,7 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
     c.Hq = a.Hq;
     c.D = a.D;
     c.T_cap = a.T_cap;
-    c.chunk = p.chunk;
+    c.tile = p.tile;
     c.S = p.splits;
 
     const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;

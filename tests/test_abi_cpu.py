@@ -141,7 +141,9 @@ def test_plans_cover_the_cache(lib, name):
         tile = 64 if p["variant"] == "valu" else 32
         S, C = p["num_splits"], p["split_tokens"]
         assert C % tile == 0 and S >= 1
-        assert S * C >= w.T_cap and (S - 1) * C < w.T_cap
+        n_tiles = -(-w.T_cap // tile)
+        assert S * C >= w.T_cap and S <= n_tiles
+        assert C == -(-n_tiles // S) * tile  # round-robin tiles: the busiest split
         if forced:
             assert S <= forced or S == 1
         lib.kvdecode_destroy(h)
