@@ -99,8 +99,12 @@ def main():
     R = args.cache_copies or max(1, math.ceil(MIN_ROTATION_BYTES / kv_bytes_one))
     R = min(R, K + W)
     appends_per_copy = math.ceil((K + W) / R)
-    T_cap = w.T_cap + appends_per_copy
-    attended = inputs.attended_lengths(w)  # lengths after the first step's append
+    # Each copy starts appends_per_copy tokens short of the workload's lengths
+    # so that its last step attends exactly them: the cache capacity is the
+    # workload's own, and attended lengths stay within appends_per_copy of it.
+    T_cap = w.T_cap
+    final = inputs.attended_lengths(w)
+    attended = (final - (appends_per_copy - 1)).clamp(min=1)  # after the first append
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T={w.T} dtype={w.dtype}; "
         f"{R} cache copies of {kv_bytes_one / 1e6:.0f} MB, capacity {T_cap}")
 
@@ -123,7 +127,7 @@ def main():
         c = copies[i % R]
         c["cache"].append(c["case"].k_new, c["case"].v_new)
         c["cache"].attend(c["case"].q, out=c["out"], scale=c["case"].scale)
-        c["len"] = [min(n + 1, T_cap) for n in c["len"]]
+        c["len"] = [n + 1 for n in c["len"]]
         return c["len"]
 
     for i in range(W):

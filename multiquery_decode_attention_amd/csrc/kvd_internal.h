@@ -82,9 +82,26 @@ hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stre
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
 
-// Workgroups of the LDS-staged kernel resident per CU (bound by the 160 KB
-// of LDS: rings of 32-token stages of 8, 16 or 32 KB for d = 64, 128, 256).
-inline int lds_groups_per_cu(int D) { return D == 256 ? 1 : (D == 128 ? 2 : 3); }
+// Ring depth (32-token stages) of the LDS-staged kernel per head dim.
+#ifndef KVD_LDS_STAGES_64
+#define KVD_LDS_STAGES_64 6
+#endif
+#ifndef KVD_LDS_STAGES_128
+#define KVD_LDS_STAGES_128 4
+#endif
+#ifndef KVD_LDS_STAGES_256
+#define KVD_LDS_STAGES_256 5
+#endif
+constexpr int LDS_BYTES_PER_CU = 160 * 1024;
+constexpr int lds_stages(int D) {
+    return D == 64 ? KVD_LDS_STAGES_64 : (D == 128 ? KVD_LDS_STAGES_128 : KVD_LDS_STAGES_256);
+}
+// Workgroups of the LDS-staged kernel resident per CU: a stage holds K and V
+// of 32 tokens (128*D bytes); the ring must fit the CU's 160 KB of LDS.
+inline int lds_groups_per_cu(int D) {
+    const int g = LDS_BYTES_PER_CU / (lds_stages(D) * 128 * D);
+    return g < 1 ? 1 : (g > 8 ? 8 : g);
+}
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
 
 // Waves per work unit of the MFMA partial pass for group size M.

@@ -125,15 +125,18 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k_cache) + slab);
     const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + slab);
 
-    // Queries of this wave's heads: B operand of the score product.
+    // Queries of this wave's heads: B operand of the score product.  Lanes
+    // past the wave's last head load a copy of its last row instead of a
+    // masked load: a row of P only feeds the same row of the output, which
+    // is never stored for those lanes, and unmasked loads let all of them
+    // be in flight at once.
     u32x4_t qop[KS];
     {
+        const int hq = hw0 + (head_ok ? c : max(nh - 1, 0));
         const uint16_t* qrow =
-            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hw0 + c) * D;
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hq) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qop[ks] = head_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq)
-                              : u32x4_t{0, 0, 0, 0};
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq);
     }
 
     // Loads of one stage: this wave's PERW loads cover LDS chunks
@@ -330,22 +333,11 @@ hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Ring depth per head dim (stages of 32 tokens: 8, 16 and 32 KB).
-#ifndef KVD_LDS_STAGES_64
-#define KVD_LDS_STAGES_64 6
-#endif
-#ifndef KVD_LDS_STAGES_128
-#define KVD_LDS_STAGES_128 4
-#endif
-#ifndef KVD_LDS_STAGES_256
-#define KVD_LDS_STAGES_256 5
-#endif
-
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 64: return launch_d<64, KVD_LDS_STAGES_64>(a, stream);
-        case 128: return launch_d<128, KVD_LDS_STAGES_128>(a, stream);
-        case 256: return launch_d<256, KVD_LDS_STAGES_256>(a, stream);
+        case 64: return launch_d<64, lds_stages(64)>(a, stream);
+        case 128: return launch_d<128, lds_stages(128)>(a, stream);
+        case 256: return launch_d<256, lds_stages(256)>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

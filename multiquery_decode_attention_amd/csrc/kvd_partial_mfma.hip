@@ -133,14 +133,15 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
     const bool head_ok = head < a.M;
 
     // Queries: B operand of the score product, k-slots 32ks + 8gq .. +7.
+    // Lanes past the group's last head load a copy of its last row (their
+    // output rows are never stored) so that no load needs a mask.
     u32x4_t qop[KS];
     {
+        const int hq = head_ok ? head : a.M - 1;
         const uint16_t* qrow =
-            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + head) * D;
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hq) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qop[ks] = head_ok ? *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq)
-                              : u32x4_t{0, 0, 0, 0};
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq);
     }
 
     const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.T_cap * D;
