@@ -192,7 +192,8 @@ int32_t ensure_events(kvdecode_s* h) {
     h->ev_append.resize(2 * (size_t)h->timing_cap, nullptr);
     for (auto* vec : {&h->ev_attend, &h->ev_append}) {
         for (hipEvent_t& ev : *vec) {
-            if (hipEventCreate(&ev) != hipSuccess) {
+            // timing only: no system-scope fence (cache writeback) at record
+            if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) {
                 ev = nullptr;
                 free_events(h);
                 return KVD_EHIP;
