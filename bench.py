@@ -4,7 +4,7 @@
 A step is the whole hot path for one decode step of one attention layer:
 append every sequence's new K/V token to its cache, then attend every query
 head over its sequence's valid prefix (split-KV partial pass + log-sum-exp
-combine).  Inputs are seeded synthetic tensors resident in HBM before the
+combine), issued as one kvdecode_append_attend call.  Inputs are seeded synthetic tensors resident in HBM before the
 timed region.  Several independent cache copies are cycled so that no step
 finds its cache in the 256 MB last-level cache (as in a model whose other
 layers' caches are read in between).
@@ -138,12 +138,12 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     for c in copies:
         cs = c["case"]
-        c["args_append"] = (c["cache"].handle, cs.k_new.data_ptr(), cs.v_new.data_ptr(), stream)
-        c["args_attend"] = (c["cache"].handle, cs.q.data_ptr(), c["out"].data_ptr(), float(cs.scale), stream)
+        c["args"] = (c["cache"].handle, cs.k_new.data_ptr(), cs.v_new.data_ptr(), cs.q.data_ptr(),
+                     c["out"].data_ptr(), float(cs.scale), stream)
 
     def step(i):
         c = copies[i % R]
-        rc = lib.kvdecode_append(*c["args_append"]) or lib.kvdecode_attend(*c["args_attend"])
+        rc = lib.kvdecode_append_attend(*c["args"])  # append, then attend
         if rc:
             raise kvd.KvdError(rc, "decode step")
         c["len"] = [n + 1 for n in c["len"]]

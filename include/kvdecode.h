@@ -131,6 +131,19 @@ int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void
 int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream);
 
 /*
+ * One decode step: exactly kvdecode_append(h, k_new, v_new) followed by
+ * kvdecode_attend(h, q, out, scale) -- same results, same cache contents,
+ * same lengths update, same sticky errors -- in fewer launches: with the
+ * LDS kernel the append is folded into the partial pass (the new token's
+ * row is read from k_new/v_new directly and written to its cache slot
+ * alongside), and the combine advances lengths.
+ * Same page, section "Implementation: JetStream": generate emits one token
+ * per batch item and appends its single-token KV cache.
+ */
+int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_new, const void* q,
+                               void* out, float scale, void* stream);
+
+/*
  * Synchronise `stream`, then report and clear the sticky device error:
  * KVD_OK, KVD_ECAPACITY or KVD_ELENGTH (capacity is reported first when both
  * occurred).  Returns KVD_OK without a device call if the handle has never

@@ -23,7 +23,8 @@ __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
-    "kvdecode_append", "kvdecode_attend", "kvdecode_status", "kvdecode_set_num_splits",
+    "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_status",
+    "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
     "LIB_PATH",
@@ -40,7 +41,8 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libkvdecode.so")
 
 EXPORTS = (
-    "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_status",
+    "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
+    "kvdecode_status",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
 )
@@ -83,6 +85,7 @@ def library():
         "kvdecode_create": (I, [ctypes.POINTER(kvdecode_desc_t), ctypes.POINTER(P)]),
         "kvdecode_append": (I, [P, P, P, P]),
         "kvdecode_attend": (I, [P, P, P, F, P]),
+        "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
         "kvdecode_status": (I, [P, P]),
         "kvdecode_set_num_splits": (I, [P, I]),
         "kvdecode_set_variant": (I, [P, I]),
@@ -155,6 +158,13 @@ def kvdecode_append(h: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=Non
 def kvdecode_attend(h: int, q: torch.Tensor, out: torch.Tensor, scale: float, stream=None) -> None:
     _check(library().kvdecode_attend(h, _ptr(q), _ptr(out), float(scale), _stream_ptr(stream)),
            "kvdecode_attend")
+
+
+def kvdecode_append_attend(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                           out: torch.Tensor, scale: float, stream=None) -> None:
+    _check(library().kvdecode_append_attend(h, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                            float(scale), _stream_ptr(stream)),
+           "kvdecode_append_attend")
 
 
 def kvdecode_status(h: int, stream=None) -> int:
@@ -232,6 +242,19 @@ class KVCache:
         else:
             self._check_token(out, self.Hq, "out")
         kvdecode_attend(self.handle, q, out, self.D ** -0.5 if scale is None else scale, stream)
+        return out
+
+    def step(self, k_new, v_new, q, out=None, scale=None, stream=None):
+        """append(k_new, v_new) then attend(q), in one call."""
+        self._check_token(k_new, self.Hkv, "k_new")
+        self._check_token(v_new, self.Hkv, "v_new")
+        self._check_token(q, self.Hq, "q")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            self._check_token(out, self.Hq, "out")
+        kvdecode_append_attend(self.handle, k_new, v_new, q, out,
+                               self.D ** -0.5 if scale is None else scale, stream)
         return out
 
     def status(self, stream=None) -> int:

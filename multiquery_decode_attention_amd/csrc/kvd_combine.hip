@@ -43,8 +43,12 @@ template <typename T>
 __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int lane = threadIdx.x;
-    int len = a.lengths[b];
-    len = len < 0 ? 0 : (len > a.T_cap ? a.T_cap : len);
+    const int len = a.len_att[b];
+    if (a.fused_append && h == 0 && lane == 0) {
+        // the only reader and writer of lengths[b] in this launch
+        const int l0 = a.lengths[b];
+        if (l0 >= 0 && l0 < a.T_cap) a.lengths[b] = l0 + 1;
+    }
     const int nsplit = splits_with_data(len, a.tile, a.S);
     T* orow = static_cast<T*>(a.out);
     const size_t obase = ((size_t)b * a.Hq + h) * a.D;

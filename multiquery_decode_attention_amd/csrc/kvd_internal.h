@@ -30,6 +30,12 @@ struct PartialArgs {
     float* o_part;          // [B, Hq, S, D] normalised partial outputs
     float* lse_part;        // [B, Hq, S]    base-2 log-sum-exp of each split
     int* err;               // sticky error word
+    int* len_att;           // [B] attended length of each sequence, for the combine
+    // Fused append (LDS kernel only; null otherwise): the new token's K/V,
+    // [B, Hkv, D].  Slot lengths[b] of the cache receives them and the pass
+    // attends lengths[b] + 1 tokens; lengths itself is advanced by the combine.
+    const void* k_new;
+    const void* v_new;
     int B, Hq, Hkv, M, D, T_cap;
     int S;                  // splits per (sequence, KV head): split s owns the
                             // kernel's token tiles s, s+S, s+2S, ...
@@ -39,7 +45,9 @@ struct PartialArgs {
 struct CombineArgs {
     const float* o_part;
     const float* lse_part;
-    const int32_t* lengths;
+    const int* len_att;     // [B] attended lengths written by the partial pass
+    int32_t* lengths;       // advanced here after a fused append (else untouched)
+    int fused_append;
     void* out;              // [B, Hq, D]
     int B, Hq, D, T_cap;
     int tile;               // tokens per tile of the partial kernel that ran
@@ -53,6 +61,36 @@ struct CombineArgs {
 // of full tiles, and only the split holding the sequence's last tile sees a
 // partial one.  A sequence of n tokens has min(S, ceil(n / tile)) non-empty
 // splits.
+// Length bookkeeping shared by the partial kernels: reads lengths[b],
+// reports out-of-range lengths and (for a fused append) a full cache, and
+// returns the number of tokens to attend.  `appended` tells whether the
+// fused append takes slot lengths[b].  The first block of the sequence also
+// records the attended length for the combine.
+struct SeqLen {
+    int len;       // tokens attended
+    int slot;      // slot of the appended token (when appended)
+    bool appended;
+};
+__device__ __forceinline__ SeqLen sequence_length(const int32_t* lengths, int* err, int* len_att,
+                                                  int b, int T_cap, bool fused, bool lead) {
+    const int l0 = lengths[b];
+    SeqLen r;
+    r.slot = l0;
+    r.appended = false;
+    if (l0 < 0 || l0 > T_cap) {
+        if (lead) atomicOr(err, ERRBIT_LENGTH);
+        r.len = l0 < 0 ? 0 : T_cap;
+    } else if (fused) {
+        r.appended = l0 < T_cap;
+        if (!r.appended && lead) atomicOr(err, ERRBIT_CAPACITY);
+        r.len = r.appended ? l0 + 1 : l0;
+    } else {
+        r.len = l0;
+    }
+    if (lead) len_att[b] = r.len;
+    return r;
+}
+
 __device__ __forceinline__ int splits_with_data(int len, int tile, int S) {
     const int nt = (len + tile - 1) / tile;
     return nt < S ? nt : S;
@@ -103,6 +141,7 @@ inline int lds_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
+
 
 // Waves per work unit of the MFMA partial pass for group size M.
 inline int mfma_head_blocks(int M) { return (M + MFMA_HEADS - 1) / MFMA_HEADS; }

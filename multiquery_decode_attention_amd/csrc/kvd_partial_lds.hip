@@ -99,11 +99,9 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const int hg = bc.unit % head_groups;
     const int g = (bc.unit / head_groups) % a.Hkv;
     const int b = bc.unit / (head_groups * a.Hkv);
-    int len = a.lengths[b];
-    if (len < 0 || len > a.T_cap) {
-        if (s == 0 && g == 0 && hg == 0 && threadIdx.x == 0) atomicOr(a.err, ERRBIT_LENGTH);
-        len = len < 0 ? 0 : a.T_cap;
-    }
+    const SeqLen sl = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
+                                      s == 0 && g == 0 && hg == 0 && threadIdx.x == 0);
+    const int len = sl.len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
     if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
     const int t_end = len;
@@ -124,6 +122,27 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.T_cap * D;
     const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k_cache) + slab);
     const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + slab);
+
+    // Fused append.  The new token is the sequence's last, so only the split
+    // owning its tile reads that slot in this launch, and it takes the row
+    // straight from k_new/v_new (below); the cache slot itself is written
+    // here with ordinary stores that nothing in this launch waits for.
+    const char* knew = nullptr;
+    const char* vnew = nullptr;
+    if (sl.appended) {
+        const size_t nrow = ((size_t)b * a.Hkv + g) * D * 2;
+        knew = static_cast<const char*>(a.k_new) + nrow;
+        vnew = static_cast<const char*>(a.v_new) + nrow;
+        if (hg == 0 && s == (sl.slot / MFMA_TILE) % a.S && threadIdx.x < 2 * CH) {
+            const bool v_half = threadIdx.x >= CH;
+            const int ch = v_half ? threadIdx.x - CH : threadIdx.x;
+            const u32x4_t x = *reinterpret_cast<const u32x4_t*>((v_half ? vnew : knew) + ch * 16);
+            char* dst = const_cast<char*>(v_half ? vb : kb) + (size_t)sl.slot * D * 2 + ch * 16;
+            *reinterpret_cast<u32x4_t*>(dst) = x;
+        }
+    }
+    // tiles ending at or before this token need no redirection
+    const int t_fast_end = sl.appended ? sl.slot : t_end;
 
     // Queries of this wave's heads: B operand of the score product.  Lanes
     // past the wave's last head load a copy of its last row instead of a
@@ -155,7 +174,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     auto issue = [&](int tile) {
         const int t0 = t_first + tile * tstride;
         unsigned char* stage = lds + (tile % NS) * STAGE;
-        if (t0 + MFMA_TILE <= t_end) {
+        if (t0 + MFMA_TILE <= t_fast_end) {
 #pragma unroll
             for (int n = 0; n < PERW; ++n) {
                 const int j0 = (wave * PERW + n) * 64;
@@ -166,15 +185,19 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                                                  (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
             }
         } else {
-            // last, partial tile: rows past the end re-read the last valid row
+            // the sequence's last tile: rows past the end re-read the last
+            // valid row, and the appended token's row comes from k_new/v_new
 #pragma unroll
             for (int n = 0; n < PERW; ++n) {
                 const int j0 = (wave * PERW + n) * 64;
-                const char* base = (j0 >= MFMA_TILE * CH ? vb : kb) + (size_t)t0 * (D * 2);
+                const bool is_v = j0 >= MFMA_TILE * CH;
+                const char* base = (is_v ? vb : kb) + (size_t)t0 * (D * 2);
                 const int t = (int)(doff[n] / (D * 2));
                 const int row = min(t, t_end - 1 - t0);
-                __builtin_amdgcn_global_load_lds((const void*)(base + (int)doff[n] + (row - t) * (D * 2)),
-                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+                const char* src = base + (int)doff[n] + (row - t) * (D * 2);
+                if (sl.appended && t0 + row == sl.slot)
+                    src = (is_v ? vnew : knew) + ((int)doff[n] - t * (D * 2));
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
             }
         }
     };

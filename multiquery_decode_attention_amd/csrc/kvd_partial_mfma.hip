@@ -116,11 +116,8 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
     const int b = bc.unit / (hb_groups * a.Hkv);
     const int hb = hbg * NW + (int)(threadIdx.x >> 6);
     if (hb * MFMA_HEADS >= a.M) return;  // whole wave past the group's last head
-    int len = a.lengths[b];
-    if (len < 0 || len > a.T_cap) {
-        if (s == 0 && g == 0 && threadIdx.x == 0) atomicOr(a.err, ERRBIT_LENGTH);
-        len = len < 0 ? 0 : a.T_cap;
-    }
+    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
+                                    s == 0 && g == 0 && hbg == 0 && threadIdx.x == 0).len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
     if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
     const int t_end = len;

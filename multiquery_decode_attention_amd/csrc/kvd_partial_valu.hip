@@ -44,11 +44,8 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     const int h = bc.unit % a.Hq;
     const int b = bc.unit / a.Hq;
     const int lane = threadIdx.x;
-    int len = a.lengths[b];
-    if (len < 0 || len > a.T_cap) {
-        if (s == 0 && h == 0 && lane == 0) atomicOr(a.err, ERRBIT_LENGTH);
-        len = len < 0 ? 0 : a.T_cap;
-    }
+    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
+                                    s == 0 && h == 0 && lane == 0).len;
     const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
     if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
     const int g = h / a.M;  // query head h reads KV head floor(h / M)

@@ -146,9 +146,11 @@ int32_t ensure_device(kvdecode_s* h) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return KVD_EHIP;
     if (h->device >= 0) return dev == h->device ? KVD_OK : KVD_EINVAL;
-    e = hipMalloc(reinterpret_cast<void**>(&h->err), sizeof(int));
+    // err word followed by the per-sequence attended lengths
+    const size_t words = 1 + (size_t)h->d.batch;
+    e = hipMalloc(reinterpret_cast<void**>(&h->err), words * sizeof(int));
     if (e != hipSuccess) return hip_fail(e);
-    e = hipMemset(h->err, 0, sizeof(int));
+    e = hipMemset(h->err, 0, words * sizeof(int));
     if (e != hipSuccess) {
         (void)hipFree(h->err);
         h->err = nullptr;
@@ -199,6 +201,92 @@ int32_t ensure_events(kvdecode_s* h) {
                 return KVD_EHIP;
             }
         }
+    }
+    return KVD_OK;
+}
+
+int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st) {
+    const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
+    if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
+    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->d.lengths, h->err,
+                                      h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
+                                      h->elem, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed) {
+        if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
+        ++h->n_append;
+    }
+    return KVD_OK;
+}
+
+// One attend, optionally preceded by an append.  The LDS kernel folds the
+// append into its partial pass (the combine then advances lengths); the
+// other kernels launch the append kernel first.  Argument checks happen
+// before any device work.
+int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void* q, void* out,
+                 float scale, hipStream_t st) {
+    if (!q || !out) return KVD_EINVAL;
+    if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
+    if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
+    const Plan p = make_plan(h);
+    if (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    int32_t rc = ensure_device(h);
+    if (rc != KVD_OK) return rc;
+    if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
+    if ((rc = ensure_events(h)) != KVD_OK) return rc;
+    const bool with_append = k_new != nullptr;
+    const bool fused = with_append && p.variant == KVD_VARIANT_LDS;
+    if (with_append && !fused) {
+        if ((rc = launch_append_timed(h, k_new, v_new, st)) != KVD_OK) return rc;
+    }
+
+    kvd::PartialArgs a;
+    a.q = q;
+    a.k_cache = h->d.k_cache;
+    a.v_cache = h->d.v_cache;
+    a.lengths = h->d.lengths;
+    a.o_part = h->o_part;
+    a.lse_part = h->lse_part;
+    a.err = h->err;
+    a.len_att = h->err + 1;
+    a.k_new = fused ? k_new : nullptr;
+    a.v_new = fused ? v_new : nullptr;
+    a.B = h->d.batch;
+    a.Hq = h->d.num_q_heads;
+    a.Hkv = h->d.num_kv_heads;
+    a.M = h->M;
+    a.D = h->d.head_dim;
+    a.T_cap = h->d.capacity;
+    a.S = p.splits;
+    a.scale_log2e = scale * kvd::LOG2E;
+
+    kvd::CombineArgs c;
+    c.o_part = h->o_part;
+    c.lse_part = h->lse_part;
+    c.len_att = h->err + 1;
+    c.lengths = h->d.lengths;
+    c.fused_append = fused ? 1 : 0;
+    c.out = out;
+    c.B = a.B;
+    c.Hq = a.Hq;
+    c.D = a.D;
+    c.T_cap = a.T_cap;
+    c.tile = p.tile;
+    c.S = p.splits;
+
+    const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
+    hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
+    if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
+    hipError_t e = p.variant == KVD_VARIANT_LDS    ? kvd::launch_partial_lds(a, st)
+                   : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
+                                                   : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
+    e = kvd::launch_combine(c, h->d.dtype == KVD_BF16, st);
+    if (e != hipSuccess) return KVD_EHIP;
+    if (timed) {
+        if (hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
+        ++h->n_attend;
     }
     return KVD_OK;
 }
@@ -255,77 +343,20 @@ int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
-    if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->d.lengths, h->err,
-                                      h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
-                                      h->elem, st);
-    if (e != hipSuccess) return KVD_EHIP;
-    if (timed) {
-        if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
-        ++h->n_append;
-    }
-    return KVD_OK;
+    return launch_append_timed(h, k_new, v_new, static_cast<hipStream_t>(stream));
 }
 
 int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream) {
     if (!is_live(h)) return KVD_EINVAL;
-    if (!q || !out) return KVD_EINVAL;
-    if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
-    if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
-    const Plan p = make_plan(h);
-    if (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
-    int32_t rc = ensure_device(h);
-    if (rc != KVD_OK) return rc;
-    if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
-    if ((rc = ensure_events(h)) != KVD_OK) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    return run_step(h, nullptr, nullptr, q, out, scale, static_cast<hipStream_t>(stream));
+}
 
-    kvd::PartialArgs a;
-    a.q = q;
-    a.k_cache = h->d.k_cache;
-    a.v_cache = h->d.v_cache;
-    a.lengths = h->d.lengths;
-    a.o_part = h->o_part;
-    a.lse_part = h->lse_part;
-    a.err = h->err;
-    a.B = h->d.batch;
-    a.Hq = h->d.num_q_heads;
-    a.Hkv = h->d.num_kv_heads;
-    a.M = h->M;
-    a.D = h->d.head_dim;
-    a.T_cap = h->d.capacity;
-    a.S = p.splits;
-    a.scale_log2e = scale * kvd::LOG2E;
-
-    kvd::CombineArgs c;
-    c.o_part = h->o_part;
-    c.lse_part = h->lse_part;
-    c.lengths = h->d.lengths;
-    c.out = out;
-    c.B = a.B;
-    c.Hq = a.Hq;
-    c.D = a.D;
-    c.T_cap = a.T_cap;
-    c.tile = p.tile;
-    c.S = p.splits;
-
-    const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
-    hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
-    if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = p.variant == KVD_VARIANT_LDS    ? kvd::launch_partial_lds(a, st)
-                   : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
-                                                   : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
-    if (e != hipSuccess) return KVD_EHIP;
-    if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
-    e = kvd::launch_combine(c, h->d.dtype == KVD_BF16, st);
-    if (e != hipSuccess) return KVD_EHIP;
-    if (timed) {
-        if (hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
-        ++h->n_attend;
-    }
-    return KVD_OK;
+int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_new, const void* q,
+                               void* out, float scale, void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (!k_new || !v_new) return KVD_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_EALIGN;
+    return run_step(h, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream));
 }
 
 int32_t kvdecode_status(kvdecode_t h, void* stream) {

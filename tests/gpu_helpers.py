@@ -27,7 +27,7 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_step(case: inputs.Case, Hq: int, *, variant=None, splits=None, append=True,
-             lengths=None, k_cache=None, v_cache=None):
+             lengths=None, k_cache=None, v_cache=None, fused=False):
     """Append (optional) then attend on the GPU, on fresh device copies of
     the case's tensors (the case itself is never modified).  Returns (out,
     k_cache, v_cache, lengths, status, plan)."""
@@ -42,9 +42,13 @@ def gpu_step(case: inputs.Case, Hq: int, *, variant=None, splits=None, append=Tr
         if splits is not None:
             cache.set_num_splits(splits)
         plan = cache.plan()
-        if append:
-            cache.append(case.k_new.to(dev).contiguous(), case.v_new.to(dev).contiguous())
-        out = cache.attend(case.q.to(dev).contiguous(), scale=case.scale)
+        kn, vn = case.k_new.to(dev).contiguous(), case.v_new.to(dev).contiguous()
+        if append and fused:
+            out = cache.step(kn, vn, case.q.to(dev).contiguous(), scale=case.scale)
+        else:
+            if append:
+                cache.append(kn, vn)
+            out = cache.attend(case.q.to(dev).contiguous(), scale=case.scale)
         status = cache.status()
         torch.cuda.synchronize()
     finally:

@@ -94,6 +94,11 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_attend(h, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         assert lib.kvdecode_attend(h, FAKE, FAKE, bad, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append_attend(h, None, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append_attend(h, FAKE, FAKE + 8, FAKE, FAKE, 1.0, None) == kvd.KVD_EALIGN
+    assert lib.kvdecode_append_attend(h, FAKE, FAKE, None, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append_attend(h, FAKE, FAKE, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
+    assert lib.kvdecode_append_attend(h, FAKE, FAKE, FAKE, FAKE, float("nan"), None) == kvd.KVD_EINVAL
     assert lib.kvdecode_append(h, None, FAKE, None) == kvd.KVD_EINVAL
     assert lib.kvdecode_append(h, FAKE, FAKE + 8, None) == kvd.KVD_EALIGN
     # knobs

@@ -43,10 +43,26 @@ def check_case(case, Hq, name, **kw):
 
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
 def test_workload_full_size(name):
-    """Each named workload at its full size, all outputs checked."""
+    """Each named workload at its full size, all outputs checked, through
+    the one-call step (kvdecode_append_attend) the benchmark times and
+    through separate append and attend calls."""
     w = inputs.WORKLOADS[name]
     case = inputs.make_workload_case(w, device="cuda")
-    check_case(case, w.Hq, name)
+    check_case(case, w.Hq, name, fused=True)
+    check_case(case, w.Hq, name + "/separate")
+
+
+@pytest.mark.parametrize("variant", ["lds", "mfma", "valu"])
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_fused_step_matches_oracle(variant, splits):
+    """kvdecode_append_attend == append then attend: ragged lengths whose
+    new token lands on every position of a tile, at tile edges, and in
+    splits other than the first."""
+    lengths = [1, 2, 31, 32, 33, 63, 64, 65, 96, 100, 127, 128, 129, 200]
+    for dtype in (["bf16"] if variant != "valu" else ["bf16", "f32"]):
+        case = inputs.make_case(len(lengths), 48, 2, 128, 200, lengths, dtype, seed=77 + splits)
+        check_case(case, 48, f"fused {variant} splits={splits} {dtype}", fused=True,
+                   variant=VARIANTS[variant], splits=splits)
 
 
 @pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 3), ("llama13b_mha_bf16", 2),
@@ -112,15 +128,31 @@ def test_empty_sequences_and_poisoned_tails():
     check_case(case, Hq, "poisoned tails + append", lengths=L0)
 
 
-def test_capacity_overflow_reported_and_harmless():
+@pytest.mark.parametrize("fused", [False, True])
+def test_capacity_overflow_reported_and_harmless(fused):
     B, Hq, Hkv, D, T_cap = 3, 8, 2, 128, 64
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, [64, 64, 10], "bf16", seed=9)
     L0 = torch.tensor([64, 63, 9], dtype=torch.int32)  # sequence 0 is already full
-    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L0)
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L0, fused=fused)
     assert status == kvd.KVD_ECAPACITY
     assert L.cpu().tolist() == [64, 64, 10]
     ref, k2, v2, L2 = oracle_step(case, lengths=L0)
     assert L2.tolist() == [64, 64, 10]
+    assert np.array_equal(inputs.host_array(kc), k2) and np.array_equal(inputs.host_array(vc), v2)
+    assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
+
+
+def test_fused_step_with_out_of_range_length():
+    """A length past capacity: no append for that sequence, attention
+    clamped to capacity, KVD_ELENGTH; the other sequence steps normally."""
+    B, Hq, Hkv, D, T_cap = 2, 16, 1, 128, 96
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, [96, 41], "bf16", seed=12)
+    L_bad = torch.tensor([1000, 40], dtype=torch.int32)
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L_bad, fused=True, variant=kvd.KVD_VARIANT_LDS)
+    assert status == kvd.KVD_ELENGTH
+    assert L.cpu().tolist() == [1000, 41]
+    ref, k2, v2, _ = oracle_step(case, lengths=torch.tensor([96, 40], dtype=torch.int32))
+    # sequence 0 is full in the oracle's run, so it is not appended there either
     assert np.array_equal(inputs.host_array(kc), k2) and np.array_equal(inputs.host_array(vc), v2)
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
@@ -204,8 +236,12 @@ def test_cached_decode_equals_naive_recompute(dtype):
     cache = kvd.KVCache(kc, vc, L, Hq)
     rows = []
     for i in range(T):
-        cache.append(K[i][None].to(dev).contiguous(), V[i][None].to(dev).contiguous())
-        rows.append(cache.attend(Q[i][None].to(dev).contiguous(), scale=scale))
+        kn, vn, qi = (X[i][None].to(dev).contiguous() for X in (K, V, Q))
+        if i % 2:  # alternate the one-call step and separate calls
+            rows.append(cache.step(kn, vn, qi, scale=scale))
+        else:
+            cache.append(kn, vn)
+            rows.append(cache.attend(qi, scale=scale))
     assert cache.status() == kvd.KVD_OK
     cache.close()
     got = torch.cat(rows).double().cpu().numpy()
