@@ -10,7 +10,6 @@
 // Attention" of "All About Transformer Inference", section "Sharding the KV
 // cache", carried out inside one GPU.
 //
-// One wave per (head, sequence); each lane owns 4 consecutive columns.
 #include "kvd_internal.h"
 
 namespace kvd {
@@ -39,12 +38,24 @@ __device__ inline void store4(uint16_t* out, size_t i, float4 v) {
     *reinterpret_cast<uint2*>(out + i) = make_uint2(a | (b << 16), c | (d << 16));
 }
 
+// One workgroup per (head, sequence) of D/4 * G threads, G = min(1024/D,
+// splits) rounded so the workgroup is whole waves.  Thread t owns column
+// vector t % (D/4) (four columns) and split group t / (D/4): group k sums
+// splits k, k+G, ... so G loads per column are in flight at once; the G
+// partial sums meet in LDS.
+// Partials are read exactly once: non-temporal loads.
+__device__ inline float4 load4_once(const float* p) {
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 template <typename T>
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const int h = blockIdx.x, b = blockIdx.y;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int len = a.len_att[b];
-    if (a.fused_append && h == 0 && lane == 0) {
+    if (a.fused_append && h == 0 && tid == 0) {
         // the only reader and writer of lengths[b] in this launch
         const int l0 = a.lengths[b];
         if (l0 >= 0 && l0 < a.T_cap) a.lengths[b] = l0 + 1;
@@ -52,66 +63,79 @@ __global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
     const int nsplit = splits_with_data(len, a.tile, a.S);
     T* orow = static_cast<T*>(a.out);
     const size_t obase = ((size_t)b * a.Hq + h) * a.D;
-    const int nvec = a.D / 4;
+    const int nvec = a.D / 4;          // column vectors per row (16, 32 or 64)
+    const int G = a.groups;            // split groups
+    const int v = tid % nvec, sg = tid / nvec;
 
     if (nsplit == 0) {
-        for (int v = lane; v < nvec; v += 64) store4(orow, obase + 4 * v, make_float4(0.f, 0.f, 0.f, 0.f));
+        if (sg == 0) store4(orow, obase + 4 * v, make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
     const size_t prow = ((size_t)b * a.Hq + h) * a.S;
     const float* lse = a.lse_part + prow;
-    // Global maximum and normaliser over all splits (lane j holds split j of
-    // each block of 64).
+    // every wave finds the maximum and normaliser over all splits itself
     float L = -INFINITY;
     for (int j = lane; j < nsplit; j += 64) L = fmaxf(L, lse[j]);
     L = wave_max(L);
     float z = 0.f;
     for (int j = lane; j < nsplit; j += 64) z += exp2f(lse[j] - L);
     z = wave_sum(z);
-    const float inv_z = 1.f / z;
 
-    const float* op = a.o_part + prow * a.D;
-    // Wave-uniform loop (the weight shuffles below need every lane active);
-    // lanes past the row's last column vector only skip their loads/stores.
-    for (int v0 = 0; v0 < nvec; v0 += 64) {
-        const int v = v0 + lane;
-        const bool col_ok = v < nvec;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j0 = 0; j0 < nsplit; j0 += 64) {
-            const int jn = min(64, nsplit - j0);
-            const float wl = lane < jn ? exp2f(lse[j0 + lane] - L) : 0.f;
-            // eight independent partial loads in flight per lane
-            for (int u0 = 0; u0 < jn; u0 += 8) {
-                float4 o[8];
+    const float* op = a.o_part + prow * a.D + 4 * v;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int j = sg;
+    for (; j + 3 * G < nsplit; j += 4 * G) {
+        float4 o[4];
+        float w[4];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = j0 + u0 + u;
-                    o[u] = (col_ok && u0 + u < jn)
-                               ? *reinterpret_cast<const float4*>(op + (size_t)j * a.D + 4 * v)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float w = __shfl(wl, (u0 + u) & 63);
-                    acc.x = fmaf(w, o[u].x, acc.x);
-                    acc.y = fmaf(w, o[u].y, acc.y);
-                    acc.z = fmaf(w, o[u].z, acc.z);
-                    acc.w = fmaf(w, o[u].w, acc.w);
-                }
-            }
+        for (int u = 0; u < 4; ++u) {
+            o[u] = load4_once(op + (size_t)(j + u * G) * a.D);
+            w[u] = lse[j + u * G];
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float wu = exp2f(w[u] - L);
+            acc.x = fmaf(wu, o[u].x, acc.x);
+            acc.y = fmaf(wu, o[u].y, acc.y);
+            acc.z = fmaf(wu, o[u].z, acc.z);
+            acc.w = fmaf(wu, o[u].w, acc.w);
+        }
+    }
+    for (; j < nsplit; j += G) {
+        const float4 o = load4_once(op + (size_t)j * a.D);
+        const float wu = exp2f(lse[j] - L);
+        acc.x = fmaf(wu, o.x, acc.x);
+        acc.y = fmaf(wu, o.y, acc.y);
+        acc.z = fmaf(wu, o.z, acc.z);
+        acc.w = fmaf(wu, o.w, acc.w);
+    }
+
+    __shared__ float4 part[256];
+    if (G > 1) {
+        part[tid] = acc;
+        __syncthreads();
+    }
+    if (sg == 0) {
+        for (int k = 1; k < G; ++k) {
+            const float4 p = part[k * nvec + v];
+            acc.x += p.x;
+            acc.y += p.y;
+            acc.z += p.z;
+            acc.w += p.w;
+        }
+        const float inv_z = 1.f / z;
         acc.x *= inv_z;
         acc.y *= inv_z;
         acc.z *= inv_z;
         acc.w *= inv_z;
-        if (col_ok) store4(orow, obase + 4 * v, acc);
+        store4(orow, obase + 4 * v, acc);
     }
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream) {
-    dim3 grid(a.Hq, a.B), block(64);
+    dim3 grid(a.Hq, a.B), block(a.D / 4 * a.groups);
     if (bf16) hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, a);
     return hipGetLastError();

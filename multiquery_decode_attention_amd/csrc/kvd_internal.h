@@ -43,6 +43,7 @@ struct PartialArgs {
 };
 
 struct CombineArgs {
+    int groups;             // split groups per workgroup (threads = D/4 * groups)
     const float* o_part;
     const float* lse_part;
     const int* len_att;     // [B] attended lengths written by the partial pass
@@ -130,6 +131,15 @@ hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
 #ifndef KVD_LDS_STAGES_256
 #define KVD_LDS_STAGES_256 5
 #endif
+// V tiles of the LDS-staged kernel trail its K tiles by this many of the
+// split's tiles (see kvd_partial_lds.hip), per head dim.
+#ifndef KVD_LDS_V_LAG_256
+#define KVD_LDS_V_LAG_256 1
+#endif
+#ifndef KVD_LDS_V_LAG_SMALL
+#define KVD_LDS_V_LAG_SMALL 0
+#endif
+constexpr int lds_v_lag(int D) { return D == 256 ? KVD_LDS_V_LAG_256 : KVD_LDS_V_LAG_SMALL; }
 constexpr int LDS_BYTES_PER_CU = 160 * 1024;
 constexpr int lds_stages(int D) {
     return D == 64 ? KVD_LDS_STAGES_64 : (D == 128 ? KVD_LDS_STAGES_128 : KVD_LDS_STAGES_256);

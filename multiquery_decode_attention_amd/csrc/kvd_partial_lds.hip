@@ -80,7 +80,7 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
     }
 }
 
-template <int D, int NS>
+template <int D, int NS, int VL>
 __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int head_groups) {
     constexpr int CH = D / 8;                        // 16-byte chunks per row
     constexpr int SWZ = (CH < 16 ? CH : 16) - 1;     // K chunk swizzle mask
@@ -91,6 +91,8 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     constexpr int PERW = STAGE / (4 * 64 * 16);      // loads per wave per stage (= D/32)
     constexpr float TAU = 8.f;                       // rescale threshold (base-2 exponent)
     static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
+    static_assert(2 * MFMA_TILE * CH == 4 * PERW * 64 && MFMA_TILE * CH == 2 * PERW * 64,
+                  "waves 0-1 load K, waves 2-3 load V");
     __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
 
     // unit = (sequence b, KV head g, head group hg), head group fastest
@@ -171,14 +173,31 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         const int p = is_v ? j % CH : (j % CH) ^ (t & SWZ);  // K: position q holds chunk q ^ (t & SWZ)
         doff[n] = (uint32_t)((t * CH + p) * 16);
     }
-    auto issue = [&](int tile) {
+    // Stage st of the ring holds K of the split's tile st and V of its tile
+    // st - VL.  Waves 0-1 load the K half of every stage and waves 2-3 the V
+    // half.  A half whose tile does not exist (V of the first VL stages, K of
+    // the last VL) points every lane at one 16-byte chunk: the load count per
+    // stage stays fixed for the vmcnt bookkeeping, and one cached line costs
+    // no HBM traffic.
+    const bool v_wave = wave >= 2;
+    auto issue = [&](int st) {
+        unsigned char* stage = lds + (st % NS) * STAGE;
+        const int tile = v_wave ? st - VL : st;
+        const char* tbase = v_wave ? vb : kb;
+        if (tile < 0 || tile >= n_tiles) {
+#pragma unroll
+            for (int n = 0; n < PERW; ++n) {
+                const int j0 = (wave * PERW + n) * 64;
+                __builtin_amdgcn_global_load_lds((const void*)tbase, (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+            }
+            return;
+        }
         const int t0 = t_first + tile * tstride;
-        unsigned char* stage = lds + (tile % NS) * STAGE;
+        const char* base = tbase + (size_t)t0 * (D * 2);
         if (t0 + MFMA_TILE <= t_fast_end) {
 #pragma unroll
             for (int n = 0; n < PERW; ++n) {
                 const int j0 = (wave * PERW + n) * 64;
-                const char* base = (j0 >= MFMA_TILE * CH ? vb : kb) + (size_t)t0 * (D * 2);
                 // (the source must reach the builtin as const void*: with a
                 // char pointer the host pass drops the kernel's launch stub)
                 __builtin_amdgcn_global_load_lds((const void*)(base + doff[n]),
@@ -190,13 +209,11 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 #pragma unroll
             for (int n = 0; n < PERW; ++n) {
                 const int j0 = (wave * PERW + n) * 64;
-                const bool is_v = j0 >= MFMA_TILE * CH;
-                const char* base = (is_v ? vb : kb) + (size_t)t0 * (D * 2);
                 const int t = (int)(doff[n] / (D * 2));
                 const int row = min(t, t_end - 1 - t0);
                 const char* src = base + (int)doff[n] + (row - t) * (D * 2);
                 if (sl.appended && t0 + row == sl.slot)
-                    src = (is_v ? vnew : knew) + ((int)doff[n] - t * (D * 2));
+                    src = (v_wave ? vnew : knew) + ((int)doff[n] - t * (D * 2));
                 __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
             }
         }
@@ -219,69 +236,14 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, l_run = 0.f;
 
-    // The prologue always requests NS-1 tiles (tiles past the split's last
-    // re-read the sequence's last row and are never consumed), so the number
-    // of loads issued after the queries is a compile-time constant for the
-    // compiler's own wait on them.
-#pragma unroll
-    for (int i = 0; i < NS - 1; ++i) issue(i);
-
-    if (nh == 0) {
-        // a wave with no heads of its own still loads its share of every tile
-        for (int it = 0; it < n_tiles; ++it) {
-            wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
-            if (it + NS - 1 < n_tiles) issue(it + NS - 1);
-        }
-        return;
-    }
-
-    for (int it = 0; it < n_tiles; ++it) {
-        // loads issued after tile `it`: tiles it+1 .. min(it+NS-2, n_tiles-1)
-        wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
-        if (it + NS - 1 < n_tiles) issue(it + NS - 1);
-
-        const unsigned char* Kl = lds + (it % NS) * STAGE;
-        const unsigned char* Vl = Kl + REGION;
-        const int t0 = t_first + it * tstride;
-
-        f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(Kl + koff[0][ks]);
-            const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(Kl + koff[1][ks]);
-            sc[0] = mfma16x16x32(k0, qop[ks], sc[0]);
-            sc[1] = mfma16x16x32(k1, qop[ks], sc[1]);
-        }
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
-        if (t0 + MFMA_TILE > t_end) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (wave_any(mx > m_ref + TAU)) {
-            // raise the reference of the heads that outgrew it; rescale
-            const float m_new = mx > m_ref + TAU ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            l_run *= alpha;
-            m_ref = m_new;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * gq + i);
-#pragma unroll
-                for (int e = 0; e < NE; ++e) acc[e][i] *= ai;
-            }
-        }
+    // Probabilities of one tile's scores against the current reference,
+    // times that tile's V from LDS, into the accumulators; 128 columns (one
+    // 16-byte chunk per lane) at a time.
+    auto value_product = [&](const float (&xs)[8], const unsigned char* Vl) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
+            p[j] = __builtin_amdgcn_exp2f(xs[j] - m_ref);
             l_run += p[j];
         }
         u32x4_t pop;
@@ -289,7 +251,6 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         pop[1] = pack_bf16x2(p[2], p[3]);
         pop[2] = pack_bf16x2(p[4], p[5]);
         pop[3] = pack_bf16x2(p[6], p[7]);
-        // Value product, 128 columns (one 16-byte chunk per lane) at a time.
         if constexpr (D >= 128) {
 #pragma unroll
             for (int i = 0; i < D / 128; ++i) {
@@ -317,6 +278,89 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = mfma16x16x32(pop, v_operand(v, e), acc[e]);
         }
+    };
+
+    // The prologue always requests NS-1 stages (stages past the last are
+    // the one-chunk dummies), so the number of loads issued after the
+    // queries is a compile-time constant for the compiler's own wait on them.
+    const int n_stages = n_tiles + VL;
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(i);
+
+    if (nh == 0) {
+        // a wave with no heads of its own still loads its share of every stage
+        for (int it = 0; it < n_stages; ++it) {
+            wait_stage<PERW, NS - 2>(min(n_stages - 1, it + NS - 2) - it);
+            if (it + NS - 1 < n_stages) issue(it + NS - 1);
+        }
+        return;
+    }
+
+    // scores of the last VL tiles, waiting for their V (oldest first)
+    float xh[VL > 0 ? VL : 1][8];
+    for (int it = 0; it < n_stages; ++it) {
+        // loads issued after stage `it`: stages it+1 .. min(it+NS-2, n_stages-1)
+        wait_stage<PERW, NS - 2>(min(n_stages - 1, it + NS - 2) - it);
+        if (it + NS - 1 < n_stages) issue(it + NS - 1);
+
+        const unsigned char* Kl = lds + (it % NS) * STAGE;
+        const unsigned char* Vl = Kl + REGION;
+
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = -INFINITY;
+        if (it < n_tiles) {
+            const int t0 = t_first + it * tstride;
+            f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(Kl + koff[0][ks]);
+                const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(Kl + koff[1][ks]);
+                sc[0] = mfma16x16x32(k0, qop[ks], sc[0]);
+                sc[1] = mfma16x16x32(k1, qop[ks], sc[1]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
+            if (t0 + MFMA_TILE > t_end) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
+            }
+            float mx = x[0];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (wave_any(mx > m_ref + TAU)) {
+                // raise the reference of the heads that outgrew it and rescale
+                // what was accumulated with the old one (pending tiles are
+                // converted later, with whatever reference holds then)
+                const float m_new = mx > m_ref + TAU ? mx : m_ref;
+                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+                l_run *= alpha;
+                m_ref = m_new;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * gq + i);
+#pragma unroll
+                    for (int e = 0; e < NE; ++e) acc[e][i] *= ai;
+                }
+            }
+        }
+        if constexpr (VL > 0) {
+            float xp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xp[j] = xh[0][j];
+#pragma unroll
+            for (int k = 0; k + 1 < VL; ++k)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xh[k][j] = xh[k + 1][j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xh[VL - 1][j] = x[j];
+            if (it >= VL) value_product(xp, Vl);
+        } else {
+            value_product(x, Vl);
+        }
     }
 
     float l = l_run;
@@ -330,27 +374,25 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         if (r < nh) {
             const float inv = 1.f / li;
             float* orow = a.o_part + (row0 + (size_t)r * a.S) * D;
-            if constexpr (D >= 128) {
+            // Non-temporal stores: the partials are read once, by the
+            // combine; kept out of the caches' dirty lines they stream to
+            // memory instead of draining at the end of the launch.
 #pragma unroll
-                for (int e = 0; e < NE; e += 4) {
-                    float4 o = make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
-                                           acc[e + 3][i] * inv);
-                    *reinterpret_cast<float4*>(orow + owned_col<D>(c, e)) = o;
-                }
-            } else {
-                float4 o = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv);
-                *reinterpret_cast<float4*>(orow + owned_col<D>(c, 0)) = o;
+            for (int e = 0; e < NE; e += 4) {
+                const f32x4_t o = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv};
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4_t*>(orow + owned_col<D>(c, e)));
             }
         }
     }
-    if (gq == 0 && head_ok) a.lse_part[row0 + (size_t)c * a.S] = m_ref + __builtin_log2f(l);
+    if (gq == 0 && head_ok)
+        __builtin_nontemporal_store(m_ref + __builtin_log2f(l), a.lse_part + row0 + (size_t)c * a.S);
 }
 
 template <int D, int NS>
 hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 63) / 64;
     dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
-    hipLaunchKernelGGL((partial_lds_kernel<D, NS>), grid, dim3(256), 0, stream, a, groups);
+    hipLaunchKernelGGL((partial_lds_kernel<D, NS, lds_v_lag(D)>), grid, dim3(256), 0, stream, a, groups);
     return hipGetLastError();
 }
 

@@ -273,6 +273,13 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     c.T_cap = a.T_cap;
     c.tile = p.tile;
     c.S = p.splits;
+    {
+        // split groups: up to 256 threads, no more groups than splits, whole waves
+        const int nvec = a.D / 4;
+        int G = 256 / nvec;
+        while (G > 1 && G / 2 >= p.splits && (nvec * (G / 2)) % 64 == 0) G /= 2;
+        c.groups = G;
+    }
 
     const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
