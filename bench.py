@@ -126,6 +126,7 @@ def main():
         cache = kvd.KVCache(case.k_cache, case.v_cache, case.lengths0, w.Hq)
         cache.set_variant(variant)
         cache.set_num_splits(args.splits)
+        cache.reserve()  # device workspace allocated now, not inside the timed steps
         copies.append({"case": case, "cache": cache, "out": torch.empty_like(case.q),
                        "len": case.lengths0.cpu().tolist()})
     plan = copies[0]["cache"].plan()
@@ -142,12 +143,9 @@ def main():
                      c["out"].data_ptr(), float(cs.scale), stream)
 
     def step(i):
-        c = copies[i % R]
-        rc = lib.kvdecode_append_attend(*c["args"])  # append, then attend
+        rc = lib.kvdecode_append_attend(*copies[i % R]["args"])  # append, then attend
         if rc:
             raise kvd.KvdError(rc, "decode step")
-        c["len"] = [n + 1 for n in c["len"]]
-        return c["len"]
 
     for i in range(W):
         step(i)
@@ -157,16 +155,27 @@ def main():
         kvd.kvdecode_timing_enable(c["cache"].handle, K)
     torch.cuda.synchronize()
 
+    # Byte and FLOP counts of the timed steps, from the lengths each step
+    # attends (every step appends one token to each sequence of its copy);
+    # computed here so that the timed loop only issues the steps.
+    lens = [list(c["len"]) for c in copies]
+    for i in range(W):
+        lens[i % R] = [n + 1 for n in lens[i % R]]
     step_bytes = 0
     partial_bytes = 0
     flops = 0
-    t0 = time.perf_counter()
     for i in range(W, W + K):
-        L = step(i)
+        L = lens[i % R] = [n + 1 for n in lens[i % R]]
         step_bytes += traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L) + \
             traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
         partial_bytes += traffic.partial_pass_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L)
         flops += traffic.attend_flops(w.Hq, w.D, L)
+    for c, L in zip(copies, lens):
+        c["len"] = L  # the lengths each copy holds once the timed steps have run
+
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 

@@ -100,11 +100,22 @@ typedef struct {
  * descriptor (KVD_EINVAL / KVD_EUNSUPPORTED / KVD_EALIGN) and makes no HIP
  * call: the device workspace (split partials, error flag) is allocated on
  * the first append or attend, on the device current at that call, and that
- * device is then bound to the handle.  Later calls never allocate unless
- * kvdecode_set_num_splits asks for more splits than any earlier plan.
+ * device is then bound to the handle (or earlier, by kvdecode_reserve).
+ * Later calls never allocate unless kvdecode_set_num_splits asks for more
+ * splits than any earlier plan.
  * Limits: B <= 65535, Hkv <= 65535, T_cap <= 2^24.
  */
 int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out);
+
+/*
+ * Bind the handle to the current device now and allocate everything its
+ * current plan needs (workspace, error flag, and the event slots of
+ * kvdecode_timing_enable), which would otherwise happen on the first append
+ * or attend: lets a caller keep every hipMalloc out of its decode loop.
+ * KVD_EINVAL if the handle is already bound to another device; KVD_ENOMEM
+ * or KVD_EHIP if an allocation fails.  Idempotent.
+ */
+int32_t kvdecode_reserve(kvdecode_t h);
 
 /*
  * Append one token per sequence (the generate-side cache update).
@@ -134,9 +145,10 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
  * One decode step: exactly kvdecode_append(h, k_new, v_new) followed by
  * kvdecode_attend(h, q, out, scale) -- same results, same cache contents,
  * same lengths update, same sticky errors -- in fewer launches: with the
- * LDS kernel the append is folded into the partial pass (the new token's
- * row is read from k_new/v_new directly and written to its cache slot
- * alongside), and the combine advances lengths.
+ * LDS and VALU kernels the append is folded into the partial pass (the new
+ * token's row is read from k_new/v_new directly and written to its cache
+ * slot alongside), and the combine advances lengths; the MFMA kernel runs
+ * the append kernel first.
  * Same page, section "Implementation: JetStream": generate emits one token
  * per batch item and appends its single-token KV cache.
  */

@@ -24,7 +24,7 @@ __all__ = [
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_status",
-    "kvdecode_set_num_splits",
+    "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
     "LIB_PATH",
@@ -42,7 +42,7 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
 
 EXPORTS = (
     "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
-    "kvdecode_status",
+    "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
 )
@@ -87,6 +87,7 @@ def library():
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
         "kvdecode_status": (I, [P, P]),
+        "kvdecode_reserve": (I, [P]),
         "kvdecode_set_num_splits": (I, [P, I]),
         "kvdecode_set_variant": (I, [P, I]),
         "kvdecode_get_plan": (I, [P, IP, IP, IP]),
@@ -170,6 +171,10 @@ def kvdecode_append_attend(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: 
 def kvdecode_status(h: int, stream=None) -> int:
     """Sync the stream and return (and clear) the sticky device status code."""
     return library().kvdecode_status(h, _stream_ptr(stream))
+
+
+def kvdecode_reserve(h: int) -> None:
+    _check(library().kvdecode_reserve(h), "kvdecode_reserve")
 
 
 def kvdecode_set_num_splits(h: int, n: int) -> None:
@@ -259,6 +264,10 @@ class KVCache:
 
     def status(self, stream=None) -> int:
         return kvdecode_status(self.handle, stream)
+
+    def reserve(self):
+        """Bind to the current device and allocate the workspace now."""
+        kvdecode_reserve(self.handle)
 
     def set_num_splits(self, n: int):
         kvdecode_set_num_splits(self.handle, n)

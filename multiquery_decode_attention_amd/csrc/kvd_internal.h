@@ -43,7 +43,7 @@ struct PartialArgs {
 };
 
 struct CombineArgs {
-    int groups;             // split groups per workgroup (threads = D/4 * groups)
+    int groups;             // split groups per row (set by the launcher)
     const float* o_part;
     const float* lse_part;
     const int* len_att;     // [B] attended lengths written by the partial pass
@@ -126,7 +126,7 @@ hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
 #define KVD_LDS_STAGES_64 6
 #endif
 #ifndef KVD_LDS_STAGES_128
-#define KVD_LDS_STAGES_128 4
+#define KVD_LDS_STAGES_128 3
 #endif
 #ifndef KVD_LDS_STAGES_256
 #define KVD_LDS_STAGES_256 5

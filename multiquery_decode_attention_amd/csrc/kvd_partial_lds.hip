@@ -180,6 +180,11 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     // stage stays fixed for the vmcnt bookkeeping, and one cached line costs
     // no HBM traffic.
     const bool v_wave = wave >= 2;
+    // Cache policy of the K/V loads: non-temporal.  Every cache byte is read
+    // once per launch, and streaming it past the caches measured up to 14%
+    // faster out of HBM than ordinary loads (the dummy loads above stay
+    // cacheable: they are meant to hit).
+    constexpr int KV_POLICY = 2;
     auto issue = [&](int st) {
         unsigned char* stage = lds + (st % NS) * STAGE;
         const int tile = v_wave ? st - VL : st;
@@ -201,7 +206,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                 // (the source must reach the builtin as const void*: with a
                 // char pointer the host pass drops the kernel's launch stub)
                 __builtin_amdgcn_global_load_lds((const void*)(base + doff[n]),
-                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, KV_POLICY);
             }
         } else {
             // the sequence's last tile: rows past the end re-read the last
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                 const char* src = base + (int)doff[n] + (row - t) * (D * 2);
                 if (sl.appended && t0 + row == sl.slot)
                     src = (v_wave ? vnew : knew) + ((int)doff[n] - t * (D * 2));
-                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(stage + j0 * 16), 16, 0, KV_POLICY);
             }
         }
     };

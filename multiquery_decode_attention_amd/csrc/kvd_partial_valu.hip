@@ -7,6 +7,9 @@
 // D/64 of the head's columns.  The split's result is stored normalised,
 // together with its base-2 log-sum-exp, for the combine pass.
 //
+// With k_new/v_new set (one decode step) the append is folded in: the new
+// token's row is read from k_new/v_new and copied to its cache slot here.
+//
 // This is the fp32-cache path (the tiny multiquery workload) and an
 // independent cross-check of the MFMA kernel in bf16; it makes no attempt
 // at bandwidth efficiency (each head re-reads its KV head's slab).
@@ -23,6 +26,17 @@ namespace {
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Element i of a 16-byte piece held as four 32-bit words.
+template <typename T>
+__device__ inline float element(const uint32_t (&w)[4], int i);
+template <>
+__device__ inline float element<float>(const uint32_t (&w)[4], int i) { return __uint_as_float(w[i]); }
+template <>
+__device__ inline float element<uint16_t>(const uint32_t (&w)[4], int i) {
+    const uint32_t x = w[i / 2];
+    return __uint_as_float(i % 2 ? (x & 0xffff0000u) : (x << 16));
+}
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -44,8 +58,9 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     const int h = bc.unit % a.Hq;
     const int b = bc.unit / a.Hq;
     const int lane = threadIdx.x;
-    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
-                                    s == 0 && h == 0 && lane == 0).len;
+    const SeqLen sl = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
+                                      s == 0 && h == 0 && lane == 0);
+    const int len = sl.len;
     const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
     if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
     const int g = h / a.M;  // query head h reads KV head floor(h / M)
@@ -59,6 +74,27 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     const T* kb = static_cast<const T*>(a.k_cache) + slab;
     const T* vb = static_cast<const T*>(a.v_cache) + slab;
 
+    // Fused append: the new token (slot sl.slot, the sequence's last) is
+    // read from k_new/v_new, and the wave of the group's first head in the
+    // split owning its tile writes it to the cache slot, which nothing else
+    // in this launch reads.
+    const T* knew = nullptr;
+    const T* vnew = nullptr;
+    const int slot = sl.appended ? sl.slot : -1;
+    if (sl.appended) {
+        const size_t nrow = ((size_t)b * a.Hkv + g) * D;
+        knew = static_cast<const T*>(a.k_new) + nrow;
+        vnew = static_cast<const T*>(a.v_new) + nrow;
+        if (h % a.M == 0 && s == (slot / VALU_TILE) % a.S) {
+            T* kw = const_cast<T*>(kb) + (size_t)slot * D;
+            T* vw = const_cast<T*>(vb) + (size_t)slot * D;
+            for (int d = lane; d < D; d += 64) {
+                kw[d] = knew[d];
+                vw[d] = vnew[d];
+            }
+        }
+    }
+
     float acc[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
@@ -69,10 +105,17 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         const int t = t0 + lane;
         float x = -INFINITY;
         if (t < len) {
-            const T* kr = kb + (size_t)t * D;
+            // the lane's key row in 16-byte pieces, all requested before use
+            const T* kr = t == slot ? knew : kb + (size_t)t * D;
+            constexpr int PIECE = 16 / sizeof(T);
             float dot = 0.f;
 #pragma unroll 8
-            for (int d = 0; d < D; ++d) dot = fmaf(qs[d], to_f32(kr[d]), dot);
+            for (int d0 = 0; d0 < D; d0 += PIECE) {
+                const uint4 kv = *reinterpret_cast<const uint4*>(kr + d0);
+                const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+                for (int i = 0; i < PIECE; ++i) dot = fmaf(qs[d0 + i], element<T>(w4, i), dot);
+            }
             x = dot * a.scale_log2e;
         }
         const float m_new = fmaxf(m_run, wave_max(x));
@@ -83,11 +126,24 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
 #pragma unroll
         for (int k = 0; k < DPL; ++k) acc[k] *= alpha;
         const int nt = min(VALU_TILE, len - t0);
-        for (int j = 0; j < nt; ++j) {
-            const float pj = __shfl(p, j);
-            const T* vr = vb + (size_t)(t0 + j) * D;
+        // Value rows in blocks of 16, all loads of a block in flight at
+        // once.  Rows past the sequence's end re-read its last row: their
+        // weights p are exactly 0 (scores of -inf).
+        for (int jb = 0; jb < nt; jb += 16) {
+            float vv[16][DPL];
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) acc[k] = fmaf(pj, to_f32(vr[lane + 64 * k]), acc[k]);
+            for (int u = 0; u < 16; ++u) {
+                const int tv = t0 + min(jb + u, nt - 1);
+                const T* vr = tv == slot ? vnew : vb + (size_t)tv * D;
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) vv[u][k] = to_f32(vr[lane + 64 * k]);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float pj = __shfl(p, jb + u);
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) acc[k] = fmaf(pj, vv[u][k], acc[k]);
+            }
         }
     }
 

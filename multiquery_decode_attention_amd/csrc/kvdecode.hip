@@ -235,7 +235,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
     const bool with_append = k_new != nullptr;
-    const bool fused = with_append && p.variant == KVD_VARIANT_LDS;
+    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA;
     if (with_append && !fused) {
         if ((rc = launch_append_timed(h, k_new, v_new, st)) != KVD_OK) return rc;
     }
@@ -273,14 +273,6 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     c.T_cap = a.T_cap;
     c.tile = p.tile;
     c.S = p.splits;
-    {
-        // split groups: up to 256 threads, no more groups than splits, whole waves
-        const int nvec = a.D / 4;
-        int G = 256 / nvec;
-        while (G > 1 && G / 2 >= p.splits && (nvec * (G / 2)) % 64 == 0) G /= 2;
-        c.groups = G;
-    }
-
     const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
@@ -383,6 +375,14 @@ int32_t kvdecode_status(kvdecode_t h, void* stream) {
     if (flag & kvd::ERRBIT_CAPACITY) return KVD_ECAPACITY;
     if (flag & kvd::ERRBIT_LENGTH) return KVD_ELENGTH;
     return KVD_OK;
+}
+
+int32_t kvdecode_reserve(kvdecode_t h) {
+    if (!is_live(h)) return KVD_EINVAL;
+    int32_t rc = ensure_device(h);
+    if (rc != KVD_OK) return rc;
+    if ((rc = ensure_workspace(h, make_plan(h).splits)) != KVD_OK) return rc;
+    return ensure_events(h);
 }
 
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {

@@ -113,6 +113,7 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_destroy(h) == kvd.KVD_EINVAL
     assert lib.kvdecode_attend(h, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
     assert lib.kvdecode_status(h, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_reserve(h) == kvd.KVD_EINVAL
     assert lib.kvdecode_destroy(None) == kvd.KVD_EINVAL
 
 

@@ -76,10 +76,10 @@ def test_split_invariance(name, B, splits):
     check_case(case, w.Hq, f"{name}/splits={splits}", splits=splits)
 
 
-VARIANTS = {"valu": kvd.KVD_VARIANT_VALU, "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}
 
 
-@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("variant", ["valu", "mfma", "lds"])
 @pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 2), ("ragged_gqa_bf16", 4),
                                     ("llama13b_mha_bf16", 1), ("longctx_mqa_bf16", 1)])
 def test_kernel_variants_bf16(name, B, variant):
@@ -128,12 +128,12 @@ def test_empty_sequences_and_poisoned_tails():
     check_case(case, Hq, "poisoned tails + append", lengths=L0)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_capacity_overflow_reported_and_harmless(fused):
+@pytest.mark.parametrize("fused,variant", [(False, "auto"), (True, "lds"), (True, "valu"), (True, "mfma")])
+def test_capacity_overflow_reported_and_harmless(fused, variant):
     B, Hq, Hkv, D, T_cap = 3, 8, 2, 128, 64
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, [64, 64, 10], "bf16", seed=9)
     L0 = torch.tensor([64, 63, 9], dtype=torch.int32)  # sequence 0 is already full
-    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L0, fused=fused)
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L0, fused=fused, variant=VARIANTS[variant])
     assert status == kvd.KVD_ECAPACITY
     assert L.cpu().tolist() == [64, 64, 10]
     ref, k2, v2, L2 = oracle_step(case, lengths=L0)
@@ -142,13 +142,21 @@ def test_capacity_overflow_reported_and_harmless(fused):
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
 
-def test_fused_step_with_out_of_range_length():
+@pytest.mark.parametrize("variant,fused", [("lds", True), ("valu", True), ("mfma", False)])
+def test_reserve_then_step(variant, fused):
+    """kvdecode_reserve before the first call changes no result."""
+    case = inputs.make_case(3, 16, 2, 128, 200, [1, 77, 199], "bf16", seed=31)
+    check_case(case, 16, f"reserve {variant}", variant=VARIANTS[variant], fused=fused, reserve=True)
+
+
+@pytest.mark.parametrize("variant", ["lds", "valu"])
+def test_fused_step_with_out_of_range_length(variant):
     """A length past capacity: no append for that sequence, attention
     clamped to capacity, KVD_ELENGTH; the other sequence steps normally."""
     B, Hq, Hkv, D, T_cap = 2, 16, 1, 128, 96
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, [96, 41], "bf16", seed=12)
     L_bad = torch.tensor([1000, 40], dtype=torch.int32)
-    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L_bad, fused=True, variant=kvd.KVD_VARIANT_LDS)
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L_bad, fused=True, variant=VARIANTS[variant])
     assert status == kvd.KVD_ELENGTH
     assert L.cpu().tolist() == [1000, 41]
     ref, k2, v2, _ = oracle_step(case, lengths=torch.tensor([96, 40], dtype=torch.int32))
