@@ -40,6 +40,7 @@ struct PartialArgs {
     int S;                  // splits per (sequence, KV head): split s owns the
                             // kernel's token tiles s, s+S, s+2S, ...
     float scale_log2e;      // scale * log2(e)
+    int lds_config;         // LDS kernel: LDS_SHORT or LDS_LONG (see below)
 };
 
 struct CombineArgs {
@@ -121,33 +122,30 @@ hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stre
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
 
-// Ring depth (32-token stages) of the LDS-staged kernel per head dim.
-#ifndef KVD_LDS_STAGES_64
-#define KVD_LDS_STAGES_64 6
-#endif
-#ifndef KVD_LDS_STAGES_128
-#define KVD_LDS_STAGES_128 3
-#endif
-#ifndef KVD_LDS_STAGES_256
-#define KVD_LDS_STAGES_256 5
-#endif
-// V tiles of the LDS-staged kernel trail its K tiles by this many of the
-// split's tiles (see kvd_partial_lds.hip), per head dim.
-#ifndef KVD_LDS_V_LAG_256
-#define KVD_LDS_V_LAG_256 1
-#endif
-#ifndef KVD_LDS_V_LAG_SMALL
-#define KVD_LDS_V_LAG_SMALL 0
-#endif
-constexpr int lds_v_lag(int D) { return D == 256 ? KVD_LDS_V_LAG_256 : KVD_LDS_V_LAG_SMALL; }
-constexpr int LDS_BYTES_PER_CU = 160 * 1024;
-constexpr int lds_stages(int D) {
-    return D == 64 ? KVD_LDS_STAGES_64 : (D == 128 ? KVD_LDS_STAGES_128 : KVD_LDS_STAGES_256);
+// Configurations of the LDS-staged kernel: ring depth (stages of K and V of
+// 32 tokens, 128*D bytes each) and how many of the split's tiles the V loads
+// trail the K loads.  LDS_SHORT is the one for d = 64 and 128 and for d = 256
+// when each split streams few tiles: one workgroup per CU at d = 256, whose
+// deeper ring keeps the per-workgroup fixed costs (pipeline fill, queries,
+// output) few.  LDS_LONG (d = 256 only) fits two workgroups per CU, which
+// hide each other's compute and barrier waits on long splits.
+enum { LDS_SHORT = 0, LDS_LONG = 1 };
+struct LdsConfig {
+    int stages, v_lag;
+};
+constexpr LdsConfig lds_config(int D, int which) {
+    return D == 64 ? LdsConfig{6, 0}
+         : D == 128 ? LdsConfig{3, 0}
+         : which == LDS_LONG ? LdsConfig{2, 1} : LdsConfig{3, 0};
 }
-// Workgroups of the LDS-staged kernel resident per CU: a stage holds K and V
-// of 32 tokens (128*D bytes); the ring must fit the CU's 160 KB of LDS.
-inline int lds_groups_per_cu(int D) {
-    const int g = LDS_BYTES_PER_CU / (lds_stages(D) * 128 * D);
+// The planner takes LDS_LONG at d = 256 when every split then holds at least
+// this many tiles of a full cache.
+constexpr int LDS_LONG_MIN_TILES = 24;
+constexpr int LDS_BYTES_PER_CU = 160 * 1024;
+// Workgroups of the LDS-staged kernel resident per CU: the ring must fit the
+// CU's 160 KB of LDS.
+inline int lds_groups_per_cu(int D, int which) {
+    const int g = LDS_BYTES_PER_CU / (lds_config(D, which).stages * 128 * D);
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);

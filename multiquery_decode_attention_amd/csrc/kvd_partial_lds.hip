@@ -393,21 +393,29 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         __builtin_nontemporal_store(m_ref + __builtin_log2f(l), a.lse_part + row0 + (size_t)c * a.S);
 }
 
-template <int D, int NS>
+template <int D, int NS, int VL>
 hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 63) / 64;
     dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
-    hipLaunchKernelGGL((partial_lds_kernel<D, NS, lds_v_lag(D)>), grid, dim3(256), 0, stream, a, groups);
+    hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL>), grid, dim3(256), 0, stream, a, groups);
     return hipGetLastError();
+}
+
+template <int D, int WHICH>
+hipError_t launch_cfg(const PartialArgs& a, hipStream_t stream) {
+    constexpr LdsConfig c = lds_config(D, WHICH);
+    return launch_d<D, c.stages, c.v_lag>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 64: return launch_d<64, lds_stages(64)>(a, stream);
-        case 128: return launch_d<128, lds_stages(128)>(a, stream);
-        case 256: return launch_d<256, lds_stages(256)>(a, stream);
+        case 64: return launch_cfg<64, LDS_SHORT>(a, stream);
+        case 128: return launch_cfg<128, LDS_SHORT>(a, stream);
+        case 256:
+            return a.lds_config == LDS_LONG ? launch_cfg<256, LDS_LONG>(a, stream)
+                                            : launch_cfg<256, LDS_SHORT>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -54,6 +54,7 @@ struct Plan {
     int tile;    // tokens per tile of the chosen partial kernel
     int splits;  // S: split s owns tiles s, s+S, ... of each sequence
     int chunk;   // most tokens any split holds for a full cache
+    int lds_config;  // kvd::LDS_SHORT or kvd::LDS_LONG (LDS kernel)
 };
 
 int resolve_variant(const kvdecode_s* h) {
@@ -70,7 +71,9 @@ int resolve_variant(const kvdecode_s* h) {
 // where rounds(S) = ceil(work units * S / resident slots): a launch whose
 // last round is partly empty wastes the rest of that round.  Among plans
 // within 2% of the cheapest, the one with most splits wins (shorter splits
-// balance ragged lengths better).
+// balance ragged lengths better).  At d = 256 the LDS kernel has a second
+// configuration with two workgroups per CU; it is planned first and taken
+// when its splits stay long (kvd::LDS_LONG_MIN_TILES tiles of a full cache).
 constexpr int CUS = 256;
 
 struct Shape {
@@ -78,12 +81,12 @@ struct Shape {
     long long slots;      // workgroups resident on the whole GPU
 };
 
-Shape shape_for(const kvdecode_s* h, int variant) {
+Shape shape_for(const kvdecode_s* h, int variant, int lds_which) {
     const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
     Shape sh;
     if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((h->M + 63) / 64);
-        sh.slots = (long long)CUS * kvd::lds_groups_per_cu(h->d.head_dim);
+        sh.slots = (long long)CUS * kvd::lds_groups_per_cu(h->d.head_dim, lds_which);
     } else if (variant == KVD_VARIANT_MFMA) {
         const int hb = kvd::mfma_head_blocks(h->M);
         const int nw = hb < 4 ? hb : 4;
@@ -97,43 +100,59 @@ Shape shape_for(const kvdecode_s* h, int variant) {
     return sh;
 }
 
-Plan make_plan(const kvdecode_s* h) {
-    Plan p;
-    p.variant = resolve_variant(h);
-    p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
-    const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
-    // tiles are dealt round-robin: a split holds at most ceil(n_tiles / S)
-    auto finish = [&](long long s) {
-        if (s < 1) s = 1;
-        if (s > n_tiles) s = n_tiles;
-        p.splits = (int)s;
-        p.chunk = (int)((n_tiles + s - 1) / s * p.tile);
-    };
-    if (h->forced_splits > 0) {
-        finish(h->forced_splits);
-        return p;
-    }
-    const Shape sh = shape_for(h, p.variant);
+// Cost-model choice of the split count for one kernel shape.
+long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles) {
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem;        // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * (h->d.head_dim + 1) * 4 * 2;
     double best = 0;
-    std::vector<std::pair<int, double>> cand;
+    std::vector<std::pair<long long, double>> cand;
     long long prev_per = -1;
     for (long long s = 1; s <= n_tiles; ++s) {
         const long long per = (n_tiles + s - 1) / s;  // tiles of the busiest split
         if (per == prev_per) continue;
         prev_per = per;
         const long long rounds = (sh.units * s + sh.slots - 1) / sh.slots;
-        const double cost = (double)rounds * (per * p.tile * tok_bytes + fill) * sh.slots +
+        const double cost = (double)rounds * (per * tile * tok_bytes + fill) * sh.slots +
                             (double)sh.units * s * part_bytes;
-        cand.emplace_back((int)s, cost);
+        cand.emplace_back(s, cost);
         if (best == 0 || cost < best) best = cost;
     }
-    int pick = 1;
+    long long pick = 1;
     for (auto& c : cand)
         if (c.second <= best * 1.02 && c.first > pick) pick = c.first;
-    finish(pick);
+    return pick;
+}
+
+Plan make_plan(const kvdecode_s* h) {
+    Plan p;
+    p.variant = resolve_variant(h);
+    p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
+    p.lds_config = kvd::LDS_SHORT;
+    const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
+    auto clamp_splits = [&](long long s) { return s < 1 ? 1 : (s > n_tiles ? n_tiles : s); };
+    // tiles are dealt round-robin: a split holds at most ceil(n_tiles / S)
+    auto finish = [&](long long s) {
+        s = clamp_splits(s);
+        p.splits = (int)s;
+        p.chunk = (int)((n_tiles + s - 1) / s * p.tile);
+    };
+    if (p.variant == KVD_VARIANT_LDS && h->d.head_dim == 256) {
+        const long long s = clamp_splits(h->forced_splits > 0
+                                             ? h->forced_splits
+                                             : plan_splits(h, shape_for(h, p.variant, kvd::LDS_LONG),
+                                                           p.tile, n_tiles));
+        if ((n_tiles + s - 1) / s >= kvd::LDS_LONG_MIN_TILES) {
+            p.lds_config = kvd::LDS_LONG;
+            finish(s);
+            return p;
+        }
+    }
+    if (h->forced_splits > 0) {
+        finish(h->forced_splits);
+        return p;
+    }
+    finish(plan_splits(h, shape_for(h, p.variant, kvd::LDS_SHORT), p.tile, n_tiles));
     return p;
 }
 
@@ -259,6 +278,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.T_cap = h->d.capacity;
     a.S = p.splits;
     a.scale_log2e = scale * kvd::LOG2E;
+    a.lds_config = p.lds_config;
 
     kvd::CombineArgs c;
     c.o_part = h->o_part;
