@@ -39,7 +39,7 @@ __device__ inline void store4(uint16_t* out, size_t i, float4 v) {
 // with A_k = sum_j 2^(L_j - m_k) O_j and Z_k = sum_j 2^(L_j - m_k) over the
 // splits j of group k.  Partials are read exactly once: non-temporal loads.
 constexpr int THREADS = 256;
-constexpr int UNROLL = 8;
+constexpr int UNROLL = 16;
 
 __device__ inline float4 load4_once(const float* p) {
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
