@@ -55,11 +55,16 @@ def kernel_source_sha(variant: str = "lds") -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, variant: str):
+def traffic_key(workload: str, page_size: int = 0) -> str:
+    """Name of a workload's traffic record (and profile summaries)."""
+    return workload + (f"_paged{page_size}" if page_size else "")
+
+
+def measured_traffic(key: str, variant: str):
     """HBM bytes per partial-pass launch from committed rocprofv3 counter
     runs, or None when absent, taken on another kernel, or taken before the
     kernel's sources last changed."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{key}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -79,6 +84,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force split count (0 = plan)")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma", "lds"])
     ap.add_argument("--cache-copies", type=int, default=0, help="0 = enough for 2 GiB")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged cache with this many tokens per page (0 = contiguous cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (counter calibration)")
@@ -123,12 +130,21 @@ def main():
     for r in range(R):
         case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
                                 seed=w.seed + 1000 * r, device=dev, k_scale=w.k_scale)
-        cache = kvd.KVCache(case.k_cache, case.v_cache, case.lengths0, w.Hq)
+        keep = {}
+        if args.page_size:
+            # the same caches laid out in shuffled pages; the page pools and
+            # block table replace the contiguous tensors on the device
+            kp, vp, bt = inputs.make_paged(case.k_cache, case.v_cache, args.page_size,
+                                           seed=w.seed + 1000 * r + 1)
+            keep = {"k_pages": kp, "v_pages": vp, "block_table": bt.to(dev)}
+            cache = kvd.KVCache(kp, vp, case.lengths0, w.Hq, block_table=keep["block_table"])
+        else:
+            cache = kvd.KVCache(case.k_cache, case.v_cache, case.lengths0, w.Hq)
         cache.set_variant(variant)
         cache.set_num_splits(args.splits)
         cache.reserve()  # device workspace allocated now, not inside the timed steps
         copies.append({"case": case, "cache": cache, "out": torch.empty_like(case.q),
-                       "len": case.lengths0.cpu().tolist()})
+                       "len": case.lengths0.cpu().tolist(), "keep": keep})
     plan = copies[0]["cache"].plan()
     log(f"plan {plan}")
     torch.cuda.synchronize()
@@ -222,11 +238,11 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "T": w.T, "cache_dtype": w.dtype, "num_splits": plan["num_splits"],
                    "split_tokens": plan["split_tokens"], "variant": plan["variant"],
-                   "cache_copies": R, "seed": w.seed},
+                   "cache_copies": R, "seed": w.seed, "page_size": args.page_size or None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, plan["variant"]),
+                     "traffic": measured_traffic(traffic_key(w.name, args.page_size), plan["variant"]),
                      "kernel": f"partial_{plan['variant']}_kernel"},
         "cpu_baseline": cpu,
     }

@@ -70,7 +70,8 @@ typedef enum {
     KVD_ECAPACITY = -4,    /* (from kvdecode_status) an append found a sequence already at capacity */
     KVD_EHIP = -5,         /* a HIP runtime call or kernel launch failed */
     KVD_ENOMEM = -6,       /* host or device allocation failed */
-    KVD_ELENGTH = -7       /* (from kvdecode_status) attend found lengths[b] outside [0, capacity] */
+    KVD_ELENGTH = -7,      /* (from kvdecode_status) attend found lengths[b] outside [0, capacity] */
+    KVD_EPAGE = -8         /* (from kvdecode_status) a block-table entry in use was outside [0, num_pages) */
 } kvd_status_t;
 
 /* Kernel variants for the partial pass (kvdecode_set_variant).
@@ -106,6 +107,54 @@ typedef struct {
  * Limits: B <= 65535, Hkv <= 65535, T_cap <= 2^24.
  */
 int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out);
+
+/*
+ * Paged KV cache: the caches of all sequences live in one pool of
+ * fixed-size pages, and a block table maps each sequence's j-th block of
+ * page_size tokens to a page of the pool, so a sequence holds only the pages
+ * it needs and a batch slot can be refilled without moving other sequences'
+ * caches.  ("All About Transformer Inference", section on tricks for
+ * generation throughput -- paged attention, the cache as pages addressed
+ * through a table -- and section "Continuous batching".)
+ *
+ * Token t of sequence b, KV head g is row
+ *     (block_table[b * max_pages + t / page_size] * Hkv + g) * page_size
+ *       + t % page_size
+ * of the pool, i.e. a page holds page_size consecutive tokens of one
+ * sequence for every KV head.  The capacity of every sequence is
+ * max_pages * page_size tokens; entries of the block table are read only for
+ * blocks holding valid tokens (and the block an append writes to), so the
+ * rest of a row may hold anything.  An entry in use outside [0, num_pages)
+ * is replaced by page 0 for memory safety and sets the sticky error
+ * KVD_EPAGE.  Pages are not reference-counted: two sequences may share a
+ * page only if neither appends into it.
+ */
+typedef struct {
+    int32_t batch;        /* B  >= 1                                              */
+    int32_t num_q_heads;  /* Hq >= 1, a multiple of num_kv_heads                   */
+    int32_t num_kv_heads; /* Hkv >= 1                                              */
+    int32_t head_dim;     /* d in {64, 128, 256}                                   */
+    int32_t page_size;    /* tokens per page: a power of two in [32, 65536]        */
+    int32_t num_pages;    /* pages in the pool, >= 1                               */
+    int32_t max_pages;    /* block-table row length (blocks per sequence), >= 1    */
+    int32_t dtype;        /* KVD_F32 or KVD_BF16                                   */
+    void* k_pages;        /* [num_pages, Hkv, page_size, d] keys   (device)        */
+    void* v_pages;        /* [num_pages, Hkv, page_size, d] values (device)        */
+    int32_t* block_table; /* [B, max_pages] page of each block (device int32)      */
+    int32_t* lengths;     /* [B] valid tokens per sequence (device int32),
+                             0 <= lengths[b] <= max_pages * page_size             */
+} kvdecode_paged_desc_t;
+
+/*
+ * Create a handle over a caller-owned paged cache.  Same validation and
+ * lazy device binding as kvdecode_create; additionally KVD_EINVAL for a
+ * page_size that is not a power of two in [32, 65536], num_pages or
+ * max_pages < 1, max_pages * page_size > 2^24, or a pool of more than 2^31
+ * rows.  Every call below works on the handle; the partial pass runs on the
+ * LDS kernel (bf16) or the VALU kernel (fp32 or bf16) -- KVD_VARIANT_MFMA is
+ * KVD_EUNSUPPORTED for a paged handle.
+ */
+int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out);
 
 /*
  * Bind the handle to the current device now and allocate everything its
@@ -157,8 +206,8 @@ int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_ne
 
 /*
  * Synchronise `stream`, then report and clear the sticky device error:
- * KVD_OK, KVD_ECAPACITY or KVD_ELENGTH (capacity is reported first when both
- * occurred).  Returns KVD_OK without a device call if the handle has never
+ * KVD_OK, KVD_ECAPACITY, KVD_ELENGTH or KVD_EPAGE (in that order of
+ * precedence when several occurred).  Returns KVD_OK without a device call if the handle has never
  * touched a device.
  */
 int32_t kvdecode_status(kvdecode_t h, void* stream);

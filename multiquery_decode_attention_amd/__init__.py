@@ -21,8 +21,8 @@ import torch
 
 __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
-    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
-    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_create",
+    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
+    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_create", "kvdecode_create_paged",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_status",
     "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
@@ -31,7 +31,7 @@ __all__ = [
 ]
 
 KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
-KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH = -4, -5, -6, -7
+KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE = -4, -5, -6, -7, -8
 KVD_F32, KVD_BF16 = 0, 1
 KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS = 0, 1, 2, 3
 
@@ -41,7 +41,7 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libkvdecode.so")
 
 EXPORTS = (
-    "kvdecode_create", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
+    "kvdecode_create", "kvdecode_create_paged", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
     "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
@@ -68,6 +68,17 @@ class kvdecode_desc_t(ctypes.Structure):
     ]
 
 
+class kvdecode_paged_desc_t(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("lengths", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -83,6 +94,7 @@ def library():
     IP = ctypes.POINTER(ctypes.c_int32)
     sig = {
         "kvdecode_create": (I, [ctypes.POINTER(kvdecode_desc_t), ctypes.POINTER(P)]),
+        "kvdecode_create_paged": (I, [ctypes.POINTER(kvdecode_paged_desc_t), ctypes.POINTER(P)]),
         "kvdecode_append": (I, [P, P, P, P]),
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
@@ -148,6 +160,33 @@ def kvdecode_create(k_cache: torch.Tensor, v_cache: torch.Tensor, lengths: torch
                            k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr())
     h = ctypes.c_void_p()
     _check(library().kvdecode_create(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create")
+    return h.value
+
+
+def kvdecode_create_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, block_table: torch.Tensor,
+                          lengths: torch.Tensor, num_q_heads: int) -> int:
+    """Handle over a caller-owned paged cache: pools [num_pages, Hkv, page_size, d],
+    block table [B, max_pages] int32 and lengths [B] int32."""
+    for t in (k_pages, v_pages):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("page pools must be contiguous [num_pages, Hkv, page_size, d] tensors")
+    if k_pages.shape != v_pages.shape or k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must match in shape and dtype")
+    if k_pages.dtype not in _DT:
+        raise ValueError(f"unsupported cache dtype {k_pages.dtype}")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor")
+    B = block_table.shape[0]
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or lengths.shape[0] != B:
+        raise ValueError("lengths must be an int32 [B] tensor")
+    if not (k_pages.is_cuda and v_pages.is_cuda and block_table.is_cuda and lengths.is_cuda):
+        raise ValueError("pools, block table and lengths must be device tensors")
+    num_pages, Hkv, page_size, D = k_pages.shape
+    desc = kvdecode_paged_desc_t(B, num_q_heads, Hkv, D, page_size, num_pages, block_table.shape[1],
+                                 _DT[k_pages.dtype], k_pages.data_ptr(), v_pages.data_ptr(),
+                                 block_table.data_ptr(), lengths.data_ptr())
+    h = ctypes.c_void_p()
+    _check(library().kvdecode_create_paged(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create_paged")
     return h.value
 
 
@@ -221,12 +260,21 @@ class KVCache:
     The tensors must outlive the object; ``close()`` frees the handle.
     """
 
-    def __init__(self, k_cache, v_cache, lengths, num_q_heads: int):
+    def __init__(self, k_cache, v_cache, lengths, num_q_heads: int, block_table=None):
+        """Contiguous caches [B, Hkv, T_cap, d], or -- with ``block_table``
+        [B, max_pages] -- page pools [num_pages, Hkv, page_size, d]."""
         self.k_cache, self.v_cache, self.lengths = k_cache, v_cache, lengths
-        self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
+        self.block_table = block_table
         self.Hq = num_q_heads
         self.dtype = k_cache.dtype
-        self.handle = kvdecode_create(k_cache, v_cache, lengths, num_q_heads)
+        if block_table is None:
+            self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
+            self.handle = kvdecode_create(k_cache, v_cache, lengths, num_q_heads)
+        else:
+            _, self.Hkv, page_size, self.D = k_cache.shape
+            self.B = block_table.shape[0]
+            self.T_cap = block_table.shape[1] * page_size
+            self.handle = kvdecode_create_paged(k_cache, v_cache, block_table, lengths, num_q_heads)
 
     def _check_token(self, t, heads, name):
         if t.shape != (self.B, heads, self.D) or t.dtype != self.dtype or not t.is_contiguous():

@@ -10,6 +10,38 @@ namespace kvd {
 // Sticky device error bits, OR-ed into the handle's flag word.
 constexpr int ERRBIT_CAPACITY = 1;  // append found lengths[b] == T_cap
 constexpr int ERRBIT_LENGTH = 2;    // a kernel saw lengths[b] outside [0, T_cap]
+constexpr int ERRBIT_PAGE = 4;      // a block-table entry in use was outside [0, num_pages)
+
+// Where the cache rows live.  Contiguous (block_table == nullptr): token t of
+// (sequence b, KV head g) is row (b * Hkv + g) * T_cap + t of k_cache/v_cache.
+// Paged: the caches are a pool of pages [num_pages, Hkv, page, d] and token t
+// is row (block_table[b * max_pages + t / page] * Hkv + g) * page + t % page,
+// page = 2^page_shift >= 32 tokens, so a 32-token tile never straddles pages.
+struct KvLayout {
+    const int32_t* block_table;
+    int page_shift;
+    int max_pages;
+    int num_pages;
+};
+
+// Page of block j of sequence b; an entry outside the pool is replaced by
+// page 0 (a valid address) and flagged.
+__device__ __forceinline__ int kv_page(const KvLayout& L, int b, int j, int* err) {
+    int p = L.block_table[(size_t)b * L.max_pages + j];
+    if ((unsigned)p >= (unsigned)L.num_pages) {
+        atomicOr(err, ERRBIT_PAGE);
+        p = 0;
+    }
+    return p;
+}
+
+// Row of token t of (b, g): contiguous, or paged given the token's page.
+__device__ __forceinline__ size_t kv_row_contiguous(int b, int g, int Hkv, int T_cap, int t) {
+    return ((size_t)b * Hkv + g) * (size_t)T_cap + t;
+}
+__device__ __forceinline__ size_t kv_row_paged(const KvLayout& L, int page, int g, int Hkv, int t) {
+    return (((size_t)page * Hkv + g) << L.page_shift) + (t & ((1 << L.page_shift) - 1));
+}
 
 // Tokens per inner iteration of each partial-pass kernel.
 constexpr int MFMA_TILE = 32;
@@ -36,6 +68,7 @@ struct PartialArgs {
     // attends lengths[b] + 1 tokens; lengths itself is advanced by the combine.
     const void* k_new;
     const void* v_new;
+    KvLayout kv;            // contiguous or paged cache rows
     int B, Hq, Hkv, M, D, T_cap;
     int S;                  // splits per (sequence, KV head): split s owns the
                             // kernel's token tiles s, s+S, s+2S, ...
@@ -116,8 +149,8 @@ __device__ __forceinline__ BlockCoord block_coord(int units) {
 
 // Each launcher returns the hipError_t of its launch.
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                         int32_t* lengths, int* err, int B, int Hkv, int D, int T_cap,
-                         int elem_bytes, hipStream_t stream);
+                         const KvLayout& kv, int32_t* lengths, int* err, int B, int Hkv, int D,
+                         int T_cap, int elem_bytes, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);

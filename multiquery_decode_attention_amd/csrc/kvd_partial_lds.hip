@@ -25,6 +25,10 @@
 // the split's end are loaded as copies of its last valid row and masked out
 // of the softmax.
 //
+// A paged cache (pages of >= 32 tokens, so a tile never straddles two) is
+// read through its block table: one page lookup per tile, from block-table
+// entries each wave holds in a register.
+//
 // Softmax bookkeeping per head keeps a reference maximum m and the sum l of
 // 2^(x - m).  A tile whose scores stay below m + 8 (base 2) leaves m alone:
 // its weights are at most 2^8, far inside fp32 and bf16 range, and since the
@@ -80,7 +84,7 @@ __device__ __forceinline__ void wait_stage(int stages_after) {
     }
 }
 
-template <int D, int NS, int VL>
+template <int D, int NS, int VL, bool PAGED>
 __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int head_groups) {
     constexpr int CH = D / 8;                        // 16-byte chunks per row
     constexpr int SWZ = (CH < 16 ? CH : 16) - 1;     // K chunk swizzle mask
@@ -121,9 +125,30 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;
 
-    const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.T_cap * D;
+    // Rows below are counted from kb/vb: the (b, g) slab of a contiguous
+    // cache, or the start of the page pool.
+    const size_t slab = PAGED ? 0 : kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0) * D;
     const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.k_cache) + slab);
     const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + slab);
+
+    // Row of the first token t0 of the split's tile `tile`.  Paged: each
+    // wave keeps the pages of 64 consecutive tiles of its split in one
+    // register (lane i: tile 64c + i) and reads them with readlane; a wave
+    // reloads it when its tiles cross into the next 64.
+    int pg_chunk = -1, pg_lane = 0;
+    auto tile_row = [&](int tile, int t0) -> size_t {
+        if constexpr (!PAGED) {
+            return (size_t)t0;
+        } else {
+            if ((tile >> 6) != pg_chunk) {
+                pg_chunk = tile >> 6;
+                const int k = min((pg_chunk << 6) + lane, n_tiles - 1);
+                pg_lane = kv_page(a.kv, b, (t_first + k * tstride) >> a.kv.page_shift, a.err);
+            }
+            const int page = __builtin_amdgcn_readlane(pg_lane, tile & 63);
+            return kv_row_paged(a.kv, page, g, a.Hkv, t0);
+        }
+    };
 
     // Fused append.  The new token is the sequence's last, so only the split
     // owning its tile reads that slot in this launch, and it takes the row
@@ -139,7 +164,10 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
             const bool v_half = threadIdx.x >= CH;
             const int ch = v_half ? threadIdx.x - CH : threadIdx.x;
             const u32x4_t x = *reinterpret_cast<const u32x4_t*>((v_half ? vnew : knew) + ch * 16);
-            char* dst = const_cast<char*>(v_half ? vb : kb) + (size_t)sl.slot * D * 2 + ch * 16;
+            size_t row = (size_t)sl.slot;
+            if constexpr (PAGED)
+                row = kv_row_paged(a.kv, kv_page(a.kv, b, sl.slot >> a.kv.page_shift, a.err), g, a.Hkv, sl.slot);
+            char* dst = const_cast<char*>(v_half ? vb : kb) + row * D * 2 + ch * 16;
             *reinterpret_cast<u32x4_t*>(dst) = x;
         }
     }
@@ -198,7 +226,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
             return;
         }
         const int t0 = t_first + tile * tstride;
-        const char* base = tbase + (size_t)t0 * (D * 2);
+        const char* base = tbase + tile_row(tile, t0) * (D * 2);
         if (t0 + MFMA_TILE <= t_fast_end) {
 #pragma unroll
             for (int n = 0; n < PERW; ++n) {
@@ -397,7 +425,10 @@ template <int D, int NS, int VL>
 hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 63) / 64;
     dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
-    hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL>), grid, dim3(256), 0, stream, a, groups);
+    if (a.kv.block_table)
+        hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, true>), grid, dim3(256), 0, stream, a, groups);
+    else
+        hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, false>), grid, dim3(256), 0, stream, a, groups);
     return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 //
 // With k_new/v_new set (one decode step) the append is folded in: the new
 // token's row is read from k_new/v_new and copied to its cache slot here.
+// A paged cache is read through its block table, one page lookup per token.
 //
 // This is the fp32-cache path (the tiny multiquery workload) and an
 // independent cross-check of the MFMA kernel in bf16; it makes no attempt
@@ -49,7 +50,7 @@ __device__ inline float wave_sum(float v) {
     return v;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     constexpr int DPL = D / 64;  // value columns per lane
     // unit = (sequence b, query head h), head fastest
@@ -70,9 +71,17 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     for (int d = lane; d < D; d += 64) qs[d] = to_f32(qrow[d]);
     __syncthreads();
 
-    const size_t slab = ((size_t)b * a.Hkv + g) * (size_t)a.T_cap * D;
+    // Rows are counted from kb/vb: the (b, g) slab of a contiguous cache, or
+    // the start of the page pool (rows < 2^31, checked at creation).
+    const size_t slab = PAGED ? 0 : kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0) * D;
     const T* kb = static_cast<const T*>(a.k_cache) + slab;
     const T* vb = static_cast<const T*>(a.v_cache) + slab;
+    auto row_of = [&](int t) -> int {
+        if constexpr (PAGED)
+            return (int)kv_row_paged(a.kv, kv_page(a.kv, b, t >> a.kv.page_shift, a.err), g, a.Hkv, t);
+        else
+            return t;
+    };
 
     // Fused append: the new token (slot sl.slot, the sequence's last) is
     // read from k_new/v_new, and the wave of the group's first head in the
@@ -86,8 +95,9 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         knew = static_cast<const T*>(a.k_new) + nrow;
         vnew = static_cast<const T*>(a.v_new) + nrow;
         if (h % a.M == 0 && s == (slot / VALU_TILE) % a.S) {
-            T* kw = const_cast<T*>(kb) + (size_t)slot * D;
-            T* vw = const_cast<T*>(vb) + (size_t)slot * D;
+            const size_t row = (size_t)row_of(slot);
+            T* kw = const_cast<T*>(kb) + row * D;
+            T* vw = const_cast<T*>(vb) + row * D;
             for (int d = lane; d < D; d += 64) {
                 kw[d] = knew[d];
                 vw[d] = vnew[d];
@@ -103,10 +113,13 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     for (int tile = s; tile < n_seq_tiles; tile += a.S) {
         const int t0 = tile * VALU_TILE;
         const int t = t0 + lane;
+        // the row of this lane's token (of the sequence's last token past
+        // the end); the value loop reads other lanes' rows by shuffle
+        const int row = row_of(min(t, len - 1));
         float x = -INFINITY;
         if (t < len) {
             // the lane's key row in 16-byte pieces, all requested before use
-            const T* kr = t == slot ? knew : kb + (size_t)t * D;
+            const T* kr = t == slot ? knew : kb + (size_t)row * D;
             constexpr int PIECE = 16 / sizeof(T);
             float dot = 0.f;
 #pragma unroll 8
@@ -133,8 +146,10 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
             float vv[16][DPL];
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
-                const int tv = t0 + min(jb + u, nt - 1);
-                const T* vr = tv == slot ? vnew : vb + (size_t)tv * D;
+                const int j = min(jb + u, nt - 1);
+                const int tv = t0 + j;
+                const int rv = PAGED ? __shfl(row, j) : tv;
+                const T* vr = tv == slot ? vnew : vb + (size_t)rv * D;
 #pragma unroll
                 for (int k = 0; k < DPL; ++k) vv[u][k] = to_f32(vr[lane + 64 * k]);
             }
@@ -154,13 +169,13 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     if (lane == 0) a.lse_part[row] = m_run + log2f(l_run);
 }
 
-template <typename T>
+template <typename T, bool PAGED>
 hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
     dim3 grid((unsigned)a.S * a.B * a.Hq), block(64);
     switch (a.D) {
-        case 64: hipLaunchKernelGGL((partial_valu_kernel<T, 64>), grid, block, 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((partial_valu_kernel<T, 128>), grid, block, 0, stream, a); break;
-        case 256: hipLaunchKernelGGL((partial_valu_kernel<T, 256>), grid, block, 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((partial_valu_kernel<T, 64, PAGED>), grid, block, 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((partial_valu_kernel<T, 128, PAGED>), grid, block, 0, stream, a); break;
+        case 256: hipLaunchKernelGGL((partial_valu_kernel<T, 256, PAGED>), grid, block, 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -169,7 +184,9 @@ hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream) {
-    return bf16 ? launch_typed<uint16_t>(a, stream) : launch_typed<float>(a, stream);
+    if (a.kv.block_table)
+        return bf16 ? launch_typed<uint16_t, true>(a, stream) : launch_typed<float, true>(a, stream);
+    return bf16 ? launch_typed<uint16_t, false>(a, stream) : launch_typed<float, false>(a, stream);
 }
 
 }  // namespace kvd

@@ -14,7 +14,8 @@
 #include "kvd_internal.h"
 
 struct kvdecode_s {
-    kvdecode_desc_t d;
+    kvdecode_desc_t d;          // for a paged cache: the pools, and capacity = max_pages * page_size
+    kvd::KvLayout kv{nullptr, 0, 0, 0};
     int M = 1;
     int elem = 4;
     int variant_req = KVD_VARIANT_AUTO;
@@ -227,7 +228,7 @@ int32_t ensure_events(kvdecode_s* h) {
 int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st) {
     const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->d.lengths, h->err,
+    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths, h->err,
                                       h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
                                       h->elem, st);
     if (e != hipSuccess) return KVD_EHIP;
@@ -279,6 +280,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.S = p.splits;
     a.scale_log2e = scale * kvd::LOG2E;
     a.lds_config = p.lds_config;
+    a.kv = h->kv;
 
     kvd::CombineArgs c;
     c.o_part = h->o_part;
@@ -324,14 +326,16 @@ const char* kvdecode_strerror(int32_t code) {
         case KVD_EHIP: return "HIP runtime error";
         case KVD_ENOMEM: return "out of memory";
         case KVD_ELENGTH: return "sequence length outside [0, capacity]";
+        case KVD_EPAGE: return "block-table entry outside the page pool";
         default: return "unknown status code";
     }
 }
 
-int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
-    if (!desc || !out) return KVD_EINVAL;
+namespace {
+
+// Validation shared by both create calls; `h` is filled on success.
+int32_t make_handle(const kvdecode_desc_t& d, const kvd::KvLayout& kv, kvdecode_t* out) {
     *out = nullptr;
-    const kvdecode_desc_t& d = *desc;
     if (d.batch < 1 || d.num_q_heads < 1 || d.num_kv_heads < 1 || d.capacity < 1) return KVD_EINVAL;
     if (d.batch > 65535 || d.num_kv_heads > 65535 || d.num_q_heads > 65535) return KVD_EINVAL;
     if (d.capacity > (1 << 24)) return KVD_EINVAL;
@@ -345,6 +349,7 @@ int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
     kvdecode_s* h = new (std::nothrow) kvdecode_s();
     if (!h) return KVD_ENOMEM;
     h->d = d;
+    h->kv = kv;
     h->M = d.num_q_heads / d.num_kv_heads;
     h->elem = d.dtype == KVD_F32 ? 4 : 2;
     {
@@ -353,6 +358,39 @@ int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
     }
     *out = h;
     return KVD_OK;
+}
+
+}  // namespace
+
+int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    return make_handle(*desc, kvd::KvLayout{nullptr, 0, 0, 0}, out);
+}
+
+int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    *out = nullptr;
+    const kvdecode_paged_desc_t& p = *desc;
+    if (p.page_size < 32 || p.page_size > 65536 || (p.page_size & (p.page_size - 1))) return KVD_EINVAL;
+    if (p.num_pages < 1 || p.max_pages < 1 || p.num_kv_heads < 1) return KVD_EINVAL;
+    if ((long long)p.max_pages * p.page_size > (1 << 24)) return KVD_EINVAL;
+    // every row index of the pool fits the kernels' 32-bit row arithmetic
+    if ((long long)p.num_pages * p.num_kv_heads * p.page_size > (1LL << 31)) return KVD_EINVAL;
+    if (!p.block_table) return KVD_EINVAL;
+    if (reinterpret_cast<uintptr_t>(p.block_table) & 3u) return KVD_EALIGN;
+    kvdecode_desc_t d;
+    d.batch = p.batch;
+    d.num_q_heads = p.num_q_heads;
+    d.num_kv_heads = p.num_kv_heads;
+    d.head_dim = p.head_dim;
+    d.capacity = p.max_pages * p.page_size;
+    d.dtype = p.dtype;
+    d.k_cache = p.k_pages;
+    d.v_cache = p.v_pages;
+    d.lengths = p.lengths;
+    int shift = 0;
+    while ((1 << shift) < p.page_size) ++shift;
+    return make_handle(d, kvd::KvLayout{p.block_table, shift, p.max_pages, p.num_pages}, out);
 }
 
 int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void* stream) {
@@ -394,6 +432,7 @@ int32_t kvdecode_status(kvdecode_t h, void* stream) {
     }
     if (flag & kvd::ERRBIT_CAPACITY) return KVD_ECAPACITY;
     if (flag & kvd::ERRBIT_LENGTH) return KVD_ELENGTH;
+    if (flag & kvd::ERRBIT_PAGE) return KVD_EPAGE;
     return KVD_OK;
 }
 
@@ -416,6 +455,7 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
     if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_LDS) return KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;
     h->variant_req = variant;
     return KVD_OK;
 }

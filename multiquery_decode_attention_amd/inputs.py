@@ -145,6 +145,33 @@ def make_workload_case(w: Workload, device="cpu", seed: Optional[int] = None,
                      w.seed if seed is None else seed, device, k_scale=w.k_scale)
 
 
+def make_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, seed: int,
+               spare_pages: Optional[int] = None):
+    """Lay contiguous caches [B, Hkv, T_cap, D] out as a page pool.
+
+    Block j (tokens j*P .. j*P+P-1) of sequence b goes to a distinct page
+    drawn by a seeded permutation; ``spare_pages`` more pages (default: one
+    sequence's worth) are filled with NaN and never listed.  Returns
+    (k_pages, v_pages, block_table) with pools [num_pages, Hkv, P, D] on the
+    caches' device and block_table [B, T_cap / P] int32 on the CPU.
+    """
+    B, Hkv, T_cap, D = k_cache.shape
+    P = int(page_size)
+    assert T_cap % P == 0, "capacity must be a whole number of pages"
+    nb = T_cap // P
+    spare = nb if spare_pages is None else int(spare_pages)
+    num_pages = B * nb + spare
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    table = torch.randperm(num_pages, generator=gen)[:B * nb].view(B, nb).to(torch.int32)
+    pools = []
+    for c in (k_cache, v_cache):
+        pool = torch.full((num_pages, Hkv, P, D), float("nan"), dtype=c.dtype, device=c.device)
+        blocks = c.view(B, Hkv, nb, P, D).permute(0, 2, 1, 3, 4)  # [B, nb, Hkv, P, D]
+        pool[table.view(-1).long().to(c.device)] = blocks.reshape(B * nb, Hkv, P, D)
+        pools.append(pool)
+    return pools[0], pools[1], table
+
+
 def bf16_bits(t: torch.Tensor):
     """Raw bf16 bit patterns of a tensor as a numpy uint16 array (host)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")

@@ -16,7 +16,17 @@ input generators, which hold none of the method's arithmetic.
   key/value projections to the cache) and section "Implementation: JetStream"
   (generate appends the single-token KV cache to the decode state).
 
-Parity status: both functions are pinned by ``tests/test_oracle_pins.py``
+* ``gather_pages`` turns a paged cache back into the contiguous one it
+  stands for: block j of sequence b (tokens j*P .. j*P+P-1) is page
+  ``block_table[b, j]`` of the pool, token by token.  ``append_paged`` is the
+  append on such a cache (the slot's page found the same way), and
+  ``decode_attention_paged`` attends over the gathered cache.  Source: "All
+  About Transformer Inference", section on tricks for generation
+  throughput (paged attention: the KV cache kept in pages addressed through
+  a table, so a batch holds only the memory it needs).
+
+Parity status: every function is pinned by ``tests/test_oracle_pins.py``
+and ``tests/test_oracle_paged.py``
 (closed forms, exact hand-worked fixture, high-precision brute force,
 invariants, naive full-prefix recomputation) and by
 ``tests/test_oracle_mutants.py`` (planted mistakes must fail a pin).
@@ -132,3 +142,56 @@ def append(k_cache, v_cache, lengths, k_new, v_new):
         v2[b, :, n[b], :] = v_new[b]
         n[b] += 1
     return k2, v2, n.astype(np.int32), overflow
+
+
+def gather_pages(pages, block_table):
+    """Contiguous cache [B, Hkv, max_pages * P, D] of a paged pool
+    [num_pages, Hkv, P, D] under ``block_table`` [B, max_pages]: token t of
+    sequence b is ``pages[block_table[b, t // P], :, t % P, :]``.  A block
+    whose entry is not a page of the pool is filled with NaN (such blocks
+    must lie past the sequence's length, where nothing is read)."""
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table)
+    num_pages, Hkv, P, D = pages.shape
+    B, max_pages = bt.shape
+    if pages.dtype.kind == "f":
+        nan = np.full((Hkv, P, D), np.nan, dtype=pages.dtype)
+    elif pages.dtype == np.uint16:  # bf16 bit patterns: quiet NaN
+        nan = np.full((Hkv, P, D), 0x7FC0, dtype=np.uint16)
+    else:
+        nan = np.zeros((Hkv, P, D), dtype=pages.dtype)
+    out = np.empty((B, Hkv, max_pages * P, D), dtype=pages.dtype)
+    for b in range(B):
+        for j in range(max_pages):
+            page = int(bt[b, j])
+            out[b, :, j * P:(j + 1) * P, :] = pages[page] if 0 <= page < num_pages else nan
+    return out
+
+
+def append_paged(k_pages, v_pages, block_table, lengths, k_new, v_new):
+    """The append on a paged cache, bit for bit: slot n = lengths[b] of
+    sequence b is offset n % P of page block_table[b, n // P].  Returns
+    (k_pages', v_pages', lengths', overflow) like ``append``; the capacity
+    is max_pages * P."""
+    k2 = np.array(k_pages, copy=True)
+    v2 = np.array(v_pages, copy=True)
+    bt = np.asarray(block_table)
+    n = np.array(lengths, dtype=np.int64, copy=True)
+    P = k2.shape[2]
+    cap = bt.shape[1] * P
+    overflow = np.zeros(n.shape, dtype=bool)
+    for b in range(bt.shape[0]):
+        if n[b] >= cap:
+            overflow[b] = True
+            continue
+        page = int(bt[b, n[b] // P])
+        k2[page, :, n[b] % P, :] = k_new[b]
+        v2[page, :, n[b] % P, :] = v_new[b]
+        n[b] += 1
+    return k2, v2, n.astype(np.int32), overflow
+
+
+def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, scale, dtype, **kw):
+    """``decode_attention`` over the contiguous caches a paged pool stands for."""
+    return decode_attention(q, gather_pages(k_pages, block_table), gather_pages(v_pages, block_table),
+                            lengths, scale, dtype, **kw)

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         assert kvd.kvdecode_strerror(code) != "unknown status code"
     assert kvd.kvdecode_strerror(-99) == "unknown status code"
 
@@ -153,6 +153,51 @@ def test_plans_cover_the_cache(lib, name):
         if forced:
             assert S <= forced or S == 1
         lib.kvdecode_destroy(h)
+
+
+def make_paged_desc(**kw):
+    d = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=64, num_pages=10,
+             max_pages=4, dtype=kvd.KVD_BF16, k_pages=FAKE, v_pages=FAKE * 2, block_table=FAKE * 3,
+             lengths=FAKE * 4)
+    d.update(kw)
+    return kvd.kvdecode_paged_desc_t(**d)
+
+
+def create_paged(lib, desc):
+    h = ctypes.c_void_p()
+    rc = lib.kvdecode_create_paged(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h.value
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("page_size", 16, kvd.KVD_EINVAL), ("page_size", 48, kvd.KVD_EINVAL),
+    ("page_size", 1 << 17, kvd.KVD_EINVAL), ("page_size", 0, kvd.KVD_EINVAL),
+    ("num_pages", 0, kvd.KVD_EINVAL), ("max_pages", 0, kvd.KVD_EINVAL),
+    ("max_pages", (1 << 18) + 1, kvd.KVD_EINVAL),       # capacity past 2^24
+    ("num_pages", (1 << 24) + 1, kvd.KVD_EINVAL),       # pool rows past 2^31
+    ("block_table", 0, kvd.KVD_EINVAL), ("block_table", FAKE + 2, kvd.KVD_EALIGN),
+    ("k_pages", 0, kvd.KVD_EINVAL), ("v_pages", FAKE + 8, kvd.KVD_EALIGN),
+    ("head_dim", 96, kvd.KVD_EUNSUPPORTED), ("num_q_heads", 9, kvd.KVD_EINVAL),
+])
+def test_create_paged_rejects(lib, field, value, code):
+    rc, h = create_paged(lib, make_paged_desc(**{field: value}))
+    assert rc == code and not h
+
+
+def test_paged_handle(lib):
+    rc, h = create_paged(lib, make_paged_desc())
+    assert rc == kvd.KVD_OK and h
+    # capacity is max_pages * page_size; the register-direct MFMA kernel has no paged mode
+    assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_MFMA) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_VALU) == kvd.KVD_OK
+    p = kvd.kvdecode_get_plan(h)
+    assert p["variant"] == "valu" and p["num_splits"] * p["split_tokens"] >= 4 * 64
+    assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_AUTO) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h)["variant"] == "lds"
+    assert lib.kvdecode_attend(h, FAKE + 4, FAKE, 1.0, None) == kvd.KVD_EALIGN
+    assert lib.kvdecode_status(h, None) == kvd.KVD_OK
+    assert lib.kvdecode_destroy(h) == kvd.KVD_OK
+    assert lib.kvdecode_create_paged(None, ctypes.byref(ctypes.c_void_p())) == kvd.KVD_EINVAL
 
 
 def test_binding_fails_loudly_without_library(tmp_path):
