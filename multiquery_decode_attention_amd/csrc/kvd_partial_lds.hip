@@ -132,20 +132,27 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.v_cache) + slab);
 
     // Row of the first token t0 of the split's tile `tile`.  Paged: each
-    // wave keeps the pages of 64 consecutive tiles of its split in one
-    // register (lane i: tile 64c + i) and reads them with readlane; a wave
-    // reloads it when its tiles cross into the next 64.
-    int pg_chunk = -1, pg_lane = 0;
+    // wave visits its tiles in order (tile, tile + 1, ...), so the page of
+    // its next tile is fetched while the current one is issued.  The block
+    // table is read through the constant address space: the kernel never
+    // writes it, and a wave-uniform address then becomes a scalar load,
+    // whose completion the compiler tracks apart from the K/V loads in
+    // flight (a vector load here made it wait for all of them).
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr bt_row = PAGED ? (const_i32_ptr)(a.kv.block_table + (size_t)b * a.kv.max_pages) : nullptr;
+    auto table_entry = [&](int tile) { return bt_row[(t_first + tile * tstride) >> a.kv.page_shift]; };
+    int next_entry = 0;  // raw entry of the wave's next tile, checked when used
+    if constexpr (PAGED) next_entry = table_entry(0);
     auto tile_row = [&](int tile, int t0) -> size_t {
         if constexpr (!PAGED) {
             return (size_t)t0;
         } else {
-            if ((tile >> 6) != pg_chunk) {
-                pg_chunk = tile >> 6;
-                const int k = min((pg_chunk << 6) + lane, n_tiles - 1);
-                pg_lane = kv_page(a.kv, b, (t_first + k * tstride) >> a.kv.page_shift, a.err);
+            int page = next_entry;
+            if (tile + 1 < n_tiles) next_entry = table_entry(tile + 1);
+            if ((unsigned)page >= (unsigned)a.kv.num_pages) {
+                if (threadIdx.x % 64 == 0) atomicOr(a.err, ERRBIT_PAGE);
+                page = 0;
             }
-            const int page = __builtin_amdgcn_readlane(pg_lane, tile & 63);
             return kv_row_paged(a.kv, page, g, a.Hkv, t0);
         }
     };
