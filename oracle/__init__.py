@@ -25,8 +25,23 @@ input generators, which hold none of the method's arithmetic.
   throughput (paged attention: the KV cache kept in pages addressed through
   a table, so a batch holds only the memory it needs).
 
-Parity status: every function is pinned by ``tests/test_oracle_pins.py``
-and ``tests/test_oracle_paged.py``
+* The fp8 cache: K and V stored as OCP FP8 E4M3 codes (1 sign, 4 exponent
+  bits with bias 7, 3 mantissa bits; largest finite 448, codes 0x7F/0xFF are
+  NaN, no infinities) with one power-of-two scale 2^e per (sequence, KV
+  head, token).  ``e4m3_value`` decodes a code from that definition;
+  ``quantize_rows`` picks, for each row, the smallest e with
+  max|x| / 2^e <= 448 and rounds x / 2^e to the nearest code (ties to the
+  even code); ``dequantize`` is code value * 2^e; ``append_fp8`` quantizes
+  the new token into its slot; ``decode_attention_fp8`` attends over the
+  dequantized cache.  Source: "All About Transformer Inference", section on
+  tricks for generation throughput (quantizing the KV cache to int8, int4
+  or fp8 saves memory bandwidth); "Efficiently Scaling Transformer
+  Inference", section 3.6 (quantized storage, bf16 arithmetic for the
+  products).  The pages fix no scale format: per-token power-of-two scales
+  are this library's choice.
+
+Parity status: every function is pinned by ``tests/test_oracle_pins.py``,
+``tests/test_oracle_paged.py`` and ``tests/test_oracle_fp8.py``
 (closed forms, exact hand-worked fixture, high-precision brute force,
 invariants, naive full-prefix recomputation) and by
 ``tests/test_oracle_mutants.py`` (planted mistakes must fail a pin).
@@ -195,3 +210,110 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, scale, dty
     """``decode_attention`` over the contiguous caches a paged pool stands for."""
     return decode_attention(q, gather_pages(k_pages, block_table), gather_pages(v_pages, block_table),
                             lengths, scale, dtype, **kw)
+
+
+# --- fp8 (OCP E4M3) cache ----------------------------------------------------
+
+E4M3_MAX = 448.0
+E4M3_EXP_MIN = -127  # range of the stored power-of-two exponents (int8)
+E4M3_EXP_MAX = 127
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code: (-1)^s * 2^(E-7) * (1 + M/8) for
+    E >= 1, (-1)^s * 2^-6 * M/8 for E = 0; E = 15 with M = 7 is NaN."""
+    s = -1.0 if code & 0x80 else 1.0
+    E = (code >> 3) & 0xF
+    M = code & 0x7
+    if E == 0xF and M == 0x7:
+        return float("nan")
+    if E == 0:
+        return s * (M / 8.0) * 2.0 ** -6
+    return s * (1.0 + M / 8.0) * 2.0 ** (E - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+# finite non-negative codes in increasing order of value (0x00 .. 0x7E)
+_POS_CODES = np.arange(0x7F, dtype=np.int64)
+_POS_VALUES = E4M3_TABLE[:0x7F]
+
+
+def _round_to_e4m3(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code of each |y| <= 448 (ties to the code with an even
+    mantissa), sign taken from y's sign bit (so -0.0 -> 0x80)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    assert np.all(a <= E4M3_MAX), "value outside the E4M3 range"
+    # index of the first representable value >= a
+    hi = np.searchsorted(_POS_VALUES, a, side="left")
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _POS_VALUES[hi] - a
+    d_lo = a - _POS_VALUES[lo]
+    pick = np.where(d_lo < d_hi, lo, hi)
+    tie = (d_lo == d_hi) & (lo != hi)
+    pick = np.where(tie, np.where(_POS_CODES[lo] % 2 == 0, lo, hi), pick)
+    code = _POS_CODES[pick]
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rows(x):
+    """Quantize each row (last axis) of x to (codes uint8, exponent int8).
+
+    e is the smallest integer with max|x| <= 448 * 2^e, clamped to
+    [-127, 127] (0 for an all-zero row); codes are x / 2^e rounded to
+    E4M3.  x must be finite.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=-1)
+    assert np.all(np.isfinite(amax)), "non-finite value to quantize"
+    e = np.zeros(amax.shape, dtype=np.int64)
+    nz = amax > 0
+    # smallest e with amax <= 448 * 2^e, from amax = f * 2^k, f in [0.5, 1)
+    f, k = np.frexp(amax[nz])
+    m, kk = 2.0 * f, k - 1                 # amax = m * 2^kk, m in [1, 2)
+    e[nz] = kk - 8 + (m > 1.75)
+    e = np.clip(e, E4M3_EXP_MIN, E4M3_EXP_MAX)
+    y = x / np.exp2(e.astype(np.float64))[..., None]
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)  # only reached when e was clamped
+    return _round_to_e4m3(y), e.astype(np.int8)
+
+
+def dequantize(codes, exps):
+    """codes [..., D] uint8 and exps [...] int8 -> float64 values."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.int64)] * np.exp2(np.asarray(exps, dtype=np.float64))[..., None]
+
+
+def append_fp8(k_codes, k_exps, v_codes, v_exps, lengths, k_new, v_new):
+    """The append on an fp8 cache: the new token's K and V rows (any float
+    array [B, Hkv, D]) are quantized per (sequence, KV head) into slot
+    lengths[b].  Returns (k_codes', k_exps', v_codes', v_exps', lengths',
+    overflow)."""
+    kc, ke = np.array(k_codes, copy=True), np.array(k_exps, copy=True)
+    vc, ve = np.array(v_codes, copy=True), np.array(v_exps, copy=True)
+    n = np.array(lengths, dtype=np.int64, copy=True)
+    T_cap = kc.shape[2]
+    qk, ek = quantize_rows(k_new)
+    qv, ev = quantize_rows(v_new)
+    overflow = np.zeros(n.shape, dtype=bool)
+    for b in range(kc.shape[0]):
+        if n[b] >= T_cap:
+            overflow[b] = True
+            continue
+        kc[b, :, n[b], :], ke[b, :, n[b]] = qk[b], ek[b]
+        vc[b, :, n[b], :], ve[b, :, n[b]] = qv[b], ev[b]
+        n[b] += 1
+    return kc, ke, vc, ve, n.astype(np.int32), overflow
+
+
+def decode_attention_fp8(q, k_codes, k_exps, v_codes, v_exps, lengths, scale, **kw):
+    """Decode attention over the dequantized fp8 cache.  q is a float32
+    array (a bf16 query widened exactly); the dequantized values are exact
+    in float32 for the exponent range the tests use."""
+    k = dequantize(k_codes, k_exps)
+    v = dequantize(v_codes, v_exps)
+    L = np.asarray(lengths)
+    # slots past the lengths are never read; keep their values finite here
+    k32, v32 = k.astype(np.float32), v.astype(np.float32)
+    assert np.array_equal(k32.astype(np.float64)[np.isfinite(k)], k[np.isfinite(k)])
+    return decode_attention(np.asarray(q, dtype=np.float32), k32, v32, L, scale, F32, **kw)
