@@ -40,7 +40,8 @@ def log(*a):
 
 # Sources that define each partial-pass kernel (the roofline kernel).
 KERNEL_SOURCES = {
-    "lds": ["kvd_partial_lds.hip", "kvd_mfma_common.h", "kvd_internal.h"],
+    "lds": ["kvd_partial_lds.hip", "kvd_lds_common.h", "kvd_mfma_common.h", "kvd_internal.h"],
+    "lds_fp8": ["kvd_partial_lds_fp8.hip", "kvd_lds_common.h", "kvd_mfma_common.h", "kvd_internal.h"],
     "mfma": ["kvd_partial_mfma.hip", "kvd_mfma_common.h", "kvd_internal.h"],
     "valu": ["kvd_partial_valu.hip", "kvd_internal.h"],
 }
@@ -55,9 +56,9 @@ def kernel_source_sha(variant: str = "lds") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload: str, page_size: int = 0) -> str:
+def traffic_key(workload: str, page_size: int = 0, kv_dtype: str = "") -> str:
     """Name of a workload's traffic record (and profile summaries)."""
-    return workload + (f"_paged{page_size}" if page_size else "")
+    return workload + (f"_paged{page_size}" if page_size else "") + (f"_{kv_dtype}" if kv_dtype else "")
 
 
 def measured_traffic(key: str, variant: str):
@@ -86,6 +87,9 @@ def main():
     ap.add_argument("--cache-copies", type=int, default=0, help="0 = enough for 2 GiB")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged cache with this many tokens per page (0 = contiguous cache)")
+    ap.add_argument("--kv-dtype", default="", choices=["", "fp8"],
+                    help="fp8: the cache as E4M3 codes with per-row power-of-two scales "
+                         "(bf16 queries and outputs); default: the workload's own dtype")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (counter calibration)")
@@ -111,7 +115,12 @@ def main():
     K, W = args.steps, args.warmup
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    kv_bytes_one = traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, [w.T_cap] * w.B)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and (args.page_size or w.dtype != "bf16"):
+        print("--kv-dtype fp8 takes a bf16 workload and a contiguous cache", file=sys.stderr)
+        sys.exit(2)
+    kv_bytes_one = (traffic.kv_read_bytes_fp8(w.Hkv, w.D, [w.T_cap] * w.B) if fp8 else
+                    traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, [w.T_cap] * w.B))
     R = args.cache_copies or max(1, math.ceil(MIN_ROTATION_BYTES / kv_bytes_one))
     R = min(R, K + W)
     appends_per_copy = math.ceil((K + W) / R)
@@ -128,10 +137,18 @@ def main():
                "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}[args.variant]
     copies = []
     for r in range(R):
-        case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
-                                seed=w.seed + 1000 * r, device=dev, k_scale=w.k_scale)
         keep = {}
-        if args.page_size:
+        if fp8:
+            case = inputs.make_fp8_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, seed=w.seed + 1000 * r,
+                                        device=dev)
+            cache = kvd.KVCache(case.k_codes, case.v_codes, case.lengths0, w.Hq, k_exp=case.k_exp,
+                                v_exp=case.v_exp)
+        else:
+            case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
+                                    seed=w.seed + 1000 * r, device=dev, k_scale=w.k_scale)
+        if fp8:
+            pass
+        elif args.page_size:
             # the same caches laid out in shuffled pages; the page pools and
             # block table replace the contiguous tensors on the device
             kp, vp, bt = inputs.make_paged(case.k_cache, case.v_cache, args.page_size,
@@ -182,9 +199,14 @@ def main():
     flops = 0
     for i in range(W, W + K):
         L = lens[i % R] = [n + 1 for n in lens[i % R]]
-        step_bytes += traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L) + \
-            traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
-        partial_bytes += traffic.partial_pass_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L)
+        if fp8:
+            step_bytes += traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L) + \
+                traffic.append_bytes_fp8(w.B, w.Hkv, w.D)
+            partial_bytes += traffic.partial_pass_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L)
+        else:
+            step_bytes += traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L) + \
+                traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
+            partial_bytes += traffic.partial_pass_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L)
         flops += traffic.attend_flops(w.Hq, w.D, L)
     for c, L in zip(copies, lens):
         c["len"] = L  # the lengths each copy holds once the timed steps have run
@@ -215,8 +237,9 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, copies[0], T_cap)
+        cpu = cpu_baseline(w, copies[0], T_cap, fp8)
 
+    kvariant = plan["variant"] + ("_fp8" if fp8 else "")
     result = {
         "metric": "decode-attention KV-cache HBM GB/s (% of peak) and tokens/sec at 1 GPU",
         "value": round(value, 2),
@@ -229,21 +252,22 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) caches and queries)",
+        "data": ("synthetic (seeded random E4M3 cache codes and exponents, N(0,1) bf16 queries and new rows)"
+                 if fp8 else "synthetic (seeded N(0,1) caches and queries)"),
         "pct_of_peak": round(value / traffic.MI355X_HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(w.B * K / elapsed, 1),
         "kernel_us": {"partial": round(partial_ms * 1e3, 2), "combine": round(tc / K * 1e3, 2),
                       "append": round(ta / K * 1e3, 2)},
         "attend_tflops": round(flops / K / ((tp + tc) / K * 1e-3) / 1e12, 2),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
-                   "T": w.T, "cache_dtype": w.dtype, "num_splits": plan["num_splits"],
+                   "T": w.T, "cache_dtype": "fp8_e4m3" if fp8 else w.dtype, "num_splits": plan["num_splits"],
                    "split_tokens": plan["split_tokens"], "variant": plan["variant"],
                    "cache_copies": R, "seed": w.seed, "page_size": args.page_size or None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(traffic_key(w.name, args.page_size), plan["variant"]),
-                     "kernel": f"partial_{plan['variant']}_kernel"},
+                     "traffic": measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype), kvariant),
+                     "kernel": f"partial_{kvariant}_kernel"},
         "cpu_baseline": cpu,
     }
     for c in copies:
@@ -269,7 +293,7 @@ def calibrate_copy(mib: int, reps: int):
                       "copy_GBps_read_plus_write": round(2 * n / sec / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(w, copy, T_cap):
+def cpu_baseline(w, copy, T_cap, fp8=False):
     """The fp64 oracle (test infrastructure) on one full step of the same
     workload: the first copy's cache as it now stands, attended once."""
     import numpy as np
@@ -280,14 +304,22 @@ def cpu_baseline(w, copy, T_cap):
     L = np.asarray(copy["len"], dtype=np.int32)
     threads = oracle.default_threads()
     log(f"cpu baseline: copying {w.name} cache to host, oracle on {threads} threads")
-    k = inputs.host_array(case.k_cache)
-    v = inputs.host_array(case.v_cache)
-    q = inputs.host_array(case.q)
-    dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
-    t0 = time.perf_counter()
-    oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
-    sec = time.perf_counter() - t0
-    b = traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L.tolist())
+    if fp8:
+        host = [t.cpu().numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
+        q = case.q.float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.decode_attention_fp8(q, *host, L, case.scale, threads=threads)
+        sec = time.perf_counter() - t0
+        b = traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L.tolist())
+    else:
+        k = inputs.host_array(case.k_cache)
+        v = inputs.host_array(case.v_cache)
+        q = inputs.host_array(case.q)
+        dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
+        sec = time.perf_counter() - t0
+        b = traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L.tolist())
     log(f"cpu baseline: {sec:.2f} s for one step")
     return {"value": round(b / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"one full attend step of {w.name} (B={w.B}, all {w.Hq} heads, "

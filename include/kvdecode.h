@@ -60,7 +60,9 @@ extern "C" {
 
 typedef struct kvdecode_s* kvdecode_t;
 
-enum { KVD_F32 = 0, KVD_BF16 = 1 };
+/* Element types.  KVD_FP8_E4M3 is a cache type only (kvdecode_create_fp8):
+ * q, k_new, v_new and out are then bf16. */
+enum { KVD_F32 = 0, KVD_BF16 = 1, KVD_FP8_E4M3 = 2 };
 
 typedef enum {
     KVD_OK = 0,
@@ -144,6 +146,44 @@ typedef struct {
     int32_t* lengths;     /* [B] valid tokens per sequence (device int32),
                              0 <= lengths[b] <= max_pages * page_size             */
 } kvdecode_paged_desc_t;
+
+/*
+ * fp8 KV cache: keys and values are stored as OCP FP8 E4M3 codes (one byte:
+ * sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite value
+ * 448; codes 0x7F and 0xFF are NaN) with one power-of-two scale per
+ * (sequence, KV head, token): the stored row is codes * 2^e.  Half the
+ * bytes of a bf16 cache per token, plus one exponent byte each for K and V.
+ * ("All About Transformer Inference", section on tricks for generation
+ * throughput: quantizing the KV cache to int8, int4 or fp8 saves memory
+ * bandwidth; "Efficiently Scaling Transformer Inference", section 3.6:
+ * quantized storage with bf16 arithmetic in the products.  The pages fix no
+ * scale format; per-token power-of-two scales keep dequantization exact.)
+ *
+ * `cache` describes the codes: dtype KVD_FP8_E4M3, k_cache / v_cache
+ * [B, Hkv, T_cap, d] uint8, capacity a multiple of 32.  q, k_new, v_new and
+ * out are bf16.  An append quantizes each new K (and V) row: e is the
+ * smallest integer with max|x| <= 448 * 2^e (clamped to [-127, 127]; 0 for
+ * an all-zero row) and each value becomes the code nearest to x * 2^-e
+ * (ties to the even code).  Attention reads code * 2^e: exact in bf16 for
+ * every e that keeps the values within bf16's normal range.  Callers that
+ * write the cache themselves (prefill) must follow the same format.
+ * Contiguous caches only; the partial pass runs on the LDS kernel
+ * (KVD_VARIANT_AUTO or KVD_VARIANT_LDS).
+ */
+typedef struct {
+    kvdecode_desc_t cache; /* dtype KVD_FP8_E4M3; caches hold the codes              */
+    int8_t* k_exp;         /* [B, Hkv, T_cap] exponent of each key row (device)       */
+    int8_t* v_exp;         /* [B, Hkv, T_cap] exponent of each value row (device)     */
+} kvdecode_fp8_desc_t;
+
+/*
+ * Create a handle over a caller-owned fp8 cache.  Validation as for
+ * kvdecode_create, plus KVD_EINVAL for a capacity that is not a multiple of
+ * 32 or a null exponent array, KVD_EALIGN for an exponent array that is not
+ * 16-byte aligned.  kvdecode_create and kvdecode_create_paged return
+ * KVD_EUNSUPPORTED for dtype KVD_FP8_E4M3.
+ */
+int32_t kvdecode_create_fp8(const kvdecode_fp8_desc_t* desc, kvdecode_t* out);
 
 /*
  * Create a handle over a caller-owned paged cache.  Same validation and

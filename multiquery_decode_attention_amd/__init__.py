@@ -21,8 +21,9 @@ import torch
 
 __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
-    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
-    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_create", "kvdecode_create_paged",
+    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
+    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
+    "kvdecode_create_fp8",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_status",
     "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
@@ -32,7 +33,7 @@ __all__ = [
 
 KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
 KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE = -4, -5, -6, -7, -8
-KVD_F32, KVD_BF16 = 0, 1
+KVD_F32, KVD_BF16, KVD_FP8_E4M3 = 0, 1, 2
 KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS = 0, 1, 2, 3
 
 # KVD_LIBRARY may name another build of the same library (e.g. one compiled
@@ -41,7 +42,7 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libkvdecode.so")
 
 EXPORTS = (
-    "kvdecode_create", "kvdecode_create_paged", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
+    "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
     "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
@@ -79,6 +80,10 @@ class kvdecode_paged_desc_t(ctypes.Structure):
     ]
 
 
+class kvdecode_fp8_desc_t(ctypes.Structure):
+    _fields_ = [("cache", kvdecode_desc_t), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -95,6 +100,7 @@ def library():
     sig = {
         "kvdecode_create": (I, [ctypes.POINTER(kvdecode_desc_t), ctypes.POINTER(P)]),
         "kvdecode_create_paged": (I, [ctypes.POINTER(kvdecode_paged_desc_t), ctypes.POINTER(P)]),
+        "kvdecode_create_fp8": (I, [ctypes.POINTER(kvdecode_fp8_desc_t), ctypes.POINTER(P)]),
         "kvdecode_append": (I, [P, P, P, P]),
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
@@ -160,6 +166,31 @@ def kvdecode_create(k_cache: torch.Tensor, v_cache: torch.Tensor, lengths: torch
                            k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr())
     h = ctypes.c_void_p()
     _check(library().kvdecode_create(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create")
+    return h.value
+
+
+def kvdecode_create_fp8(k_codes: torch.Tensor, v_codes: torch.Tensor, k_exp: torch.Tensor,
+                        v_exp: torch.Tensor, lengths: torch.Tensor, num_q_heads: int) -> int:
+    """Handle over an fp8 cache: E4M3 codes [B, Hkv, T_cap, d] uint8 and
+    per-row power-of-two exponents [B, Hkv, T_cap] int8 for K and for V."""
+    for t in (k_codes, v_codes):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("fp8 caches must be contiguous uint8 [B, Hkv, T_cap, d] tensors of codes")
+    if k_codes.shape != v_codes.shape:
+        raise ValueError("k and v codes must match in shape")
+    for t in (k_exp, v_exp):
+        if t.dtype != torch.int8 or tuple(t.shape) != tuple(k_codes.shape[:3]) or not t.is_contiguous():
+            raise ValueError("exponents must be contiguous int8 [B, Hkv, T_cap] tensors")
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or lengths.shape[0] != k_codes.shape[0]:
+        raise ValueError("lengths must be an int32 [B] tensor")
+    if not all(t.is_cuda for t in (k_codes, v_codes, k_exp, v_exp, lengths)):
+        raise ValueError("caches, exponents and lengths must be device tensors")
+    B, Hkv, T_cap, D = k_codes.shape
+    desc = kvdecode_fp8_desc_t(kvdecode_desc_t(B, num_q_heads, Hkv, D, T_cap, KVD_FP8_E4M3,
+                                               k_codes.data_ptr(), v_codes.data_ptr(), lengths.data_ptr()),
+                               k_exp.data_ptr(), v_exp.data_ptr())
+    h = ctypes.c_void_p()
+    _check(library().kvdecode_create_fp8(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create_fp8")
     return h.value
 
 
@@ -260,14 +291,21 @@ class KVCache:
     The tensors must outlive the object; ``close()`` frees the handle.
     """
 
-    def __init__(self, k_cache, v_cache, lengths, num_q_heads: int, block_table=None):
-        """Contiguous caches [B, Hkv, T_cap, d], or -- with ``block_table``
-        [B, max_pages] -- page pools [num_pages, Hkv, page_size, d]."""
+    def __init__(self, k_cache, v_cache, lengths, num_q_heads: int, block_table=None,
+                 k_exp=None, v_exp=None):
+        """Contiguous caches [B, Hkv, T_cap, d]; or -- with ``block_table``
+        [B, max_pages] -- page pools [num_pages, Hkv, page_size, d]; or --
+        with ``k_exp``/``v_exp`` [B, Hkv, T_cap] int8 -- an fp8 cache of
+        uint8 E4M3 codes, whose queries and outputs are bf16."""
         self.k_cache, self.v_cache, self.lengths = k_cache, v_cache, lengths
         self.block_table = block_table
+        self.k_exp, self.v_exp = k_exp, v_exp
         self.Hq = num_q_heads
-        self.dtype = k_cache.dtype
-        if block_table is None:
+        self.dtype = torch.bfloat16 if k_exp is not None else k_cache.dtype
+        if k_exp is not None:
+            self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
+            self.handle = kvdecode_create_fp8(k_cache, v_cache, k_exp, v_exp, lengths, num_q_heads)
+        elif block_table is None:
             self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
             self.handle = kvdecode_create(k_cache, v_cache, lengths, num_q_heads)
         else:

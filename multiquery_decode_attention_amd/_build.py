@@ -33,12 +33,13 @@ CFLAGS = [
 ]
 
 
-# Per-file extra flags.  The LDS-staged kernel keeps its matrix-core
+# Per-file extra flags.  The LDS-staged kernels keep their matrix-core
 # accumulators in ordinary VGPRs: its rare softmax rescale multiplies them on
 # the vector ALU, and accumulators in AGPRs made the compiler copy all of
 # them between register files on every loop iteration.
 FILE_FLAGS = {
     "kvd_partial_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kvd_partial_lds_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

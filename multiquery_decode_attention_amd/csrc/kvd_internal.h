@@ -69,6 +69,10 @@ struct PartialArgs {
     const void* k_new;
     const void* v_new;
     KvLayout kv;            // contiguous or paged cache rows
+    // fp8 cache only: power-of-two exponent of each key / value row,
+    // [B, Hkv, T_cap] int8 (the row's values are code * 2^e).
+    const int8_t* k_exp;
+    const int8_t* v_exp;
     int B, Hq, Hkv, M, D, T_cap;
     int S;                  // splits per (sequence, KV head): split s owns the
                             // kernel's token tiles s, s+S, s+2S, ...
@@ -182,6 +186,20 @@ inline int lds_groups_per_cu(int D, int which) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
+
+// fp8 (OCP E4M3 codes with a power-of-two exponent per row) cache.
+// Ring depth of the fp8 LDS kernel; a stage holds K and V codes of 32
+// tokens (64*D bytes) and their exponents (a 1 KB block).
+constexpr int lds_fp8_stages(int D) { return D == 64 ? 6 : 4; }
+inline int lds_fp8_groups_per_cu(int D) {
+    const int g = LDS_BYTES_PER_CU / (lds_fp8_stages(D) * (64 * D + 1024));
+    return g < 1 ? 1 : (g > 8 ? 8 : g);
+}
+hipError_t launch_partial_lds_fp8(const PartialArgs& a, hipStream_t stream);
+// Quantize the new token's bf16 K/V rows into slot lengths[b] and advance it.
+hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             int8_t* k_exp, int8_t* v_exp, int32_t* lengths, int* err, int B,
+                             int Hkv, int D, int T_cap, hipStream_t stream);
 
 
 // Waves per work unit of the MFMA partial pass for group size M.

@@ -1,0 +1,45 @@
+// kvd_lds_common.h -- device helpers of the LDS-staged partial kernels:
+// workgroup-wide waits on the direct global->LDS loads of a ring stage.
+#pragma once
+
+#include "kvd_mfma_common.h"
+
+namespace kvd {
+namespace lds {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; a compiler memory barrier
+// so no LDS access moves across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_index() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// True when the predicate holds in any active lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
+// Wait until at most `stages_after` stages of this wave's loads (PERW
+// each) are still in flight, then meet the workgroup at the barrier.
+template <int PERW, int MAXA>
+__device__ __forceinline__ void wait_stage(int stages_after) {
+    static_assert(MAXA >= 0 && MAXA <= 6, "ring depth");
+    switch (stages_after) {
+        case 0: wait_vm_barrier<0>(); break;
+        case 1: wait_vm_barrier<(MAXA >= 1) * PERW>(); break;
+        case 2: wait_vm_barrier<(MAXA >= 2) * 2 * PERW>(); break;
+        case 3: wait_vm_barrier<(MAXA >= 3) * 3 * PERW>(); break;
+        case 4: wait_vm_barrier<(MAXA >= 4) * 4 * PERW>(); break;
+        case 5: wait_vm_barrier<(MAXA >= 5) * 5 * PERW>(); break;
+        default: wait_vm_barrier<(MAXA >= 6) * 6 * PERW>(); break;
+    }
+}
+
+}  // namespace lds
+}  // namespace kvd

@@ -43,46 +43,13 @@
 // Scaling Transformer Inference", section 3.3); base-2 softmax (same page,
 // section 3.5).  FlashDecoding++'s double-buffered shared-memory loads (the
 // blog summary of that paper) are the prior art for the staging.
-#include "kvd_mfma_common.h"
+#include "kvd_lds_common.h"
 
 namespace kvd {
 namespace {
 
 using namespace mfma;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier; a compiler memory barrier
-// so no LDS access moves across it.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Index of the calling wave in its workgroup, as a wave-uniform value.
-__device__ __forceinline__ int wave_index() {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
-// True when the predicate holds in any active lane of the wave.
-__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
-
-// Wait until at most `stages_after` stages of this wave's loads (PERW
-// each) are still in flight, then meet the workgroup at the barrier.
-template <int PERW, int MAXA>
-__device__ __forceinline__ void wait_stage(int stages_after) {
-    static_assert(MAXA >= 0 && MAXA <= 6, "ring depth");
-    switch (stages_after) {
-        case 0: wait_vm_barrier<0>(); break;
-        case 1: wait_vm_barrier<(MAXA >= 1) * PERW>(); break;
-        case 2: wait_vm_barrier<(MAXA >= 2) * 2 * PERW>(); break;
-        case 3: wait_vm_barrier<(MAXA >= 3) * 3 * PERW>(); break;
-        case 4: wait_vm_barrier<(MAXA >= 4) * 4 * PERW>(); break;
-        case 5: wait_vm_barrier<(MAXA >= 5) * 5 * PERW>(); break;
-        default: wait_vm_barrier<(MAXA >= 6) * 6 * PERW>(); break;
-    }
-}
+using namespace lds;
 
 template <int D, int NS, int VL, bool PAGED>
 __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int head_groups) {

@@ -1,0 +1,330 @@
+// kvd_partial_lds_fp8.hip -- split-KV partial pass over an fp8 KV cache.
+//
+// The cache holds OCP FP8 E4M3 codes (one byte per value) and, per
+// (sequence, KV head, token), a power-of-two exponent e: the stored value is
+// code * 2^e.  Queries, the appended rows and the output are bf16.  The
+// kernel has the structure of the bf16 LDS kernel -- one workgroup of four
+// waves per (split, sequence, KV head), a ring of NS stages filled by direct
+// global->LDS loads, matrix-core score and value products, a lazily raised
+// softmax reference -- with half the bytes per tile:
+//   - K codes are widened to bf16 as they are read from LDS for the score
+//     product, with gfx950's scaled conversion, whose scale operand carries
+//     the row's 2^e (it uses the scale's exponent only, and every E4M3 value
+//     times a power of two within range is exact in bf16);
+//   - V codes are widened with scale 1, and each token's 2^e multiplies its
+//     softmax weight before the weights are packed for the value product
+//     (the normaliser sums the unscaled weights).
+// A stage holds 32 K rows and 32 V rows of codes (K chunks XOR-swizzled by
+// row as in the bf16 kernel) and a 1 KB block whose first 64 bytes are the
+// tile's 32 K and 32 V exponents, loaded by one more 16-byte direct load per
+// wave.  Rows past the sequence's end re-read its last valid row (their
+// weights are zero, and finite codes keep the products finite).
+//
+// Sources: quantized KV caches save memory bandwidth ("All About Transformer
+// Inference", section on tricks for generation throughput); quantized
+// storage with bf16 arithmetic for the products ("Efficiently Scaling
+// Transformer Inference", section 3.6); the attention itself as in the bf16
+// kernel ("All About Transformer Inference", section "Sharding the KV
+// cache"; "Efficiently Scaling Transformer Inference", sections 3.3, 3.5).
+#include "kvd_lds_common.h"
+
+namespace kvd {
+namespace {
+
+using namespace mfma;
+using namespace lds;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// 2^e as an fp32 whose exponent field is e + 127 (e in [-127, 127]); the
+// scaled conversions read only that field.
+__device__ __forceinline__ float pow2_scale(int e) {
+    e = max(-127, min(127, e));
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// Two E4M3 codes (bytes 2h, 2h+1 of w) times 2^e(scale) as a bf16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t widen2(uint32_t w, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI));
+}
+
+// Eight codes (two dwords) -> a bf16x8 matrix-core operand.
+__device__ __forceinline__ u32x4_t widen8(u32x2_t x, float scale) {
+    u32x4_t o;
+    o[0] = widen2<false>(x[0], scale);
+    o[1] = widen2<true>(x[0], scale);
+    o[2] = widen2<false>(x[1], scale);
+    o[3] = widen2<true>(x[1], scale);
+    return o;
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int head_groups) {
+    constexpr int CH = D / 16;                   // 16-byte chunks per row of codes
+    constexpr int SWZ = CH - 1;                  // K chunk swizzle mask
+    constexpr int KS = D / 32;                   // k-steps of the score product
+    constexpr int NE = D / 16;                   // output column blocks per lane
+    constexpr int REGION = MFMA_TILE * D;        // bytes of K (or V) codes per stage
+    constexpr int EXPS = 1024;                   // exponent block per stage
+    constexpr int STAGE = 2 * REGION + EXPS;
+    constexpr int PERWD = 2 * REGION / (4 * 64 * 16);  // code loads per wave per stage (D/64)
+    constexpr int PERW = PERWD + 1;                     // + the exponent load
+    constexpr float TAU = 8.f;
+    static_assert(PERWD >= 1 && REGION == 2 * PERWD * 64 * 16, "waves 0-1 load K, waves 2-3 load V");
+    static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
+
+    const BlockCoord bc = block_coord(a.B * a.Hkv * head_groups);
+    const int s = bc.split;
+    const int hg = bc.unit % head_groups;
+    const int g = (bc.unit / head_groups) % a.Hkv;
+    const int b = bc.unit / (head_groups * a.Hkv);
+    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
+                                    s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
+    const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
+    if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
+    const int t_end = len;
+    const int n_tiles = (n_seq_tiles - s + a.S - 1) / a.S;
+    const int tstride = a.S * MFMA_TILE;
+    const int t_first = s * MFMA_TILE;
+
+    const int wave = wave_index();
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, gq = lane >> 4;
+    const int mg = min(a.M - hg * 64, 64);
+    const int hpw = (mg + 3) / 4;
+    const int hw0 = hg * 64 + wave * hpw;
+    const int nh = max(0, min(hpw, mg - wave * hpw));
+    const bool head_ok = c < nh;
+
+    const size_t slab = kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
+    const char* kb = static_cast<const char*>(a.k_cache) + slab * D;
+    const char* vb = static_cast<const char*>(a.v_cache) + slab * D;
+    const char* ke = reinterpret_cast<const char*>(a.k_exp) + slab;
+    const char* ve = reinterpret_cast<const char*>(a.v_exp) + slab;
+
+    // Queries (bf16), as in the bf16 kernel: lanes past the wave's last head
+    // load a copy of its last row.
+    u32x4_t qop[KS];
+    {
+        const int hq = hw0 + (head_ok ? c : max(nh - 1, 0));
+        const uint16_t* qrow =
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hq) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qrow + 32 * ks + 8 * gq);
+    }
+
+    // Code loads of one stage: chunks j0 .. j0+63, j0 = (wave*PERWD + n)*64;
+    // waves 0-1 the K rows (swizzled), waves 2-3 the V rows.
+    const bool v_wave = wave >= 2;
+    uint32_t doff[PERWD];
+#pragma unroll
+    for (int n = 0; n < PERWD; ++n) {
+        const int j0 = (wave * PERWD + n) * 64;
+        const int j = (v_wave ? j0 - MFMA_TILE * CH : j0) + lane;
+        const int t = j / CH;
+        const int p = v_wave ? j % CH : (j % CH) ^ (t & SWZ);
+        doff[n] = (uint32_t)((t * CH + p) * 16);
+    }
+    // Exponent load: lane l fetches 16 bytes -- K exponents of tokens
+    // 16(l&1) .. +15 for (l&3) < 2, else V exponents -- into byte 16 l of the
+    // block; the first 64 bytes are K[0..31], V[0..31].  Every wave issues
+    // it (same bytes, same place), so all waves count PERW loads per stage.
+    const int xl = lane & 3;
+    auto issue = [&](int st) {
+        unsigned char* stage = lds + (st % NS) * STAGE;
+        const char* tbase = v_wave ? vb : kb;
+        if (st >= n_tiles) {
+#pragma unroll
+            for (int n = 0; n < PERWD; ++n) {
+                const int j0 = (wave * PERWD + n) * 64;
+                __builtin_amdgcn_global_load_lds((const void*)tbase, (lds_void_t*)(stage + j0 * 16), 16, 0, 0);
+            }
+            __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)(stage + 2 * REGION), 16, 0, 0);
+            return;
+        }
+        const int t0 = t_first + st * tstride;
+        const char* base = tbase + (size_t)t0 * D;
+        if (t0 + MFMA_TILE <= t_end) {
+#pragma unroll
+            for (int n = 0; n < PERWD; ++n) {
+                const int j0 = (wave * PERWD + n) * 64;
+                __builtin_amdgcn_global_load_lds((const void*)(base + doff[n]),
+                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 2);
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < PERWD; ++n) {
+                const int j0 = (wave * PERWD + n) * 64;
+                const int t = (int)(doff[n] / D);
+                const int row = min(t, t_end - 1 - t0);
+                __builtin_amdgcn_global_load_lds((const void*)(base + (int)doff[n] + (row - t) * D),
+                                                 (lds_void_t*)(stage + j0 * 16), 16, 0, 2);
+            }
+        }
+        const char* xsrc = (xl < 2 ? ke : ve) + t0 + 16 * (xl & 1);
+        __builtin_amdgcn_global_load_lds((const void*)xsrc, (lds_void_t*)(stage + 2 * REGION), 16, 0, 0);
+    };
+
+    // LDS read offsets of the score operand: k-step ks, rows c and 16+c,
+    // bytes 32ks + 8gq .. +7 (half of a swizzled chunk).
+    uint32_t koff[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int t = 16 * sb + c;
+            const int p = 2 * ks + (gq >> 1);
+            koff[sb][ks] = (uint32_t)((t * CH + (p ^ (t & SWZ))) * 16 + 8 * (gq & 1));
+        }
+    }
+
+    f32x4_t acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, l_run = 0.f;
+
+#pragma unroll
+    for (int i = 0; i < NS - 1; ++i) issue(i);
+
+    if (nh == 0) {
+        for (int it = 0; it < n_tiles; ++it) {
+            wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
+            if (it + NS - 1 < n_tiles) issue(it + NS - 1);
+        }
+        return;
+    }
+
+    for (int it = 0; it < n_tiles; ++it) {
+        wait_stage<PERW, NS - 2>(min(n_tiles - 1, it + NS - 2) - it);
+        if (it + NS - 1 < n_tiles) issue(it + NS - 1);
+        const unsigned char* Kl = lds + (it % NS) * STAGE;
+        const unsigned char* Vl = Kl + REGION;
+        const signed char* X = reinterpret_cast<const signed char*>(Kl + 2 * REGION);
+        const int t0 = t_first + it * tstride;
+
+        // scores: K rows c and 16+c widened with their own 2^e
+        const float sk0 = pow2_scale(X[c]), sk1 = pow2_scale(X[16 + c]);
+        f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x2_t k0 = *reinterpret_cast<const u32x2_t*>(Kl + koff[0][ks]);
+            const u32x2_t k1 = *reinterpret_cast<const u32x2_t*>(Kl + koff[1][ks]);
+            sc[0] = mfma16x16x32(widen8(k0, sk0), qop[ks], sc[0]);
+            sc[1] = mfma16x16x32(widen8(k1, sk1), qop[ks], sc[1]);
+        }
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
+        if (t0 + MFMA_TILE > t_end) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (wave_any(mx > m_ref + TAU)) {
+            const float m_new = mx > m_ref + TAU ? mx : m_ref;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_run *= alpha;
+            m_ref = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * gq + i);
+#pragma unroll
+                for (int e = 0; e < NE; ++e) acc[e][i] *= ai;
+            }
+        }
+
+        // weights: the normaliser sums them as they are; the value product
+        // takes them times their token's 2^e
+        const uint32_t xv0 = *reinterpret_cast<const uint32_t*>(X + 32 + 4 * gq);
+        const uint32_t xv1 = *reinterpret_cast<const uint32_t*>(X + 48 + 4 * gq);
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
+            l_run += p[j];
+            const uint32_t w = j < 4 ? xv0 : xv1;
+            p[j] *= pow2_scale((int)(signed char)(w >> (8 * (j & 3))));
+        }
+        u32x4_t pop;
+        pop[0] = pack_bf16x2(p[0], p[1]);
+        pop[1] = pack_bf16x2(p[2], p[3]);
+        pop[2] = pack_bf16x2(p[4], p[5]);
+        pop[3] = pack_bf16x2(p[6], p[7]);
+        if constexpr (D >= 128) {
+#pragma unroll
+            for (int i = 0; i < D / 128; ++i) {
+                uint32_t v[8][4];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const u32x2_t xw = *reinterpret_cast<const u32x2_t*>(Vl + slot_token(gq, j) * D + 128 * i + 8 * c);
+                    const u32x4_t w = widen8(xw, 1.0f);
+                    v[j][0] = w[0];
+                    v[j][1] = w[1];
+                    v[j][2] = w[2];
+                    v[j][3] = w[3];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[8 * i + e] = mfma16x16x32(pop, v_operand(v, e), acc[8 * i + e]);
+            }
+        } else {
+            uint32_t v[8][2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t xw = *reinterpret_cast<const uint32_t*>(Vl + slot_token(gq, j) * D + 4 * c);
+                v[j][0] = widen2<false>(xw, 1.0f);
+                v[j][1] = widen2<true>(xw, 1.0f);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = mfma16x16x32(pop, v_operand(v, e), acc[e]);
+        }
+    }
+
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const size_t row0 = ((size_t)b * a.Hq + (size_t)g * a.M + hw0) * a.S + s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * gq + i;
+        const float li = __shfl(l, r);
+        if (r < nh) {
+            const float inv = 1.f / li;
+            float* orow = a.o_part + (row0 + (size_t)r * a.S) * D;
+#pragma unroll
+            for (int e = 0; e < NE; e += 4) {
+                const f32x4_t o = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv};
+                __builtin_nontemporal_store(o, reinterpret_cast<f32x4_t*>(orow + owned_col<D>(c, e)));
+            }
+        }
+    }
+    if (gq == 0 && head_ok)
+        __builtin_nontemporal_store(m_ref + __builtin_log2f(l), a.lse_part + row0 + (size_t)c * a.S);
+}
+
+template <int D>
+hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
+    const int groups = (a.M + 63) / 64;
+    dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
+    hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D)>), grid, dim3(256), 0, stream, a, groups);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial_lds_fp8(const PartialArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 64: return launch_d<64>(a, stream);
+        case 128: return launch_d<128>(a, stream);
+        case 256: return launch_d<256>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvd

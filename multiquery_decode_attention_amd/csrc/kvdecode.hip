@@ -16,6 +16,9 @@
 struct kvdecode_s {
     kvdecode_desc_t d;          // for a paged cache: the pools, and capacity = max_pages * page_size
     kvd::KvLayout kv{nullptr, 0, 0, 0};
+    // fp8 cache (d.dtype == KVD_FP8_E4M3): per-row power-of-two exponents
+    int8_t* k_exp = nullptr;
+    int8_t* v_exp = nullptr;
     int M = 1;
     int elem = 4;
     int variant_req = KVD_VARIANT_AUTO;
@@ -58,8 +61,11 @@ struct Plan {
     int lds_config;  // kvd::LDS_SHORT or kvd::LDS_LONG (LDS kernel)
 };
 
+bool is_fp8(const kvdecode_s* h) { return h->d.dtype == KVD_FP8_E4M3; }
+
 int resolve_variant(const kvdecode_s* h) {
     if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
+    if (is_fp8(h)) return KVD_VARIANT_LDS;
     return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
 }
 
@@ -87,7 +93,8 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which) {
     Shape sh;
     if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((h->M + 63) / 64);
-        sh.slots = (long long)CUS * kvd::lds_groups_per_cu(h->d.head_dim, lds_which);
+        sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
+                                               : kvd::lds_groups_per_cu(h->d.head_dim, lds_which));
     } else if (variant == KVD_VARIANT_MFMA) {
         const int hb = kvd::mfma_head_blocks(h->M);
         const int nw = hb < 4 ? hb : 4;
@@ -103,7 +110,7 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which) {
 
 // Cost-model choice of the split count for one kernel shape.
 long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles) {
-    const double tok_bytes = 2.0 * h->d.head_dim * h->elem;        // K+V of one token
+    const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * (h->d.head_dim + 1) * 4 * 2;
     double best = 0;
@@ -138,7 +145,7 @@ Plan make_plan(const kvdecode_s* h) {
         p.splits = (int)s;
         p.chunk = (int)((n_tiles + s - 1) / s * p.tile);
     };
-    if (p.variant == KVD_VARIANT_LDS && h->d.head_dim == 256) {
+    if (p.variant == KVD_VARIANT_LDS && h->d.head_dim == 256 && !is_fp8(h)) {
         const long long s = clamp_splits(h->forced_splits > 0
                                              ? h->forced_splits
                                              : plan_splits(h, shape_for(h, p.variant, kvd::LDS_LONG),
@@ -228,9 +235,13 @@ int32_t ensure_events(kvdecode_s* h) {
 int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st) {
     const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths, h->err,
-                                      h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
-                                      h->elem, st);
+    hipError_t e =
+        is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp,
+                                           h->d.lengths, h->err, h->d.batch, h->d.num_kv_heads,
+                                           h->d.head_dim, h->d.capacity, st)
+                  : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths,
+                                       h->err, h->d.batch, h->d.num_kv_heads, h->d.head_dim,
+                                       h->d.capacity, h->elem, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed) {
         if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
@@ -249,13 +260,15 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
     const Plan p = make_plan(h);
-    if (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    if (is_fp8(h) ? p.variant != KVD_VARIANT_LDS : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
+        return KVD_EUNSUPPORTED;
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
     const bool with_append = k_new != nullptr;
-    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA;
+    // the fp8 append quantizes in its own kernel, before the partial pass
+    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA && !is_fp8(h);
     if (with_append && !fused) {
         if ((rc = launch_append_timed(h, k_new, v_new, st)) != KVD_OK) return rc;
     }
@@ -281,6 +294,8 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.scale_log2e = scale * kvd::LOG2E;
     a.lds_config = p.lds_config;
     a.kv = h->kv;
+    a.k_exp = h->k_exp;
+    a.v_exp = h->v_exp;
 
     kvd::CombineArgs c;
     c.o_part = h->o_part;
@@ -298,12 +313,13 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = p.variant == KVD_VARIANT_LDS    ? kvd::launch_partial_lds(a, st)
+    hipError_t e = is_fp8(h)                       ? kvd::launch_partial_lds_fp8(a, st)
+                   : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
                                                    : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
-    e = kvd::launch_combine(c, h->d.dtype == KVD_BF16, st);
+    e = kvd::launch_combine(c, h->d.dtype != KVD_F32, st);  // fp8 caches give bf16 outputs
     if (e != hipSuccess) return KVD_EHIP;
     if (timed) {
         if (hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
@@ -341,7 +357,7 @@ int32_t make_handle(const kvdecode_desc_t& d, const kvd::KvLayout& kv, kvdecode_
     if (d.capacity > (1 << 24)) return KVD_EINVAL;
     if (d.num_q_heads % d.num_kv_heads != 0) return KVD_EINVAL;
     if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return KVD_EUNSUPPORTED;
-    if (d.dtype != KVD_F32 && d.dtype != KVD_BF16) return KVD_EUNSUPPORTED;
+    if (d.dtype != KVD_F32 && d.dtype != KVD_BF16 && d.dtype != KVD_FP8_E4M3) return KVD_EUNSUPPORTED;
     if (!d.k_cache || !d.v_cache || !d.lengths) return KVD_EINVAL;
     if (!aligned16(d.k_cache) || !aligned16(d.v_cache) ||
         (reinterpret_cast<uintptr_t>(d.lengths) & 3u))
@@ -351,7 +367,7 @@ int32_t make_handle(const kvdecode_desc_t& d, const kvd::KvLayout& kv, kvdecode_
     h->d = d;
     h->kv = kv;
     h->M = d.num_q_heads / d.num_kv_heads;
-    h->elem = d.dtype == KVD_F32 ? 4 : 2;
+    h->elem = d.dtype == KVD_F32 ? 4 : (d.dtype == KVD_BF16 ? 2 : 1);
     {
         std::lock_guard<std::mutex> lk(g_mu);
         live().insert(h);
@@ -364,7 +380,24 @@ int32_t make_handle(const kvdecode_desc_t& d, const kvd::KvLayout& kv, kvdecode_
 
 int32_t kvdecode_create(const kvdecode_desc_t* desc, kvdecode_t* out) {
     if (!desc || !out) return KVD_EINVAL;
+    if (desc->dtype == KVD_FP8_E4M3) return KVD_EUNSUPPORTED;  // kvdecode_create_fp8
     return make_handle(*desc, kvd::KvLayout{nullptr, 0, 0, 0}, out);
+}
+
+int32_t kvdecode_create_fp8(const kvdecode_fp8_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    *out = nullptr;
+    kvdecode_desc_t d = desc->cache;
+    if (d.dtype != KVD_FP8_E4M3) return KVD_EUNSUPPORTED;
+    if (d.capacity < 1 || d.capacity % 32 != 0) return KVD_EINVAL;
+    if (!desc->k_exp || !desc->v_exp) return KVD_EINVAL;
+    if (!aligned16(desc->k_exp) || !aligned16(desc->v_exp)) return KVD_EALIGN;
+    const int32_t rc = make_handle(d, kvd::KvLayout{nullptr, 0, 0, 0}, out);
+    if (rc == KVD_OK) {
+        (*out)->k_exp = desc->k_exp;
+        (*out)->v_exp = desc->v_exp;
+    }
+    return rc;
 }
 
 int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out) {
@@ -377,6 +410,7 @@ int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out
     // every row index of the pool fits the kernels' 32-bit row arithmetic
     if ((long long)p.num_pages * p.num_kv_heads * p.page_size > (1LL << 31)) return KVD_EINVAL;
     if (!p.block_table) return KVD_EINVAL;
+    if (p.dtype == KVD_FP8_E4M3) return KVD_EUNSUPPORTED;  // fp8 caches are contiguous
     if (reinterpret_cast<uintptr_t>(p.block_table) & 3u) return KVD_EALIGN;
     kvdecode_desc_t d;
     d.batch = p.batch;
@@ -453,6 +487,9 @@ int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
     if (!is_live(h)) return KVD_EINVAL;
     if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_LDS) return KVD_EUNSUPPORTED;
+    if (is_fp8(h)) return variant == KVD_VARIANT_AUTO || variant == KVD_VARIANT_LDS
+                              ? (h->variant_req = variant, KVD_OK)
+                              : KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;

@@ -145,6 +145,52 @@ def make_workload_case(w: Workload, device="cpu", seed: Optional[int] = None,
                      w.seed if seed is None else seed, device, k_scale=w.k_scale)
 
 
+@dataclasses.dataclass
+class Fp8Case:
+    """One decode step over an fp8 cache: E4M3 codes and per-row
+    power-of-two exponents (value = code * 2^e); bf16 query and new rows."""
+    q: torch.Tensor          # [B, Hq, D] bf16
+    k_codes: torch.Tensor    # [B, Hkv, T_cap, D] uint8
+    k_exp: torch.Tensor      # [B, Hkv, T_cap] int8
+    v_codes: torch.Tensor
+    v_exp: torch.Tensor
+    lengths0: torch.Tensor   # [B] int32, before the step's append
+    k_new: torch.Tensor      # [B, Hkv, D] bf16
+    v_new: torch.Tensor
+    scale: float
+
+
+def _e4m3_codes(shape, gen, device):
+    """Random finite E4M3 codes: uniform sign and mantissa, exponent field
+    8..15 (magnitudes 2 .. 448, where a row scaled to its largest value
+    puts most codes); the NaN pattern S.1111.111 is mapped to S.1111.110."""
+    S = torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int32)
+    E = torch.randint(8, 16, shape, generator=gen, device=device, dtype=torch.int32)
+    M = torch.randint(0, 8, shape, generator=gen, device=device, dtype=torch.int32)
+    M = torch.where((E == 15) & (M == 7), torch.full_like(M, 6), M)
+    return ((S << 7) | (E << 3) | M).to(torch.uint8)
+
+
+def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu") -> Fp8Case:
+    """Seeded fp8-cache case: the cache is drawn directly as codes and
+    exponents (no quantization here: that is the method's own step, done by
+    the append under test and by the oracle); q and the new rows are N(0,1)
+    rounded to bf16."""
+    lengths_attended = torch.as_tensor(lengths_attended, dtype=torch.int32).cpu()
+    assert lengths_attended.shape == (B,)
+    assert int(lengths_attended.min()) >= 1 and int(lengths_attended.max()) <= T_cap
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    q = _normal((B, Hq, D), gen, device, torch.bfloat16)
+    k_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
+    v_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
+    k_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
+    v_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
+    k_new = _normal((B, Hkv, D), gen, device, torch.bfloat16)
+    v_new = _normal((B, Hkv, D), gen, device, torch.bfloat16)
+    lengths0 = (lengths_attended - 1).to(torch.int32).to(device)
+    return Fp8Case(q, k_codes, k_exp, v_codes, v_exp, lengths0, k_new, v_new, float(D) ** -0.5)
+
+
 def make_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, seed: int,
                spare_pages: Optional[int] = None):
     """Lay contiguous caches [B, Hkv, T_cap, D] out as a page pool.

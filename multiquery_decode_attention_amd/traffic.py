@@ -43,6 +43,30 @@ def append_bytes(B: int, Hkv: int, D: int, elem: int) -> int:
     return 4 * B * Hkv * D * elem
 
 
+# fp8 cache: one byte per value plus one exponent byte per K row and per V
+# row; queries, outputs and the appended rows stay bf16.
+
+def kv_read_bytes_fp8(kv_heads: int, head_dim: int, lengths: Sequence[int]) -> int:
+    """K and V codes and exponents of every valid cached token."""
+    return 2 * kv_heads * (head_dim + 1) * sum(int(n) for n in lengths)
+
+
+def partial_pass_bytes_fp8(B: int, Hq: int, Hkv: int, D: int, lengths: Sequence[int]) -> int:
+    """Partial-kernel reads over an fp8 cache: codes and exponents of the
+    valid prefixes plus the bf16 queries."""
+    return kv_read_bytes_fp8(Hkv, D, lengths) + B * Hq * D * 2
+
+
+def attend_bytes_fp8(B: int, Hq: int, Hkv: int, D: int, lengths: Sequence[int]) -> int:
+    """Whole attend pass over an fp8 cache (bf16 q in, bf16 out)."""
+    return kv_read_bytes_fp8(Hkv, D, lengths) + 2 * B * Hq * D * 2
+
+
+def append_bytes_fp8(B: int, Hkv: int, D: int) -> int:
+    """Read the new bf16 K and V rows, write their codes and exponents."""
+    return 2 * B * Hkv * D * 2 + 2 * B * Hkv * (D + 1)
+
+
 def attend_flops(Hq: int, D: int, lengths: Sequence[int]) -> int:
     """2*D for the score and 2*D for the value product per (head, token)."""
     return 4 * Hq * D * sum(int(n) for n in lengths)

@@ -212,3 +212,38 @@ def test_binding_fails_loudly_without_library(tmp_path):
     )
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert "missing-raised" in r.stdout, r.stderr
+
+
+def make_fp8_desc(**kw):
+    cache = dict(batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, capacity=64,
+                 dtype=kvd.KVD_FP8_E4M3, k_cache=FAKE, v_cache=FAKE * 2, lengths=FAKE * 3)
+    exps = dict(k_exp=FAKE * 4, v_exp=FAKE * 5)
+    for k, v in kw.items():
+        (exps if k in exps else cache)[k] = v
+    return kvd.kvdecode_fp8_desc_t(kvd.kvdecode_desc_t(**cache), exps["k_exp"], exps["v_exp"])
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("capacity", 48, kvd.KVD_EINVAL), ("capacity", 0, kvd.KVD_EINVAL),
+    ("k_exp", 0, kvd.KVD_EINVAL), ("v_exp", FAKE + 4, kvd.KVD_EALIGN),
+    ("dtype", kvd.KVD_BF16, kvd.KVD_EUNSUPPORTED), ("head_dim", 96, kvd.KVD_EUNSUPPORTED),
+])
+def test_create_fp8_rejects(lib, field, value, code):
+    h = ctypes.c_void_p()
+    rc = lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc(**{field: value})), ctypes.byref(h))
+    assert rc == code and not h.value
+
+
+def test_fp8_handle(lib):
+    h = ctypes.c_void_p()
+    assert lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc()), ctypes.byref(h)) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
+    for v in (kvd.KVD_VARIANT_VALU, kvd.KVD_VARIANT_MFMA):
+        assert lib.kvdecode_set_variant(h.value, v) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_LDS) == kvd.KVD_OK
+    assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
+    # the fp8 cache type is only reachable through kvdecode_create_fp8
+    rc, h2 = create(lib, make_desc(dtype=kvd.KVD_FP8_E4M3))
+    assert rc == kvd.KVD_EUNSUPPORTED and not h2
+    rc, h3 = create_paged(lib, make_paged_desc(dtype=kvd.KVD_FP8_E4M3))
+    assert rc == kvd.KVD_EUNSUPPORTED and not h3

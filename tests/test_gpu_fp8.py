@@ -1,0 +1,120 @@
+"""GPU parity of the fp8 (E4M3 + per-row power-of-two exponent) KV cache.
+
+The cache is drawn as codes and exponents; the step's new bf16 rows are
+quantized by the library's append and by the oracle's append_fp8, which
+must agree bit for bit on every code, exponent and length.  Attention is
+compared with the oracle's fp64 attention over the dequantized cache, to
+the bf16 tolerance (the kernel widens codes to bf16 exactly; its error is
+the bf16 rounding of the weights and of the output, as in the bf16 path).
+"""
+import numpy as np
+import pytest
+import torch
+
+import multiquery_decode_attention_amd as kvd
+import oracle
+from multiquery_decode_attention_amd import inputs
+from conftest import TOL_BF16, rel_err_rows
+from gpu_helpers import say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None):
+    dev = torch.device("cuda")
+    kc, vc = case.k_codes.to(dev, copy=True), case.v_codes.to(dev, copy=True)
+    ke, ve = case.k_exp.to(dev, copy=True), case.v_exp.to(dev, copy=True)
+    L = (lengths if lengths is not None else case.lengths0).to(dev, torch.int32, copy=True)
+    cache = kvd.KVCache(kc, vc, L, Hq, k_exp=ke, v_exp=ve)
+    try:
+        if splits is not None:
+            cache.set_num_splits(splits)
+        plan = cache.plan()
+        kn, vn, q = (t.to(dev).contiguous() for t in (case.k_new, case.v_new, case.q))
+        if fused:
+            out = cache.step(kn, vn, q, scale=case.scale)
+        else:
+            cache.append(kn, vn)
+            out = cache.attend(q, scale=case.scale)
+        status = cache.status()
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    return out, kc, ke, vc, ve, L, status, plan
+
+
+def oracle_fp8_step(case, lengths=None):
+    L = (lengths if lengths is not None else case.lengths0).cpu().numpy().astype(np.int32)
+    f32 = lambda t: t.float().cpu().numpy()
+    kc, ke, vc, ve, L2, _ = oracle.append_fp8(case.k_codes.numpy(), case.k_exp.numpy(), case.v_codes.numpy(),
+                                              case.v_exp.numpy(), L, f32(case.k_new), f32(case.v_new))
+    ref = oracle.decode_attention_fp8(f32(case.q), kc, ke, vc, ve, L2, case.scale)
+    return ref, kc, ke, vc, ve, L2
+
+
+def check_fp8(case, Hq, name, **kw):
+    say(f"{name}: fp8 B={case.q.shape[0]} Hq={Hq} Hkv={case.k_codes.shape[1]} "
+        f"T_cap={case.k_codes.shape[2]} D={case.q.shape[2]} {kw}")
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, Hq, **kw)
+    say(f"{name}: gpu done, plan={plan}, status={status}")
+    ref, kc2, ke2, vc2, ve2, L2 = oracle_fp8_step(case, kw.get("lengths"))
+    assert status == kvd.KVD_OK
+    assert np.array_equal(L.cpu().numpy(), L2)
+    assert np.array_equal(ke.cpu().numpy(), ke2) and np.array_equal(ve.cpu().numpy(), ve2), "exponents differ"
+    assert np.array_equal(kc.cpu().numpy(), kc2), "K codes differ after append"
+    assert np.array_equal(vc.cpu().numpy(), vc2), "V codes differ after append"
+    err = rel_err_rows(to_f64(out), ref)
+    say(f"{name}: max row-relative error {err:.3e} (tol {TOL_BF16:.0e})")
+    assert err <= TOL_BF16, err
+    return out, plan
+
+
+SHAPES = {  # name: (B, Hq, Hkv, D, T_cap, lengths)
+    "palm_like": (3, 48, 1, 256, 2048, [2048, 1000, 33]),
+    "mha_like": (2, 40, 40, 128, 4096, [4096, 1500]),
+    "ragged_gqa_like": (8, 64, 8, 128, 8192, [64, 8192, 4000, 77, 1024, 5000, 31, 8000]),
+    "long_mqa": (1, 48, 1, 256, 16384, [16384]),
+    "small_d64": (2, 8, 1, 64, 160, [129, 64]),
+}
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_fp8_shapes(name, fused):
+    B, Hq, Hkv, D, T, L = SHAPES[name]
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=90 + len(name))
+    check_fp8(case, Hq, f"fp8/{name}", fused=fused)
+
+
+@pytest.mark.parametrize("splits", [1, 5])
+def test_fp8_forced_splits(splits):
+    lengths = [1, 31, 32, 33, 64, 65, 127, 128, 200, 256]
+    case = inputs.make_fp8_case(len(lengths), 16, 2, 128, 256, lengths, seed=95 + splits)
+    check_fp8(case, 16, f"fp8 S={splits}", splits=splits)
+
+
+def test_fp8_append_extremes():
+    """An all-zero row (exponent 0), a row needing a positive exponent, a
+    row of tiny values and exact midpoints between codes."""
+    B, Hq, Hkv, D, T = 4, 8, 2, 128, 64
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, [10, 20, 30, 40], seed=97)
+    kn = case.k_new.float()
+    kn[0, 0] = 0.0
+    kn[1, 1] *= 5000.0
+    kn[2, 0] *= 1e-6
+    # midpoints of E4M3 neighbours, scaled so the row's maximum is exactly 448 * 2^-7
+    kn[3, 0] = torch.tensor([1.0625, 1.1875, -1.0625, 448.0] * (D // 4)) * 2.0 ** -7
+    case.k_new = kn.to(torch.bfloat16)
+    case.v_new = (case.v_new.float() * 300.0).to(torch.bfloat16)
+    check_fp8(case, Hq, "fp8 append extremes")
+
+
+def test_fp8_capacity_overflow():
+    case = inputs.make_fp8_case(2, 8, 1, 128, 64, [64, 10], seed=98)
+    L0 = torch.tensor([64, 9], dtype=torch.int32)
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, 8, lengths=L0)
+    assert status == kvd.KVD_ECAPACITY
+    assert L.cpu().tolist() == [64, 10]
+    ref, kc2, ke2, vc2, ve2, L2 = oracle_fp8_step(case, lengths=L0)
+    assert np.array_equal(kc.cpu().numpy(), kc2) and np.array_equal(ke.cpu().numpy(), ke2)
+    assert rel_err_rows(to_f64(out), ref) <= TOL_BF16

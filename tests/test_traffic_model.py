@@ -68,3 +68,18 @@ def test_ragged_lengths_recipe():
     L = attended_lengths(w)
     assert L.min() >= 64 and L.max() <= 8192 and len(set(L.tolist())) > 100
     assert attended_lengths(w).tolist() == L.tolist()  # seeded
+
+
+def test_fp8_byte_counts():
+    """fp8 cache: one byte per value plus an exponent byte per K and per V
+    row; bf16 queries and outputs.  The long-context step reads a little
+    over half the bf16 bytes."""
+    w = WORKLOADS["longctx_mqa_bf16"]
+    L = [65536] * 8
+    kv = traffic.kv_read_bytes_fp8(w.Hkv, w.D, L)
+    assert kv == 2 * 1 * (256 + 1) * 65536 * 8
+    assert traffic.partial_pass_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L) == kv + 8 * 48 * 256 * 2
+    assert traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L) == kv + 2 * 8 * 48 * 256 * 2
+    ratio = kv / traffic.kv_read_bytes(w.Hkv, w.D, 2, L)
+    assert ratio == pytest.approx(257 / 512)
+    assert traffic.append_bytes_fp8(8, 1, 256) == 2 * 8 * 256 * 2 + 2 * 8 * 257
