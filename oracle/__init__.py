@@ -40,8 +40,19 @@ input generators, which hold none of the method's arithmetic.
   products).  The pages fix no scale format: per-token power-of-two scales
   are this library's choice.
 
+* Several new tokens per sequence (a speculative-verify step): ``append_multi``
+  writes T_q new K/V rows at slots lengths[b] .. lengths[b]+T_q-1 (or none,
+  when they do not fit), and ``decode_attention_multi`` lets query i of
+  sequence b attend over the tokens before it and itself: the first
+  n - a + min(i + 1, a) cached tokens, with n the length after the append
+  and a the number of rows appended.  Source: "All About Transformer
+  Inference", appendix on speculative sampling (the large model scores all
+  drafted tokens in one pass, sharing the KV cache load) and section
+  "Transformer inference basics" (a token attends to the tokens before it).
+
 Parity status: every function is pinned by ``tests/test_oracle_pins.py``,
-``tests/test_oracle_paged.py`` and ``tests/test_oracle_fp8.py``
+``tests/test_oracle_paged.py``, ``tests/test_oracle_fp8.py`` and
+``tests/test_oracle_multi.py``
 (closed forms, exact hand-worked fixture, high-precision brute force,
 invariants, naive full-prefix recomputation) and by
 ``tests/test_oracle_mutants.py`` (planted mistakes must fail a pin).
@@ -317,3 +328,44 @@ def decode_attention_fp8(q, k_codes, k_exps, v_codes, v_exps, lengths, scale, **
     k32, v32 = k.astype(np.float32), v.astype(np.float32)
     assert np.array_equal(k32.astype(np.float64)[np.isfinite(k)], k[np.isfinite(k)])
     return decode_attention(np.asarray(q, dtype=np.float32), k32, v32, L, scale, F32, **kw)
+
+
+# --- several new tokens per sequence -----------------------------------------
+
+def append_multi(k_cache, v_cache, lengths, k_new, v_new):
+    """Append T_q tokens per sequence: k_new, v_new [B, Hkv, T_q, D] go to
+    slots lengths[b] .. lengths[b] + T_q - 1 in order.  A sequence they do not
+    fit is left unchanged and flagged.  Returns (k', v', lengths', appended)
+    with appended[b] = T_q or 0."""
+    k2 = np.array(k_cache, copy=True)
+    v2 = np.array(v_cache, copy=True)
+    n = np.array(lengths, dtype=np.int64, copy=True)
+    T_cap = k2.shape[2]
+    T_q = np.asarray(k_new).shape[2]
+    appended = np.zeros(n.shape, dtype=np.int32)
+    for b in range(k2.shape[0]):
+        if n[b] < 0 or n[b] + T_q > T_cap:
+            continue
+        for i in range(T_q):
+            k2[b, :, n[b] + i, :] = k_new[b, :, i]
+            v2[b, :, n[b] + i, :] = v_new[b, :, i]
+        n[b] += T_q
+        appended[b] = T_q
+    return k2, v2, n.astype(np.int32), appended
+
+
+def decode_attention_multi(q, k_cache, v_cache, lengths, appended, scale, dtype, **kw):
+    """q [B, Hq, T_q, D]; lengths after the append, appended [B] rows added.
+    Query i of sequence b attends over its first
+    lengths[b] - appended[b] + min(i + 1, appended[b]) tokens.  Returns
+    [B, Hq, T_q, D]."""
+    q = np.asarray(q)
+    B, Hq, T_q, D = q.shape
+    L = np.asarray(lengths, dtype=np.int64)
+    a = np.asarray(appended, dtype=np.int64)
+    out = np.empty((B, Hq, T_q, D), dtype=np.float64)
+    for i in range(T_q):
+        Li = (L - a + np.minimum(i + 1, a)).astype(np.int32)
+        out[:, :, i, :] = decode_attention(np.ascontiguousarray(q[:, :, i, :]), k_cache, v_cache, Li, scale,
+                                           dtype, **kw)
+    return out
