@@ -245,6 +245,27 @@ int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_ne
                                void* out, float scale, void* stream);
 
 /*
+ * A step with several new tokens per sequence, as when a large model checks
+ * n_tokens drafted tokens in one pass ("All About Transformer Inference",
+ * appendix on speculative sampling: the drafted tokens are scored together
+ * and share the KV cache load).  1 <= n_tokens <= KVD_MAX_NEW_TOKENS.
+ *   k_new, v_new: [B, Hkv, n_tokens, d]; q, out: [B, Hq, n_tokens, d].
+ * Each sequence with room for all n_tokens rows gets them at slots
+ * lengths[b] .. lengths[b] + n_tokens - 1 (in order) and lengths[b]
+ * advances by n_tokens; then query i of head h attends causally: over the
+ * cached tokens and the new tokens 0 .. i.  A sequence without room is not
+ * appended (sticky KVD_ECAPACITY) and all its queries attend over its
+ * lengths[b] cached tokens.  Same dtype rules as kvdecode_append_attend;
+ * bf16 or fp32 contiguous or paged caches (KVD_EUNSUPPORTED for fp8 caches
+ * and for KVD_VARIANT_MFMA).  n_tokens = 1 gives kvdecode_append_attend's
+ * results.
+ */
+enum { KVD_MAX_NEW_TOKENS = 16 };
+int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void* k_new,
+                                     const void* v_new, const void* q, void* out, float scale,
+                                     void* stream);
+
+/*
  * Synchronise `stream`, then report and clear the sticky device error:
  * KVD_OK, KVD_ECAPACITY, KVD_ELENGTH or KVD_EPAGE (in that order of
  * precedence when several occurred).  Returns KVD_OK without a device call if the handle has never

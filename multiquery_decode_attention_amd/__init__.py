@@ -24,7 +24,8 @@ __all__ = [
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
     "kvdecode_create_fp8",
-    "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_status",
+    "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
+    "kvdecode_status", "KVD_MAX_NEW_TOKENS",
     "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
@@ -42,8 +43,8 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libkvdecode.so")
 
 EXPORTS = (
-    "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend",
-    "kvdecode_status", "kvdecode_reserve",
+    "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_append", "kvdecode_attend",
+    "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
 )
@@ -104,6 +105,7 @@ def library():
         "kvdecode_append": (I, [P, P, P, P]),
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
+        "kvdecode_append_attend_multi": (I, [P, I, P, P, P, P, F, P]),
         "kvdecode_status": (I, [P, P]),
         "kvdecode_reserve": (I, [P]),
         "kvdecode_set_num_splits": (I, [P, I]),
@@ -238,6 +240,18 @@ def kvdecode_append_attend(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: 
            "kvdecode_append_attend")
 
 
+KVD_MAX_NEW_TOKENS = 16
+
+
+def kvdecode_append_attend_multi(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                                 out: torch.Tensor, scale: float, stream=None) -> None:
+    """Several new tokens per sequence: k_new/v_new [B, Hkv, T, d], q/out [B, Hq, T, d]."""
+    n = k_new.shape[2]
+    _check(library().kvdecode_append_attend_multi(h, n, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                                  float(scale), _stream_ptr(stream)),
+           "kvdecode_append_attend_multi")
+
+
 def kvdecode_status(h: int, stream=None) -> int:
     """Sync the stream and return (and clear) the sticky device status code."""
     return library().kvdecode_status(h, _stream_ptr(stream))
@@ -346,6 +360,24 @@ class KVCache:
             self._check_token(out, self.Hq, "out")
         kvdecode_append_attend(self.handle, k_new, v_new, q, out,
                                self.D ** -0.5 if scale is None else scale, stream)
+        return out
+
+    def step_multi(self, k_new, v_new, q, out=None, scale=None, stream=None):
+        """Append T new tokens per sequence (k_new/v_new [B, Hkv, T, d]) and
+        attend their queries (q [B, Hq, T, d]) causally, in one call."""
+        T = k_new.shape[2] if k_new.dim() == 4 else -1
+        for t, heads, name in ((k_new, self.Hkv, "k_new"), (v_new, self.Hkv, "v_new"), (q, self.Hq, "q")):
+            if t.shape != (self.B, heads, T, self.D) or t.dtype != self.dtype or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [{self.B}, {heads}, T, {self.D}] {self.dtype} "
+                                 f"tensor with the same T, got {tuple(t.shape)} {t.dtype}")
+            if t.device != self.k_cache.device:
+                raise ValueError(f"{name} is on {t.device}, the cache on {self.k_cache.device}")
+        if out is None:
+            out = torch.empty_like(q)
+        elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must match q")
+        kvdecode_append_attend_multi(self.handle, k_new, v_new, q, out,
+                                     self.D ** -0.5 if scale is None else scale, stream)
         return out
 
     def status(self, stream=None) -> int:

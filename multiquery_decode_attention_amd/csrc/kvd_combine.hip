@@ -87,8 +87,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
         float mc = m;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) mc = fmaxf(mc, w[u]);
-        // j0 < nsplit, so w[0] and with it mc are finite
-        const float r = exp2f(m - mc);
+        // a split can be empty for an early query of a several-token step
+        // (log-sum-exp -inf); all of this thread's may be
+        const float r = mc == -INFINITY ? 1.f : exp2f(m - mc);
         z *= r;
         acc.x *= r;
         acc.y *= r;
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
         acc.w *= r;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            const float wu = exp2f(w[u] - mc);
+            const float wu = w[u] == -INFINITY ? 0.f : exp2f(w[u] - mc);
             z += wu;
             acc.x = fmaf(wu, o[u].x, acc.x);
             acc.y = fmaf(wu, o[u].y, acc.y);
@@ -121,7 +122,8 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
         store4(orow, obase + 4 * v, make_float4(0.f, 0.f, 0.f, 0.f));
         return;
     }
-    // group 0 always holds split 0, so its maximum is finite
+    // group 0 holds split 0, which holds token 0 for every row: its maximum
+    // is finite
     const int base = tid - rt;  // first thread of this row
     float mt = m;
     for (int k = 1; k < G; ++k) mt = fmaxf(mt, mz[base + k * nvec + v].x);

@@ -78,6 +78,13 @@ struct PartialArgs {
                             // kernel's token tiles s, s+S, s+2S, ...
     float scale_log2e;      // scale * log2(e)
     int lds_config;         // LDS kernel: LDS_SHORT or LDS_LONG (see below)
+    // Several new tokens per sequence: T_q query rows per head (q and the
+    // partials hold Hq = heads * T_q rows, M = group heads * T_q, row
+    // r = head * T_q + i), and n_new[b] rows appended by this step (null for
+    // a one-token step).  Query i attends over the first
+    // len - n_new[b] + min(i + 1, n_new[b]) tokens.
+    int T_q;
+    const int* n_new;
 };
 
 struct CombineArgs {
@@ -130,6 +137,14 @@ __device__ __forceinline__ SeqLen sequence_length(const int32_t* lengths, int* e
     return r;
 }
 
+// Tokens query row r attends to (see PartialArgs::T_q).
+__device__ __forceinline__ int row_limit(int len, int r, int T_q, const int* n_new, int b) {
+    if (T_q == 1 || n_new == nullptr) return len;
+    const int a = n_new[b];
+    const int i = r % T_q;
+    return len - a + (i + 1 < a ? i + 1 : a);
+}
+
 __device__ __forceinline__ int splits_with_data(int len, int tile, int S) {
     const int nt = (len + tile - 1) / tile;
     return nt < S ? nt : S;
@@ -152,9 +167,13 @@ __device__ __forceinline__ BlockCoord block_coord(int units) {
 }
 
 // Each launcher returns the hipError_t of its launch.
+// Append T_q >= 1 new rows per (sequence, KV head) at slots lengths[b] ..
+// lengths[b] + T_q - 1 (k_new/v_new [B, Hkv, T_q, D]); a sequence they do
+// not fit is left unchanged and flagged.  n_new (may be null) receives the
+// rows appended per sequence.
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                         const KvLayout& kv, int32_t* lengths, int* err, int B, int Hkv, int D,
-                         int T_cap, int elem_bytes, hipStream_t stream);
+                         const KvLayout& kv, int32_t* lengths, int* err, int* n_new, int B, int Hkv,
+                         int D, int T_cap, int T_q, int elem_bytes, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
 hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);

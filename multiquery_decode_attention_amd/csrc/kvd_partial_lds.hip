@@ -91,6 +91,12 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const int hw0 = hg * 64 + wave * hpw;     // first head (within the KV group) of this wave
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;
+    // Tokens this lane's query row attends: all `len` of them, except in a
+    // step with several new tokens, where the earlier ones see fewer; tiles
+    // reaching past the smallest such limit are masked per row.
+    const int lim = row_limit(len, hg * 64 + min(wave * hpw + (head_ok ? c : max(nh - 1, 0)), mg - 1),
+                              a.T_q, a.n_new, b);
+    const int mask_from = a.T_q == 1 ? len : len - a.T_q + 1;
 
     // Rows below are counted from kb/vb: the (b, g) slab of a contiguous
     // cache, or the start of the page pool.
@@ -155,7 +161,9 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     // be in flight at once.
     u32x4_t qop[KS];
     {
-        const int hq = hw0 + (head_ok ? c : max(nh - 1, 0));
+        // (a wave with no heads reads the group's last row: every row read
+        // lies inside the group)
+        const int hq = hg * 64 + min(wave * hpw + (head_ok ? c : max(nh - 1, 0)), mg - 1);
         const uint16_t* qrow =
             static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hq) * D;
 #pragma unroll
@@ -247,10 +255,13 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     // times that tile's V from LDS, into the accumulators; 128 columns (one
     // 16-byte chunk per lane) at a time.
     auto value_product = [&](const float (&xs)[8], const unsigned char* Vl) {
+        // a row with no token yet in this split keeps m_ref = -inf; its
+        // scores are -inf too and must weigh 0, not NaN
+        const float m_sub = m_ref == -INFINITY ? 0.f : m_ref;
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(xs[j] - m_ref);
+            p[j] = __builtin_amdgcn_exp2f(xs[j] - m_sub);
             l_run += p[j];
         }
         u32x4_t pop;
@@ -328,10 +339,10 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
-            if (t0 + MFMA_TILE > t_end) {
+            if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
+                    if (t0 + slot_token(gq, j) >= lim) x[j] = -INFINITY;
             }
             float mx = x[0];
 #pragma unroll
@@ -343,7 +354,8 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                 // what was accumulated with the old one (pending tiles are
                 // converted later, with whatever reference holds then)
                 const float m_new = mx > m_ref + TAU ? mx : m_ref;
-                const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+                // (a row with no token yet keeps m_ref = m_new = -inf: factor 1)
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
                 l_run *= alpha;
                 m_ref = m_new;
 #pragma unroll
@@ -379,7 +391,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         const int r = 4 * gq + i;
         const float li = __shfl(l, r);
         if (r < nh) {
-            const float inv = 1.f / li;
+            const float inv = li > 0.f ? 1.f / li : 0.f;  // a row with no token in this split: 0
             float* orow = a.o_part + (row0 + (size_t)r * a.S) * D;
             // Non-temporal stores: the partials are read once, by the
             // combine; kept out of the caches' dirty lines they stream to
@@ -392,7 +404,8 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         }
     }
     if (gq == 0 && head_ok)
-        __builtin_nontemporal_store(m_ref + __builtin_log2f(l), a.lse_part + row0 + (size_t)c * a.S);
+        __builtin_nontemporal_store(l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY,
+                                    a.lse_part + row0 + (size_t)c * a.S);
 }
 
 template <int D, int NS, int VL>

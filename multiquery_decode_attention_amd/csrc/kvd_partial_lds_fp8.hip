@@ -108,7 +108,9 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     // load a copy of its last row.
     u32x4_t qop[KS];
     {
-        const int hq = hw0 + (head_ok ? c : max(nh - 1, 0));
+        // (a wave with no heads reads the group's last row: every row read
+        // lies inside the group)
+        const int hq = hg * 64 + min(wave * hpw + (head_ok ? c : max(nh - 1, 0)), mg - 1);
         const uint16_t* qrow =
             static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + (size_t)g * a.M + hq) * D;
 #pragma unroll
@@ -229,7 +231,8 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (wave_any(mx > m_ref + TAU)) {
             const float m_new = mx > m_ref + TAU ? mx : m_ref;
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            // (a row with no token yet keeps m_ref = m_new = -inf: factor 1)
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
             l_run *= alpha;
             m_ref = m_new;
 #pragma unroll

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     const int len = sl.len;
     const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
     if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
-    const int g = h / a.M;  // query head h reads KV head floor(h / M)
+    const int g = h / a.M;  // query row h reads KV head floor(h / M)
+    const int row_len = row_limit(len, h, a.T_q, a.n_new, b);  // tokens this row attends
 
     __shared__ float qs[D];
     const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + h) * D;
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         // the end); the value loop reads other lanes' rows by shuffle
         const int row = row_of(min(t, len - 1));
         float x = -INFINITY;
-        if (t < len) {
+        if (t < row_len) {
             // the lane's key row in 16-byte pieces, all requested before use
             const T* kr = t == slot ? knew : kb + (size_t)row * D;
             constexpr int PIECE = 16 / sizeof(T);
@@ -132,8 +133,10 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
             x = dot * a.scale_log2e;
         }
         const float m_new = fmaxf(m_run, wave_max(x));
-        const float alpha = exp2f(m_run - m_new);
-        const float p = exp2f(x - m_new);
+        // nothing seen yet in this split (only with several new tokens)
+        const bool none = m_new == -INFINITY;
+        const float alpha = none ? 1.f : exp2f(m_run - m_new);
+        const float p = none ? 0.f : exp2f(x - m_new);
         l_run = l_run * alpha + wave_sum(p);
         m_run = m_new;
 #pragma unroll
@@ -163,10 +166,10 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     }
 
     const size_t row = ((size_t)b * a.Hq + h) * a.S + s;
-    const float inv = 1.f / l_run;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) a.o_part[row * D + lane + 64 * k] = acc[k] * inv;
-    if (lane == 0) a.lse_part[row] = m_run + log2f(l_run);
+    if (lane == 0) a.lse_part[row] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
 }
 
 template <typename T, bool PAGED>

@@ -88,11 +88,12 @@ struct Shape {
     long long slots;      // workgroups resident on the whole GPU
 };
 
-Shape shape_for(const kvdecode_s* h, int variant, int lds_which) {
+Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
     const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
+    const int rows = h->M * T_q;  // query rows per KV head
     Shape sh;
     if (variant == KVD_VARIANT_LDS) {
-        sh.units = bkv * ((h->M + 63) / 64);
+        sh.units = bkv * ((rows + 63) / 64);
         sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
                                                : kvd::lds_groups_per_cu(h->d.head_dim, lds_which));
     } else if (variant == KVD_VARIANT_MFMA) {
@@ -102,17 +103,17 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which) {
         const int waves_per_cu = h->d.head_dim == 256 ? 4 : (h->d.head_dim == 128 ? 8 : 16);
         sh.slots = (long long)CUS * (waves_per_cu / nw > 0 ? waves_per_cu / nw : 1);
     } else {
-        sh.units = bkv * h->M;
+        sh.units = bkv * rows;
         sh.slots = (long long)CUS * 16;
     }
     return sh;
 }
 
 // Cost-model choice of the split count for one kernel shape.
-long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles) {
+long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles, int T_q) {
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
-    const double part_bytes = (double)h->M * (h->d.head_dim + 1) * 4 * 2;
+    const double part_bytes = (double)h->M * T_q * (h->d.head_dim + 1) * 4 * 2;
     double best = 0;
     std::vector<std::pair<long long, double>> cand;
     long long prev_per = -1;
@@ -132,7 +133,8 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
     return pick;
 }
 
-Plan make_plan(const kvdecode_s* h) {
+// T_q: query rows per head (new tokens per sequence in this step).
+Plan make_plan(const kvdecode_s* h, int T_q = 1) {
     Plan p;
     p.variant = resolve_variant(h);
     p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
@@ -148,8 +150,8 @@ Plan make_plan(const kvdecode_s* h) {
     if (p.variant == KVD_VARIANT_LDS && h->d.head_dim == 256 && !is_fp8(h)) {
         const long long s = clamp_splits(h->forced_splits > 0
                                              ? h->forced_splits
-                                             : plan_splits(h, shape_for(h, p.variant, kvd::LDS_LONG),
-                                                           p.tile, n_tiles));
+                                             : plan_splits(h, shape_for(h, p.variant, kvd::LDS_LONG, T_q),
+                                                           p.tile, n_tiles, T_q));
         if ((n_tiles + s - 1) / s >= kvd::LDS_LONG_MIN_TILES) {
             p.lds_config = kvd::LDS_LONG;
             finish(s);
@@ -160,7 +162,7 @@ Plan make_plan(const kvdecode_s* h) {
         finish(h->forced_splits);
         return p;
     }
-    finish(plan_splits(h, shape_for(h, p.variant, kvd::LDS_SHORT), p.tile, n_tiles));
+    finish(plan_splits(h, shape_for(h, p.variant, kvd::LDS_SHORT, T_q), p.tile, n_tiles, T_q));
     return p;
 }
 
@@ -173,8 +175,9 @@ int32_t ensure_device(kvdecode_s* h) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return KVD_EHIP;
     if (h->device >= 0) return dev == h->device ? KVD_OK : KVD_EINVAL;
-    // err word followed by the per-sequence attended lengths
-    const size_t words = 1 + (size_t)h->d.batch;
+    // err word, then per sequence the attended length of the last step and
+    // the rows its last append added
+    const size_t words = 1 + 2 * (size_t)h->d.batch;
     e = hipMalloc(reinterpret_cast<void**>(&h->err), words * sizeof(int));
     if (e != hipSuccess) return hip_fail(e);
     e = hipMemset(h->err, 0, words * sizeof(int));
@@ -187,7 +190,10 @@ int32_t ensure_device(kvdecode_s* h) {
     return KVD_OK;
 }
 
-int32_t ensure_workspace(kvdecode_s* h, int splits) {
+// Workspace for `splits` splits of B * Hq * T_q query rows (row_splits =
+// splits * T_q; the capacity is kept in the same unit).
+int32_t ensure_workspace(kvdecode_s* h, int row_splits) {
+    const int splits = row_splits;
     if (splits <= h->ws_splits) return KVD_OK;
     if (h->o_part) (void)hipFree(h->o_part);
     if (h->lse_part) (void)hipFree(h->lse_part);
@@ -232,7 +238,8 @@ int32_t ensure_events(kvdecode_s* h) {
     return KVD_OK;
 }
 
-int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st) {
+int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st,
+                            int T_q = 1) {
     const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
     hipError_t e =
@@ -240,8 +247,8 @@ int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new,
                                            h->d.lengths, h->err, h->d.batch, h->d.num_kv_heads,
                                            h->d.head_dim, h->d.capacity, st)
                   : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths,
-                                       h->err, h->d.batch, h->d.num_kv_heads, h->d.head_dim,
-                                       h->d.capacity, h->elem, st);
+                                       h->err, h->err + 1 + h->d.batch, h->d.batch, h->d.num_kv_heads,
+                                       h->d.head_dim, h->d.capacity, T_q, h->elem, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed) {
         if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
@@ -254,23 +261,27 @@ int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new,
 // append into its partial pass (the combine then advances lengths); the
 // other kernels launch the append kernel first.  Argument checks happen
 // before any device work.
+// T_q > 1: a step with T_q new tokens per sequence (append then causal
+// attend of their T_q queries); q and out then hold Hq * T_q rows.
 int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void* q, void* out,
-                 float scale, hipStream_t st) {
+                 float scale, hipStream_t st, int T_q = 1) {
     if (!q || !out) return KVD_EINVAL;
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
-    const Plan p = make_plan(h);
+    const Plan p = make_plan(h, T_q);
     if (is_fp8(h) ? p.variant != KVD_VARIANT_LDS : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
         return KVD_EUNSUPPORTED;
+    if (T_q > 1 && (is_fp8(h) || p.variant == KVD_VARIANT_MFMA)) return KVD_EUNSUPPORTED;
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
-    if ((rc = ensure_workspace(h, p.splits)) != KVD_OK) return rc;
+    if ((rc = ensure_workspace(h, p.splits * T_q)) != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
     const bool with_append = k_new != nullptr;
-    // the fp8 append quantizes in its own kernel, before the partial pass
-    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA && !is_fp8(h);
+    // the fp8 append quantizes in its own kernel, before the partial pass,
+    // and so does an append of several tokens
+    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA && !is_fp8(h) && T_q == 1;
     if (with_append && !fused) {
-        if ((rc = launch_append_timed(h, k_new, v_new, st)) != KVD_OK) return rc;
+        if ((rc = launch_append_timed(h, k_new, v_new, st, T_q)) != KVD_OK) return rc;
     }
 
     kvd::PartialArgs a;
@@ -285,9 +296,11 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.k_new = fused ? k_new : nullptr;
     a.v_new = fused ? v_new : nullptr;
     a.B = h->d.batch;
-    a.Hq = h->d.num_q_heads;
+    a.Hq = h->d.num_q_heads * T_q;
     a.Hkv = h->d.num_kv_heads;
-    a.M = h->M;
+    a.M = h->M * T_q;
+    a.T_q = T_q;
+    a.n_new = T_q > 1 ? h->err + 1 + h->d.batch : nullptr;
     a.D = h->d.head_dim;
     a.T_cap = h->d.capacity;
     a.S = p.splits;
@@ -448,6 +461,16 @@ int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_ne
     if (!k_new || !v_new) return KVD_EINVAL;
     if (!aligned16(k_new) || !aligned16(v_new)) return KVD_EALIGN;
     return run_step(h, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream));
+}
+
+int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void* k_new,
+                                     const void* v_new, const void* q, void* out, float scale,
+                                     void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (n_tokens < 1 || n_tokens > KVD_MAX_NEW_TOKENS) return KVD_EINVAL;
+    if (!k_new || !v_new) return KVD_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_EALIGN;
+    return run_step(h, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream), n_tokens);
 }
 
 int32_t kvdecode_status(kvdecode_t h, void* stream) {

@@ -146,6 +146,32 @@ def make_workload_case(w: Workload, device="cpu", seed: Optional[int] = None,
 
 
 @dataclasses.dataclass
+class MultiCase:
+    """A step with T_q new tokens per sequence (drafted tokens to verify)."""
+    q: torch.Tensor          # [B, Hq, T_q, D]
+    k_cache: torch.Tensor    # [B, Hkv, T_cap, D]
+    v_cache: torch.Tensor
+    lengths0: torch.Tensor   # [B] int32, before the append
+    k_new: torch.Tensor      # [B, Hkv, T_q, D]
+    v_new: torch.Tensor
+    scale: float
+
+
+def make_multi_case(B, Hq, Hkv, D, T_cap, lengths0, T_q, dtype, seed, device="cpu") -> MultiCase:
+    """Seeded case with T_q new tokens per sequence; lengths0 are the cached
+    lengths before the step (they may leave no room, to test overflow)."""
+    tdt = torch.float32 if dtype in ("f32", torch.float32) else torch.bfloat16
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    q = _normal((B, Hq, T_q, D), gen, device, tdt)
+    k_cache = _normal((B, Hkv, T_cap, D), gen, device, tdt)
+    v_cache = _normal((B, Hkv, T_cap, D), gen, device, tdt)
+    k_new = _normal((B, Hkv, T_q, D), gen, device, tdt)
+    v_new = _normal((B, Hkv, T_q, D), gen, device, tdt)
+    lengths0 = torch.as_tensor(lengths0, dtype=torch.int32).to(device)
+    return MultiCase(q, k_cache, v_cache, lengths0, k_new, v_new, float(D) ** -0.5)
+
+
+@dataclasses.dataclass
 class Fp8Case:
     """One decode step over an fp8 cache: E4M3 codes and per-row
     power-of-two exponents (value = code * 2^e); bf16 query and new rows."""

@@ -99,6 +99,10 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_append_attend(h, FAKE, FAKE, None, FAKE, 1.0, None) == kvd.KVD_EINVAL
     assert lib.kvdecode_append_attend(h, FAKE, FAKE, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
     assert lib.kvdecode_append_attend(h, FAKE, FAKE, FAKE, FAKE, float("nan"), None) == kvd.KVD_EINVAL
+    for n in (0, -1, kvd.KVD_MAX_NEW_TOKENS + 1):
+        assert lib.kvdecode_append_attend_multi(h, n, FAKE, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append_attend_multi(h, 2, FAKE + 8, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EALIGN
+    assert lib.kvdecode_append_attend_multi(h, 2, FAKE, FAKE, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
     assert lib.kvdecode_append(h, None, FAKE, None) == kvd.KVD_EINVAL
     assert lib.kvdecode_append(h, FAKE, FAKE + 8, None) == kvd.KVD_EALIGN
     # knobs
