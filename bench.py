@@ -56,9 +56,10 @@ def kernel_source_sha(variant: str = "lds") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_key(workload: str, page_size: int = 0, kv_dtype: str = "") -> str:
+def traffic_key(workload: str, page_size: int = 0, kv_dtype: str = "", new_tokens: int = 1) -> str:
     """Name of a workload's traffic record (and profile summaries)."""
-    return workload + (f"_paged{page_size}" if page_size else "") + (f"_{kv_dtype}" if kv_dtype else "")
+    return (workload + (f"_paged{page_size}" if page_size else "") + (f"_{kv_dtype}" if kv_dtype else "")
+            + (f"_tq{new_tokens}" if new_tokens > 1 else ""))
 
 
 def measured_traffic(key: str, variant: str):
@@ -90,6 +91,9 @@ def main():
     ap.add_argument("--kv-dtype", default="", choices=["", "fp8"],
                     help="fp8: the cache as E4M3 codes with per-row power-of-two scales "
                          "(bf16 queries and outputs); default: the workload's own dtype")
+    ap.add_argument("--new-tokens", type=int, default=1,
+                    help="tokens appended and attended per sequence per step (>1: a speculative-"
+                         "verify step through kvdecode_append_attend_multi)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (counter calibration)")
@@ -116,6 +120,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fp8 = args.kv_dtype == "fp8"
+    tq = args.new_tokens
+    if tq < 1 or tq > kvd.KVD_MAX_NEW_TOKENS or (tq > 1 and fp8):
+        print(f"--new-tokens must be 1..{kvd.KVD_MAX_NEW_TOKENS} (1 with --kv-dtype fp8)", file=sys.stderr)
+        sys.exit(2)
     if fp8 and (args.page_size or w.dtype != "bf16"):
         print("--kv-dtype fp8 takes a bf16 workload and a contiguous cache", file=sys.stderr)
         sys.exit(2)
@@ -129,7 +137,7 @@ def main():
     # workload's own, and attended lengths stay within appends_per_copy of it.
     T_cap = w.T_cap
     final = inputs.attended_lengths(w)
-    attended = (final - (appends_per_copy - 1)).clamp(min=1)  # after the first append
+    attended = (final - tq * (appends_per_copy - 1)).clamp(min=tq)  # after the first append
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T={w.T} dtype={w.dtype}; "
         f"{R} cache copies of {kv_bytes_one / 1e6:.0f} MB, capacity {T_cap}")
 
@@ -143,6 +151,9 @@ def main():
                                         device=dev)
             cache = kvd.KVCache(case.k_codes, case.v_codes, case.lengths0, w.Hq, k_exp=case.k_exp,
                                 v_exp=case.v_exp)
+        elif tq > 1:
+            case = inputs.make_multi_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended - tq, tq, w.dtype,
+                                          seed=w.seed + 1000 * r, device=dev)
         else:
             case = inputs.make_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, w.dtype,
                                     seed=w.seed + 1000 * r, device=dev, k_scale=w.k_scale)
@@ -176,7 +187,11 @@ def main():
                      c["out"].data_ptr(), float(cs.scale), stream)
 
     def step(i):
-        rc = lib.kvdecode_append_attend(*copies[i % R]["args"])  # append, then attend
+        if tq > 1:  # append tq drafted tokens, then attend their queries causally
+            a = copies[i % R]["args"]
+            rc = lib.kvdecode_append_attend_multi(a[0], tq, *a[1:])
+        else:
+            rc = lib.kvdecode_append_attend(*copies[i % R]["args"])  # append, then attend
         if rc:
             raise kvd.KvdError(rc, "decode step")
 
@@ -193,13 +208,20 @@ def main():
     # computed here so that the timed loop only issues the steps.
     lens = [list(c["len"]) for c in copies]
     for i in range(W):
-        lens[i % R] = [n + 1 for n in lens[i % R]]
+        lens[i % R] = [n + tq for n in lens[i % R]]
     step_bytes = 0
     partial_bytes = 0
     flops = 0
     for i in range(W, W + K):
-        L = lens[i % R] = [n + 1 for n in lens[i % R]]
-        if fp8:
+        L = lens[i % R] = [n + tq for n in lens[i % R]]
+        if tq > 1:
+            # the cache is read once for all tq queries; q, out and the
+            # appended rows scale with tq
+            kv = traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, L)
+            step_bytes += kv + 2 * w.B * w.Hq * tq * w.D * w.elem_bytes + \
+                traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes) * tq
+            partial_bytes += kv + w.B * w.Hq * tq * w.D * w.elem_bytes
+        elif fp8:
             step_bytes += traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L) + \
                 traffic.append_bytes_fp8(w.B, w.Hkv, w.D)
             partial_bytes += traffic.partial_pass_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L)
@@ -207,7 +229,7 @@ def main():
             step_bytes += traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L) + \
                 traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
             partial_bytes += traffic.partial_pass_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L)
-        flops += traffic.attend_flops(w.Hq, w.D, L)
+        flops += traffic.attend_flops(w.Hq * tq, w.D, L)
     for c, L in zip(copies, lens):
         c["len"] = L  # the lengths each copy holds once the timed steps have run
 
@@ -237,7 +259,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, copies[0], T_cap, fp8)
+        cpu = cpu_baseline(w, copies[0], T_cap, fp8, tq)
 
     kvariant = plan["variant"] + ("_fp8" if fp8 else "")
     result = {
@@ -255,18 +277,19 @@ def main():
         "data": ("synthetic (seeded random E4M3 cache codes and exponents, N(0,1) bf16 queries and new rows)"
                  if fp8 else "synthetic (seeded N(0,1) caches and queries)"),
         "pct_of_peak": round(value / traffic.MI355X_HBM_PEAK_GBPS, 4),
-        "tokens_per_s": round(w.B * K / elapsed, 1),
+        "tokens_per_s": round(w.B * tq * K / elapsed, 1),
         "kernel_us": {"partial": round(partial_ms * 1e3, 2), "combine": round(tc / K * 1e3, 2),
                       "append": round(ta / K * 1e3, 2)},
         "attend_tflops": round(flops / K / ((tp + tc) / K * 1e-3) / 1e12, 2),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "T": w.T, "cache_dtype": "fp8_e4m3" if fp8 else w.dtype, "num_splits": plan["num_splits"],
                    "split_tokens": plan["split_tokens"], "variant": plan["variant"],
-                   "cache_copies": R, "seed": w.seed, "page_size": args.page_size or None},
+                   "cache_copies": R, "seed": w.seed, "page_size": args.page_size or None,
+                   "new_tokens": tq},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
                      "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype), kvariant),
+                     "traffic": measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype, tq), kvariant),
                      "kernel": f"partial_{kvariant}_kernel"},
         "cpu_baseline": cpu,
     }
@@ -293,7 +316,7 @@ def calibrate_copy(mib: int, reps: int):
                       "copy_GBps_read_plus_write": round(2 * n / sec / 1e9, 1)}), flush=True)
 
 
-def cpu_baseline(w, copy, T_cap, fp8=False):
+def cpu_baseline(w, copy, T_cap, fp8=False, tq=1):
     """The fp64 oracle (test infrastructure) on one full step of the same
     workload: the first copy's cache as it now stands, attended once."""
     import numpy as np
@@ -317,14 +340,17 @@ def cpu_baseline(w, copy, T_cap, fp8=False):
         q = inputs.host_array(case.q)
         dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
         t0 = time.perf_counter()
-        oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
+        if tq > 1:
+            oracle.decode_attention_multi(q, k, v, L, np.full(w.B, tq), case.scale, dt, threads=threads)
+        else:
+            oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
         sec = time.perf_counter() - t0
-        b = traffic.attend_bytes(w.B, w.Hq, w.Hkv, w.D, w.elem_bytes, L.tolist())
+        b = traffic.attend_bytes(w.B, w.Hq * tq, w.Hkv, w.D, w.elem_bytes, L.tolist())
     log(f"cpu baseline: {sec:.2f} s for one step")
     return {"value": round(b / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"one full attend step of {w.name} (B={w.B}, all {w.Hq} heads, "
                       f"{int(L.sum())} cached tokens), fp64, {sec:.2f} s",
-            "tokens_per_s": round(w.B / sec, 2)}
+            "tokens_per_s": round(w.B * tq / sec, 2)}
 
 
 if __name__ == "__main__":
