@@ -283,6 +283,24 @@ int32_t kvdecode_status(kvdecode_t h, void* stream);
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n);
 
 /*
+ * Asynchronous softmax with a unified maximum (FlashDecoding++, "Asynchronous
+ * softmax with unified max value", as summarised on the blog-aggregator
+ * page): with enable != 0 every partial softmax of the LDS kernels starts
+ * from the same reference phi -- a bound on the attention logits
+ * scale * q.k chosen by the caller -- instead of its own first scores, and
+ * keeps it unless a score exceeds phi by more than 64 / log2(e) (the
+ * overflow fallback: that wave's reference is raised and its partial sums
+ * rescaled); a split whose first scores all lie more than that below phi
+ * starts from its own maximum instead (the underflow fallback).  Results
+ * are those of the default mode up to rounding for any finite phi; a good
+ * phi removes every rescale.  enable = 0 restores the default (each split's
+ * reference starts at its first scores, raised past a 2^8 headroom).  The
+ * VALU and MFMA kernels keep exact running maxima and ignore the setting.
+ * KVD_EINVAL for a non-finite phi.
+ */
+int32_t kvdecode_set_unified_max(kvdecode_t h, int32_t enable, float phi);
+
+/*
  * Choose the partial-pass kernel: KVD_VARIANT_AUTO (LDS for bf16, VALU for
  * fp32), KVD_VARIANT_VALU (any dtype), KVD_VARIANT_MFMA or KVD_VARIANT_LDS
  * (bf16 only; KVD_EUNSUPPORTED for fp32).

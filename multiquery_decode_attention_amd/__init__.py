@@ -27,7 +27,7 @@ __all__ = [
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
     "kvdecode_status", "KVD_MAX_NEW_TOKENS",
     "kvdecode_reserve", "kvdecode_set_num_splits",
-    "kvdecode_set_variant", "kvdecode_get_plan", "kvdecode_timing_enable",
+    "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
     "LIB_PATH",
 ]
@@ -45,7 +45,7 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
 EXPORTS = (
     "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_append", "kvdecode_attend",
     "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_status", "kvdecode_reserve",
-    "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_get_plan",
+    "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
 )
 
@@ -110,6 +110,7 @@ def library():
         "kvdecode_reserve": (I, [P]),
         "kvdecode_set_num_splits": (I, [P, I]),
         "kvdecode_set_variant": (I, [P, I]),
+        "kvdecode_set_unified_max": (I, [P, I, F]),
         "kvdecode_get_plan": (I, [P, IP, IP, IP]),
         "kvdecode_timing_enable": (I, [P, I]),
         "kvdecode_timing_read": (I, [P, D, D, D, IP, IP]),
@@ -265,6 +266,12 @@ def kvdecode_set_num_splits(h: int, n: int) -> None:
     _check(library().kvdecode_set_num_splits(h, n), "kvdecode_set_num_splits")
 
 
+def kvdecode_set_unified_max(h: int, phi) -> None:
+    """Unified softmax maximum phi (a bound on scale*q.k), or None to turn it off."""
+    _check(library().kvdecode_set_unified_max(h, 0 if phi is None else 1, 0.0 if phi is None else float(phi)),
+           "kvdecode_set_unified_max")
+
+
 def kvdecode_set_variant(h: int, variant: int) -> None:
     _check(library().kvdecode_set_variant(h, variant), "kvdecode_set_variant")
 
@@ -389,6 +396,9 @@ class KVCache:
 
     def set_num_splits(self, n: int):
         kvdecode_set_num_splits(self.handle, n)
+
+    def set_unified_max(self, phi):
+        kvdecode_set_unified_max(self.handle, phi)
 
     def set_variant(self, variant: int):
         kvdecode_set_variant(self.handle, variant)

@@ -85,6 +85,11 @@ struct PartialArgs {
     // len - n_new[b] + min(i + 1, n_new[b]) tokens.
     int T_q;
     const int* n_new;
+    // Softmax reference of the LDS kernels (base 2): the starting reference
+    // (-inf, or a unified maximum given by the caller) and the headroom past
+    // which it is raised (8; 64 with a unified maximum).
+    float m_init;
+    float tau;
 };
 
 struct CombineArgs {

@@ -36,6 +36,16 @@
 // head of the wave exceeds m + 8 are m, l and that wave's accumulators
 // rescaled, which after the first tiles almost never happens.
 //
+// Unified maximum (kvdecode_set_unified_max): every split starts from the
+// caller's bound phi instead of its own first scores and keeps it unless a
+// score exceeds it by more than 2^64 -- weights and sums stay far inside
+// fp32 -- so with a good bound no split ever rescales; a bound far above
+// every score of a split's first tile is replaced by that tile's maximum
+// (nothing has been accumulated yet), so small weights never underflow.
+// FlashDecoding++'s asynchronous softmax with a unified maximum ("FlashDecoding++"
+// blog summary) is the idea; the splits' log-sum-exps stay exact, so the
+// combine is unchanged.
+//
 // Sources: as for the register kernel -- the grouped contraction and the
 // cross-shard Flash-style accumulation ("All About Transformer Inference",
 // section "Sharding the KV cache"); multiquery K/V shared by all query heads
@@ -60,7 +70,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     constexpr int REGION = MFMA_TILE * D * 2;        // bytes of K (or V) per stage
     constexpr int STAGE = 2 * REGION;
     constexpr int PERW = STAGE / (4 * 64 * 16);      // loads per wave per stage (= D/32)
-    constexpr float TAU = 8.f;                       // rescale threshold (base-2 exponent)
+    const float TAU = a.tau;                         // reference headroom (base-2 exponent)
     static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
     static_assert(2 * MFMA_TILE * CH == 4 * PERW * 64 && MFMA_TILE * CH == 2 * PERW * 64,
                   "waves 0-1 load K, waves 2-3 load V");
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     f32x4_t acc[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY, l_run = 0.f;
+    float m_ref = a.m_init, l_run = 0.f;  // -inf, or the unified maximum
 
     // Probabilities of one tile's scores against the current reference,
     // times that tile's V from LDS, into the accumulators; 128 columns (one
@@ -349,13 +359,18 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
             for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            if (wave_any(mx > m_ref + TAU)) {
+            // raise the reference past the headroom; on the first tile also drop a
+            // unified maximum that lies far above every score
+            const bool low = it == 0 && mx < m_ref - TAU;
+            if (wave_any(mx > m_ref + TAU || low)) {
                 // raise the reference of the heads that outgrew it and rescale
                 // what was accumulated with the old one (pending tiles are
                 // converted later, with whatever reference holds then)
-                const float m_new = mx > m_ref + TAU ? mx : m_ref;
-                // (a row with no token yet keeps m_ref = m_new = -inf: factor 1)
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+                const float m_new = mx > m_ref + TAU || low ? mx : m_ref;
+                // (nothing is accumulated before the first tile's value
+                // product, and a row with no token yet keeps m_ref = m_new =
+                // -inf: factor 1 in both cases)
+                const float alpha = it == 0 || m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
                 l_run *= alpha;
                 m_ref = m_new;
 #pragma unroll

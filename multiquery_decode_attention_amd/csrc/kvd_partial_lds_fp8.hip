@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     constexpr int STAGE = 2 * REGION + EXPS;
     constexpr int PERWD = 2 * REGION / (4 * 64 * 16);  // code loads per wave per stage (D/64)
     constexpr int PERW = PERWD + 1;                     // + the exponent load
-    constexpr float TAU = 8.f;
+    const float TAU = a.tau;  // reference headroom (base-2 exponent)
     static_assert(PERWD >= 1 && REGION == 2 * PERWD * 64 * 16, "waves 0-1 load K, waves 2-3 load V");
     static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
     __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     f32x4_t acc[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) acc[e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY, l_run = 0.f;
+    float m_ref = a.m_init, l_run = 0.f;  // -inf, or the unified maximum
 
 #pragma unroll
     for (int i = 0; i < NS - 1; ++i) issue(i);
@@ -229,10 +229,14 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (wave_any(mx > m_ref + TAU)) {
-            const float m_new = mx > m_ref + TAU ? mx : m_ref;
+        // raise the reference past the headroom; on the first tile also drop a
+        // unified maximum that lies far above every score
+        const bool low = it == 0 && mx < m_ref - TAU;
+        if (wave_any(mx > m_ref + TAU || low)) {
+            const float m_new = mx > m_ref + TAU || low ? mx : m_ref;
             // (a row with no token yet keeps m_ref = m_new = -inf: factor 1)
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+            // (nothing is accumulated before the first tile: factor 1)
+            const float alpha = it == 0 || m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
             l_run *= alpha;
             m_ref = m_new;
 #pragma unroll

@@ -23,6 +23,8 @@ struct kvdecode_s {
     int elem = 4;
     int variant_req = KVD_VARIANT_AUTO;
     int forced_splits = 0;
+    bool unified = false;     // unified softmax maximum (LDS kernels)
+    float unified_max = 0.f;  // in units of scale * q.k
 
     // Device resources (allocated on first use, on the then-current device).
     int device = -1;
@@ -309,6 +311,8 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.kv = h->kv;
     a.k_exp = h->k_exp;
     a.v_exp = h->v_exp;
+    a.m_init = h->unified ? h->unified_max * kvd::LOG2E : -INFINITY;
+    a.tau = h->unified ? 64.f : 8.f;
 
     kvd::CombineArgs c;
     c.o_part = h->o_part;
@@ -499,6 +503,14 @@ int32_t kvdecode_reserve(kvdecode_t h) {
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_workspace(h, make_plan(h).splits)) != KVD_OK) return rc;
     return ensure_events(h);
+}
+
+int32_t kvdecode_set_unified_max(kvdecode_t h, int32_t enable, float phi) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (enable && !isfinite(phi)) return KVD_EINVAL;
+    h->unified = enable != 0;
+    h->unified_max = enable ? phi : 0.f;
+    return KVD_OK;
 }
 
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {

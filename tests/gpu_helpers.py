@@ -27,7 +27,7 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def gpu_step(case: inputs.Case, Hq: int, *, variant=None, splits=None, append=True,
-             lengths=None, k_cache=None, v_cache=None, fused=False, reserve=False):
+             lengths=None, k_cache=None, v_cache=None, fused=False, reserve=False, unified_max=None):
     """Append (optional) then attend on the GPU, on fresh device copies of
     the case's tensors (the case itself is never modified).  Returns (out,
     k_cache, v_cache, lengths, status, plan)."""
@@ -41,6 +41,8 @@ def gpu_step(case: inputs.Case, Hq: int, *, variant=None, splits=None, append=Tr
             cache.set_variant(variant)
         if splits is not None:
             cache.set_num_splits(splits)
+        if unified_max is not None:
+            cache.set_unified_max(unified_max)
         if reserve:  # twice: binding and allocation happen once
             cache.reserve()
             cache.reserve()

@@ -109,6 +109,10 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_set_num_splits(h, -1) == kvd.KVD_EINVAL
     assert lib.kvdecode_set_variant(h, 9) == kvd.KVD_EUNSUPPORTED
     assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_VALU) == kvd.KVD_OK
+    assert lib.kvdecode_set_unified_max(h, 1, float("inf")) == kvd.KVD_EINVAL
+    assert lib.kvdecode_set_unified_max(h, 1, float("nan")) == kvd.KVD_EINVAL
+    assert lib.kvdecode_set_unified_max(h, 1, 3.5) == kvd.KVD_OK
+    assert lib.kvdecode_set_unified_max(h, 0, float("nan")) == kvd.KVD_OK  # off: phi unused
     assert lib.kvdecode_timing_enable(h, -1) == kvd.KVD_EINVAL
     assert lib.kvdecode_timing_enable(h, 4) == kvd.KVD_OK
     assert lib.kvdecode_timing_enable(h, 0) == kvd.KVD_OK

@@ -20,7 +20,7 @@ from gpu_helpers import say, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None):
+def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None, unified_max=None):
     dev = torch.device("cuda")
     kc, vc = case.k_codes.to(dev, copy=True), case.v_codes.to(dev, copy=True)
     ke, ve = case.k_exp.to(dev, copy=True), case.v_exp.to(dev, copy=True)
@@ -29,6 +29,8 @@ def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None):
     try:
         if splits is not None:
             cache.set_num_splits(splits)
+        if unified_max is not None:
+            cache.set_unified_max(unified_max)
         plan = cache.plan()
         kn, vn, q = (t.to(dev).contiguous() for t in (case.k_new, case.v_new, case.q))
         if fused:
@@ -118,3 +120,10 @@ def test_fp8_capacity_overflow():
     ref, kc2, ke2, vc2, ve2, L2 = oracle_fp8_step(case, lengths=L0)
     assert np.array_equal(kc.cpu().numpy(), kc2) and np.array_equal(ke.cpu().numpy(), ke2)
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("phi", [0.0, -40.0, 1e4])
+def test_fp8_unified_max(phi):
+    B, Hq, Hkv, D, T, L = SHAPES["palm_like"]
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=99)
+    check_fp8(case, Hq, f"fp8 unified max {phi}", unified_max=phi)

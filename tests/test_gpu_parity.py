@@ -256,3 +256,17 @@ def test_cached_decode_equals_naive_recompute(dtype):
     tol = TOL_F32 if dtype == "f32" else TOL_BF16
     assert rel_err_rows(got, full.numpy()) <= tol
     assert L.item() == T
+
+
+@pytest.mark.parametrize("phi", [None, 0.0, 6.0, -40.0, 200.0, 1e4])
+@pytest.mark.parametrize("name,B", [("palm_mqa_bf16", 2), ("ragged_gqa_bf16", 4), ("longctx_mqa_bf16", 1)])
+def test_unified_max_any_bound_same_result(name, B, phi):
+    """Asynchronous softmax with a unified maximum: a bound near the logits,
+    far below them (every split raises it), far above them (every split
+    starts from its own maximum) -- the oracle's result every time, through
+    the long-split and short-split LDS configurations."""
+    w = inputs.WORKLOADS[name]
+    case = inputs.make_workload_case(w, device="cpu", B=B)
+    if name == "longctx_mqa_bf16":
+        case = inputs.make_case(1, w.Hq, w.Hkv, w.D, 16384, [16384], "bf16", seed=w.seed)
+    check_case(case, w.Hq, f"{name} unified max {phi}", fused=True, unified_max=phi)
