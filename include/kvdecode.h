@@ -316,15 +316,21 @@ int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
                           int32_t* split_tokens);
 
 /*
- * Kernel timing with HIP events recorded on the call's stream around the
- * partial and combine launches of each attend (and the append kernel).
- * kvdecode_timing_enable(h, n) allocates n event slots (n = 0 disables and
- * frees them); at most n attends are timed before the slots are full.
+ * Kernel timing with HIP events recorded on the call's stream.  `what` picks
+ * the brackets: KVD_TIME_PARTIAL around the partial-pass launch of each
+ * attend, KVD_TIME_COMBINE around its combine launch, KVD_TIME_APPEND around
+ * a separate append kernel.  Every recorded event costs the stream about
+ * 2 us, so ask only for what is read.
+ * kvdecode_timing_enable(h, n, what) allocates n event slots (n = 0 or
+ * what = 0 disables and frees them); at most n attends (and n appends) are
+ * timed before the slots are full.  KVD_EINVAL for n < 0 or unknown bits.
  * kvdecode_timing_read synchronises the recorded events, returns the summed
- * durations in milliseconds and the number of timed attends and appends,
- * and resets the slots.  Any output pointer may be NULL.
+ * durations in milliseconds (0 for a bracket not asked for) and the number
+ * of timed attends and appends, and resets the slots.  Any output pointer
+ * may be NULL.
  */
-int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls);
+enum { KVD_TIME_PARTIAL = 1, KVD_TIME_COMBINE = 2, KVD_TIME_APPEND = 4, KVD_TIME_ALL = 7 };
+int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls, int32_t what);
 int32_t kvdecode_timing_read(kvdecode_t h, double* partial_ms, double* combine_ms,
                              double* append_ms, int32_t* n_attend, int32_t* n_append);
 

@@ -25,7 +25,8 @@ __all__ = [
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
     "kvdecode_create_fp8",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
-    "kvdecode_status", "KVD_MAX_NEW_TOKENS",
+    "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
+    "KVD_TIME_APPEND", "KVD_TIME_ALL",
     "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan", "kvdecode_timing_enable",
     "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
@@ -36,6 +37,7 @@ KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
 KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE = -4, -5, -6, -7, -8
 KVD_F32, KVD_BF16, KVD_FP8_E4M3 = 0, 1, 2
 KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS = 0, 1, 2, 3
+KVD_TIME_PARTIAL, KVD_TIME_COMBINE, KVD_TIME_APPEND, KVD_TIME_ALL = 1, 2, 4, 7
 
 # KVD_LIBRARY may name another build of the same library (e.g. one compiled
 # with different tuning constants); by default the in-tree build is used.
@@ -112,7 +114,7 @@ def library():
         "kvdecode_set_variant": (I, [P, I]),
         "kvdecode_set_unified_max": (I, [P, I, F]),
         "kvdecode_get_plan": (I, [P, IP, IP, IP]),
-        "kvdecode_timing_enable": (I, [P, I]),
+        "kvdecode_timing_enable": (I, [P, I, I]),
         "kvdecode_timing_read": (I, [P, D, D, D, IP, IP]),
         "kvdecode_destroy": (I, [P]),
         "kvdecode_strerror": (ctypes.c_char_p, [I]),
@@ -284,8 +286,12 @@ def kvdecode_get_plan(h: int) -> dict:
             "num_splits": s.value, "split_tokens": c.value}
 
 
-def kvdecode_timing_enable(h: int, max_calls: int) -> None:
-    _check(library().kvdecode_timing_enable(h, max_calls), "kvdecode_timing_enable")
+def kvdecode_timing_enable(h: int, max_calls: int, what: int = None) -> None:
+    """Time up to max_calls attends (and appends) with HIP events; `what` is
+    a mask of KVD_TIME_PARTIAL / KVD_TIME_COMBINE / KVD_TIME_APPEND
+    (default all three)."""
+    what = KVD_TIME_ALL if what is None else what
+    _check(library().kvdecode_timing_enable(h, max_calls, what), "kvdecode_timing_enable")
 
 
 def kvdecode_timing_read(h: int) -> dict:

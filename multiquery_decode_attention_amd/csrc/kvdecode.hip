@@ -35,6 +35,7 @@ struct kvdecode_s {
 
     // Event timing.
     int timing_cap = 0;
+    int timing_what = 0;                // KVD_TIME_* bits
     std::vector<hipEvent_t> ev_attend;  // 3 per timed attend
     std::vector<hipEvent_t> ev_append;  // 2 per timed append
     int n_attend = 0, n_append = 0;
@@ -242,7 +243,7 @@ int32_t ensure_events(kvdecode_s* h) {
 
 int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st,
                             int T_q = 1) {
-    const bool timed = h->timing_cap > 0 && h->n_append < h->timing_cap;
+    const bool timed = (h->timing_what & KVD_TIME_APPEND) && h->timing_cap > 0 && h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
     hipError_t e =
         is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp,
@@ -327,9 +328,15 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     c.T_cap = a.T_cap;
     c.tile = p.tile;
     c.S = p.splits;
-    const bool timed = h->timing_cap > 0 && h->n_attend < h->timing_cap;
+    // Each recorded event is one more command-processor round trip on the
+    // stream (about 2 us), so only the brackets asked for are recorded:
+    // ev[0] before the partial pass, ev[1] between the two launches, ev[2]
+    // after the combine.
+    const int what = h->timing_what;
+    const bool timed = (what & (KVD_TIME_PARTIAL | KVD_TIME_COMBINE)) && h->timing_cap > 0 &&
+                       h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
-    if (timed && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
+    if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
     hipError_t e = is_fp8(h)                       ? kvd::launch_partial_lds_fp8(a, st)
                    : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
@@ -339,7 +346,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     e = kvd::launch_combine(c, h->d.dtype != KVD_F32, st);  // fp8 caches give bf16 outputs
     if (e != hipSuccess) return KVD_EHIP;
     if (timed) {
-        if (hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
+        if ((what & KVD_TIME_COMBINE) && hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
         ++h->n_attend;
     }
     return KVD_OK;
@@ -541,10 +548,11 @@ int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits, i
     return KVD_OK;
 }
 
-int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls) {
-    if (!is_live(h) || max_calls < 0) return KVD_EINVAL;
+int32_t kvdecode_timing_enable(kvdecode_t h, int32_t max_calls, int32_t what) {
+    if (!is_live(h) || max_calls < 0 || (what & ~KVD_TIME_ALL) != 0) return KVD_EINVAL;
     free_events(h);
-    h->timing_cap = max_calls;
+    h->timing_what = what;
+    h->timing_cap = what ? max_calls : 0;
     if (h->device >= 0) return ensure_events(h);
     return KVD_OK;
 }
@@ -553,12 +561,13 @@ int32_t kvdecode_timing_read(kvdecode_t h, double* partial_ms, double* combine_m
                              int32_t* n_attend, int32_t* n_append) {
     if (!is_live(h)) return KVD_EINVAL;
     double tp = 0, tc = 0, ta = 0;
+    const int what = h->timing_what;
     for (int i = 0; i < h->n_attend; ++i) {
+        hipEvent_t* ev = &h->ev_attend[3 * i];
         float a = 0, b = 0;
-        if (hipEventSynchronize(h->ev_attend[3 * i + 2]) != hipSuccess) return KVD_EHIP;
-        if (hipEventElapsedTime(&a, h->ev_attend[3 * i], h->ev_attend[3 * i + 1]) != hipSuccess ||
-            hipEventElapsedTime(&b, h->ev_attend[3 * i + 1], h->ev_attend[3 * i + 2]) != hipSuccess)
-            return KVD_EHIP;
+        if (hipEventSynchronize(ev[(what & KVD_TIME_COMBINE) ? 2 : 1]) != hipSuccess) return KVD_EHIP;
+        if ((what & KVD_TIME_PARTIAL) && hipEventElapsedTime(&a, ev[0], ev[1]) != hipSuccess) return KVD_EHIP;
+        if ((what & KVD_TIME_COMBINE) && hipEventElapsedTime(&b, ev[1], ev[2]) != hipSuccess) return KVD_EHIP;
         tp += a;
         tc += b;
     }

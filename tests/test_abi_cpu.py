@@ -113,9 +113,11 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_set_unified_max(h, 1, float("nan")) == kvd.KVD_EINVAL
     assert lib.kvdecode_set_unified_max(h, 1, 3.5) == kvd.KVD_OK
     assert lib.kvdecode_set_unified_max(h, 0, float("nan")) == kvd.KVD_OK  # off: phi unused
-    assert lib.kvdecode_timing_enable(h, -1) == kvd.KVD_EINVAL
-    assert lib.kvdecode_timing_enable(h, 4) == kvd.KVD_OK
-    assert lib.kvdecode_timing_enable(h, 0) == kvd.KVD_OK
+    assert lib.kvdecode_timing_enable(h, -1, kvd.KVD_TIME_ALL) == kvd.KVD_EINVAL
+    assert lib.kvdecode_timing_enable(h, 4, 8) == kvd.KVD_EINVAL
+    assert lib.kvdecode_timing_enable(h, 4, kvd.KVD_TIME_ALL) == kvd.KVD_OK
+    assert lib.kvdecode_timing_enable(h, 4, kvd.KVD_TIME_PARTIAL) == kvd.KVD_OK
+    assert lib.kvdecode_timing_enable(h, 0, kvd.KVD_TIME_ALL) == kvd.KVD_OK
     assert lib.kvdecode_destroy(h) == kvd.KVD_OK
     # a destroyed handle is unknown to every call
     assert lib.kvdecode_destroy(h) == kvd.KVD_EINVAL

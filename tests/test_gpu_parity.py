@@ -270,3 +270,38 @@ def test_unified_max_any_bound_same_result(name, B, phi):
     if name == "longctx_mqa_bf16":
         case = inputs.make_case(1, w.Hq, w.Hkv, w.D, 16384, [16384], "bf16", seed=w.seed)
     check_case(case, w.Hq, f"{name} unified max {phi}", fused=True, unified_max=phi)
+
+
+@pytest.mark.parametrize("what", ["all", "partial"])
+def test_timing_brackets(what):
+    """Event timing records only the brackets asked for and leaves results
+    unchanged: timed steps equal untimed ones bit for bit."""
+    case = inputs.make_case(2, 16, 2, 128, 300, [100, 250], "bf16", seed=41)
+    dev = torch.device("cuda")
+    mask = kvd.KVD_TIME_ALL if what == "all" else kvd.KVD_TIME_PARTIAL
+    outs, timings = [], []
+    for timed in (False, True):
+        kc, vc = case.k_cache.to(dev, copy=True), case.v_cache.to(dev, copy=True)
+        L = case.lengths0.to(dev, torch.int32, copy=True)
+        cache = kvd.KVCache(kc, vc, L, 16)
+        try:
+            if timed:
+                kvd.kvdecode_timing_enable(cache.handle, 3, mask)
+            kn, vn, q = (t.to(dev) for t in (case.k_new, case.v_new, case.q))
+            outs.append(cache.step(kn, vn, q, scale=case.scale))
+            cache.append(kn, vn)  # separate append, then attend
+            outs.append(cache.attend(q, scale=case.scale))
+            torch.cuda.synchronize()
+            if timed:
+                timings.append(kvd.kvdecode_timing_read(cache.handle))
+        finally:
+            cache.close()
+    say(f"timing {what}: {timings}")
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+    assert torch.equal(outs[1].view(torch.int16), outs[3].view(torch.int16))
+    t = timings[0]
+    assert t["n_attend"] == 2 and t["partial_ms"] > 0
+    if what == "all":
+        assert t["combine_ms"] > 0 and t["append_ms"] > 0 and t["n_append"] == 1
+    else:
+        assert t["combine_ms"] == 0 and t["append_ms"] == 0 and t["n_append"] == 0
