@@ -30,24 +30,36 @@ __device__ inline void store4(uint16_t* out, size_t i, float4 v) {
 // Workgroups of 256 threads; a (sequence, head) row takes D/4 * G of them
 // (G a power of two), so a workgroup merges 256 / (D/4 * G) rows.  Within
 // its row, thread t owns column vector v = t % (D/4) (four columns) and
-// split group k = t / (D/4), which takes splits k, k+G, k+2G, ...: all of
-// its partial vectors and their log-sum-exps are requested at once, up to
-// UNROLL of them, so one memory round trip covers the row whenever
-// splits <= UNROLL * G.  Each thread merges its splits against its own
-// maximum; the G groups then meet in LDS, rescaled to the row's maximum:
+// split group k = t / (D/4), which takes splits k, k+G, k+2G, ...: U of its
+// partial vectors and their log-sum-exps are requested at once (U * G >= S
+// whenever a row fits a workgroup), so one memory round trip covers the row.
+// The requests depend on nothing loaded: indices are clamped to the
+// workspace's splits, and which of them hold data this launch (those below
+// splits_with_data of the attended length) is decided only when the values
+// are used, by selects -- a conditional load would make the compiler wait
+// for each load before the next.  Each thread merges its splits against its
+// own maximum; the G groups then meet in LDS, rescaled to the row's maximum:
 //     out = sum_k 2^(m_k - m) A_k / sum_k 2^(m_k - m) Z_k,
 // with A_k = sum_j 2^(L_j - m_k) O_j and Z_k = sum_j 2^(L_j - m_k) over the
 // splits j of group k.  Partials are read exactly once: non-temporal loads.
 constexpr int THREADS = 256;
-constexpr int UNROLL = 16;
+constexpr int MAX_UNROLL = 16;
 
+// Four consecutive partial columns; the partials have the output's
+// precision (fp32, or bf16 widened exactly).
 __device__ inline float4 load4_once(const float* p) {
     typedef float f32x4_t __attribute__((ext_vector_type(4)));
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
     return make_float4(v[0], v[1], v[2], v[3]);
 }
+__device__ inline float4 load4_once(const uint16_t* p) {
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_float4(__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                       __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u));
+}
 
-template <typename T>
+template <typename T, int U>
 __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
     const int tid = threadIdx.x;
     const int nvec = a.D / 4;          // column vectors per row (16, 32 or 64)
@@ -58,37 +70,37 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
     const int row = blockIdx.x * (THREADS / row_threads) + tid / row_threads;
     const bool live = row < a.B * a.Hq;  // the last workgroup may hold fewer rows
     const int b = live ? row / a.Hq : 0, h = row % a.Hq;
-    const int len = a.len_att[b];
-    if (live && a.fused_append && h == 0 && rt == 0) {
-        // the only reader and writer of lengths[b] in this launch
-        const int l0 = a.lengths[b];
-        if (l0 >= 0 && l0 < a.T_cap) a.lengths[b] = l0 + 1;
-    }
-    const int nsplit = live ? splits_with_data(len, a.tile, a.S) : 0;
     const size_t prow = ((size_t)b * a.Hq + h) * a.S;
     const float* lse = a.lse_part + prow;
-    const float* op = a.o_part + prow * a.D + 4 * v;
+    const T* op = static_cast<const T*>(a.o_part) + prow * a.D + 4 * v;
 
     float m = -INFINITY, z = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = sg; j0 < nsplit; j0 += UNROLL * G) {
-        float4 o[UNROLL];
-        float w[UNROLL];
+    int nsplit = 0;
+    for (int j0 = sg; j0 < a.S; j0 += U * G) {
+        float4 o[U];
+        float w[U];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int j = j0 + u * G;
-            w[u] = -INFINITY;
-            o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < nsplit) {
-                w[u] = lse[j];
-                o[u] = load4_once(op + (size_t)j * a.D);
-            }
+        for (int u = 0; u < U; ++u) {
+            const int jc = min(j0 + u * G, a.S - 1);
+            w[u] = lse[jc];
+            o[u] = load4_once(op + (size_t)jc * a.D);
         }
+        // the attended length is requested after the partials (the compiler
+        // would otherwise hoist it, and wait for it, ahead of them)
+        asm volatile("" ::: "memory");
+        nsplit = live ? splits_with_data(a.len_att[b], a.tile, a.S) : 0;
         float mc = m;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) mc = fmaxf(mc, w[u]);
-        // a split can be empty for an early query of a several-token step
-        // (log-sum-exp -inf); all of this thread's may be
+        for (int u = 0; u < U; ++u) {
+            // a split can be empty for an early query of a several-token
+            // step (log-sum-exp -inf); splits past nsplit hold stale data
+            const bool ok = j0 + u * G < nsplit && w[u] != -INFINITY;
+            w[u] = ok ? w[u] : -INFINITY;
+            o[u] = ok ? o[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            mc = fmaxf(mc, w[u]);
+        }
+        // all of this thread's splits may be empty
         const float r = mc == -INFINITY ? 1.f : exp2f(m - mc);
         z *= r;
         acc.x *= r;
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
         acc.z *= r;
         acc.w *= r;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < U; ++u) {
             const float wu = w[u] == -INFINITY ? 0.f : exp2f(w[u] - mc);
             z += wu;
             acc.x = fmaf(wu, o[u].x, acc.x);
@@ -105,6 +117,11 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
             acc.w = fmaf(wu, o[u].w, acc.w);
         }
         m = mc;
+    }
+    if (live && a.fused_append && h == 0 && rt == 0) {
+        // the only reader and writer of lengths[b] in this launch
+        const int l0 = a.lengths[b];
+        if (l0 >= 0 && l0 < a.T_cap) a.lengths[b] = l0 + 1;
     }
 
     __shared__ float4 part[THREADS];
@@ -151,22 +168,35 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
     store4(orow, obase + 4 * v, acc);
 }
 
+template <typename T>
+hipError_t launch_t(const CombineArgs& a, int U, dim3 grid, hipStream_t stream) {
+    switch (U) {
+        case 1: hipLaunchKernelGGL((combine_kernel<T, 1>), grid, dim3(THREADS), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((combine_kernel<T, 2>), grid, dim3(THREADS), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((combine_kernel<T, 4>), grid, dim3(THREADS), 0, stream, a); break;
+        case 8: hipLaunchKernelGGL((combine_kernel<T, 8>), grid, dim3(THREADS), 0, stream, a); break;
+        default: hipLaunchKernelGGL((combine_kernel<T, MAX_UNROLL>), grid, dim3(THREADS), 0, stream, a); break;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& args, bool bf16, hipStream_t stream) {
-    // split groups per row: enough that UNROLL loads per thread cover the
-    // splits in one round, and a row no wider than a workgroup
+    // split groups per row: enough that MAX_UNROLL loads per thread cover
+    // the splits in one round, and a row no wider than a workgroup; then
+    // the smallest power-of-two unroll that covers them
     CombineArgs a = args;
     const int nvec = a.D / 4;
     int G = 1;
-    while (G * UNROLL < a.S && nvec * G * 2 <= THREADS) G *= 2;
+    while (G * MAX_UNROLL < a.S && nvec * G * 2 <= THREADS) G *= 2;
     a.groups = G;
+    int U = 1;
+    while (U < MAX_UNROLL && U * G < a.S) U *= 2;
     const int rows = a.B * a.Hq;
     const int per_block = THREADS / (nvec * G);
-    dim3 grid((rows + per_block - 1) / per_block), block(THREADS);
-    if (bf16) hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, stream, a);
-    return hipGetLastError();
+    dim3 grid((rows + per_block - 1) / per_block);
+    return bf16 ? launch_t<uint16_t>(a, U, grid, stream) : launch_t<float>(a, U, grid, stream);
 }
 
 }  // namespace kvd

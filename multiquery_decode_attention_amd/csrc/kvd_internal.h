@@ -59,7 +59,9 @@ struct PartialArgs {
     const void* k_cache;    // [B, Hkv, T_cap, D]
     const void* v_cache;    // [B, Hkv, T_cap, D]
     const int32_t* lengths; // [B]
-    float* o_part;          // [B, Hq, S, D] normalised partial outputs
+    // [B, Hq, S, D] normalised partial outputs, in the output's precision:
+    // bf16 (rounded to nearest even) when the output is bf16, else fp32
+    void* o_part;
     float* lse_part;        // [B, Hq, S]    base-2 log-sum-exp of each split
     int* err;               // sticky error word
     int* len_att;           // [B] attended length of each sequence, for the combine
@@ -94,7 +96,7 @@ struct PartialArgs {
 
 struct CombineArgs {
     int groups;             // split groups per row (set by the launcher)
-    const float* o_part;
+    const void* o_part;     // bf16 when the output is bf16, else fp32
     const float* lse_part;
     const int* len_att;     // [B] attended lengths written by the partial pass
     int32_t* lengths;       // advanced here after a fused append (else untouched)

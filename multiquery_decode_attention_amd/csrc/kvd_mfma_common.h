@@ -38,6 +38,30 @@ __device__ __forceinline__ int owned_col(int c, int e) {
     }
 }
 
+// Row i (of the lane's four accumulator rows) of a value product, times
+// inv, rounded to bf16 (nearest even) and stored with non-temporal stores:
+// one 16-byte store per 8 owned columns for D >= 128, one 8-byte store of
+// the 4 owned columns for D == 64.  The partials are read once, by the
+// combine.
+template <int D>
+__device__ __forceinline__ void store_partial_row(uint16_t* orow, const f32x4_t (&acc)[D / 16], int i, int c,
+                                                  float inv) {
+    if constexpr (D >= 128) {
+#pragma unroll
+        for (int e = 0; e < D / 16; e += 8) {
+            const u32x4_t o = {pack_bf16x2(acc[e][i] * inv, acc[e + 1][i] * inv),
+                               pack_bf16x2(acc[e + 2][i] * inv, acc[e + 3][i] * inv),
+                               pack_bf16x2(acc[e + 4][i] * inv, acc[e + 5][i] * inv),
+                               pack_bf16x2(acc[e + 6][i] * inv, acc[e + 7][i] * inv)};
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(orow + owned_col<D>(c, e)));
+        }
+    } else {
+        const u32x2_t o = {pack_bf16x2(acc[0][i] * inv, acc[1][i] * inv),
+                           pack_bf16x2(acc[2][i] * inv, acc[3][i] * inv)};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2_t*>(orow + owned_col<D>(c, 0)));
+    }
+}
+
 // B operand of the value product for output column block e: the 8 tokens'
 // bf16 values of that column, two per dword, gathered with byte permutes
 // from v[j][w] (token slot j, dword w of the lane's owned columns).

@@ -303,12 +303,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         const float li = __shfl(l, r);
         if (r < nh) {
             const float inv = 1.f / li;
-            float* orow = a.o_part + (row0 + (size_t)r * a.S) * D;
-#pragma unroll
-            for (int e = 0; e < NE; e += 4) {
-                const f32x4_t o = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv, acc[e + 3][i] * inv};
-                __builtin_nontemporal_store(o, reinterpret_cast<f32x4_t*>(orow + owned_col<D>(c, e)));
-            }
+            store_partial_row<D>(static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D, acc, i, c, inv);
         }
     }
     if (gq == 0 && head_ok)

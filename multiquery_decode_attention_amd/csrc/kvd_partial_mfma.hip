@@ -218,19 +218,7 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
         const float li = __shfl(l, 4 * gq + i);
         if (hi < a.M) {
             const float inv = 1.f / li;
-            float* orow = a.o_part + (row0 + (size_t)hi * a.S) * D;
-            if constexpr (D >= 128) {
-#pragma unroll
-                for (int e = 0; e < NE; e += 4) {
-                    float4 v = make_float4(acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
-                                           acc[e + 3][i] * inv);
-                    *reinterpret_cast<float4*>(orow + owned_col<D>(c, e)) = v;
-                }
-            } else {
-                float4 v = make_float4(acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv,
-                                       acc[3][i] * inv);
-                *reinterpret_cast<float4*>(orow + owned_col<D>(c, 0)) = v;
-            }
+            store_partial_row<D>(static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)hi * a.S) * D, acc, i, c, inv);
         }
     }
     if (gq == 0 && head_ok) a.lse_part[row0 + (size_t)head * a.S] = m_run + __builtin_log2f(l);

@@ -27,6 +27,12 @@ namespace {
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <typename T>
+__device__ inline T from_f32(float x);
+template <>
+__device__ inline float from_f32<float>(float x) { return x; }
+template <>
+__device__ inline uint16_t from_f32<uint16_t>(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // Element i of a 16-byte piece held as four 32-bit words.
 template <typename T>
@@ -167,8 +173,11 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
 
     const size_t row = ((size_t)b * a.Hq + h) * a.S + s;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    // partials in the output's precision (bf16 rounded to nearest even for
+    // a bf16 cache)
+    T* orow = static_cast<T*>(a.o_part) + row * D;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) a.o_part[row * D + lane + 64 * k] = acc[k] * inv;
+    for (int k = 0; k < DPL; ++k) orow[lane + 64 * k] = from_f32<T>(acc[k] * inv);
     if (lane == 0) a.lse_part[row] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
 }
 

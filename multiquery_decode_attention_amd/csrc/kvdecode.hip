@@ -29,7 +29,7 @@ struct kvdecode_s {
     // Device resources (allocated on first use, on the then-current device).
     int device = -1;
     int* err = nullptr;
-    float* o_part = nullptr;
+    void* o_part = nullptr;    // partials: bf16 for bf16 outputs, else fp32
     float* lse_part = nullptr;
     int ws_splits = 0;
 
@@ -204,7 +204,8 @@ int32_t ensure_workspace(kvdecode_s* h, int row_splits) {
     h->lse_part = nullptr;
     h->ws_splits = 0;
     const size_t rows = (size_t)h->d.batch * h->d.num_q_heads * (size_t)splits;
-    hipError_t e = hipMalloc(reinterpret_cast<void**>(&h->o_part), rows * h->d.head_dim * sizeof(float));
+    const size_t part_elem = h->d.dtype == KVD_F32 ? sizeof(float) : sizeof(uint16_t);
+    hipError_t e = hipMalloc(&h->o_part, rows * h->d.head_dim * part_elem);
     if (e != hipSuccess) return hip_fail(e);
     e = hipMalloc(reinterpret_cast<void**>(&h->lse_part), rows * sizeof(float));
     if (e != hipSuccess) {
