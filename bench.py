@@ -170,7 +170,7 @@ def main():
             cache = kvd.KVCache(case.k_cache, case.v_cache, case.lengths0, w.Hq)
         cache.set_variant(variant)
         cache.set_num_splits(args.splits)
-        cache.reserve()  # device workspace allocated now, not inside the timed steps
+        cache.reserve(tq)  # device workspace allocated now, not inside the timed steps
         copies.append({"case": case, "cache": cache, "out": torch.empty_like(case.q),
                        "len": case.lengths0.cpu().tolist(), "keep": keep})
     plan = copies[0]["cache"].plan()

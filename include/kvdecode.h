@@ -198,13 +198,16 @@ int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out
 
 /*
  * Bind the handle to the current device now and allocate everything its
- * current plan needs (workspace, error flag, and the event slots of
- * kvdecode_timing_enable), which would otherwise happen on the first append
- * or attend: lets a caller keep every hipMalloc out of its decode loop.
- * KVD_EINVAL if the handle is already bound to another device; KVD_ENOMEM
- * or KVD_EHIP if an allocation fails.  Idempotent.
+ * current plan needs for steps of up to max_new_tokens new tokens per
+ * sequence (1 for one-token decode; the draft length for
+ * kvdecode_append_attend_multi): workspace, error flag, and the event slots
+ * of kvdecode_timing_enable, which would otherwise happen on the first call
+ * that needs them.  Lets a caller keep every hipMalloc out of its decode
+ * loop.  KVD_EINVAL if max_new_tokens is outside 1..KVD_MAX_NEW_TOKENS or the
+ * handle is already bound to another device; KVD_ENOMEM or KVD_EHIP if an
+ * allocation fails.  Idempotent.
  */
-int32_t kvdecode_reserve(kvdecode_t h);
+int32_t kvdecode_reserve(kvdecode_t h, int32_t max_new_tokens);
 
 /*
  * Append one token per sequence (the generate-side cache update).

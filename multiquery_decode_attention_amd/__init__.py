@@ -109,7 +109,7 @@ def library():
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
         "kvdecode_append_attend_multi": (I, [P, I, P, P, P, P, F, P]),
         "kvdecode_status": (I, [P, P]),
-        "kvdecode_reserve": (I, [P]),
+        "kvdecode_reserve": (I, [P, I]),
         "kvdecode_set_num_splits": (I, [P, I]),
         "kvdecode_set_variant": (I, [P, I]),
         "kvdecode_set_unified_max": (I, [P, I, F]),
@@ -260,8 +260,8 @@ def kvdecode_status(h: int, stream=None) -> int:
     return library().kvdecode_status(h, _stream_ptr(stream))
 
 
-def kvdecode_reserve(h: int) -> None:
-    _check(library().kvdecode_reserve(h), "kvdecode_reserve")
+def kvdecode_reserve(h: int, max_new_tokens: int = 1) -> None:
+    _check(library().kvdecode_reserve(h, max_new_tokens), "kvdecode_reserve")
 
 
 def kvdecode_set_num_splits(h: int, n: int) -> None:
@@ -396,9 +396,10 @@ class KVCache:
     def status(self, stream=None) -> int:
         return kvdecode_status(self.handle, stream)
 
-    def reserve(self):
-        """Bind to the current device and allocate the workspace now."""
-        kvdecode_reserve(self.handle)
+    def reserve(self, max_new_tokens: int = 1):
+        """Bind to the current device and allocate now the workspace of
+        steps with up to max_new_tokens new tokens per sequence."""
+        kvdecode_reserve(self.handle, max_new_tokens)
 
     def set_num_splits(self, n: int):
         kvdecode_set_num_splits(self.handle, n)

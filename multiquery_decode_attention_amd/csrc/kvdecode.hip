@@ -505,11 +505,19 @@ int32_t kvdecode_status(kvdecode_t h, void* stream) {
     return KVD_OK;
 }
 
-int32_t kvdecode_reserve(kvdecode_t h) {
+int32_t kvdecode_reserve(kvdecode_t h, int32_t max_new_tokens) {
     if (!is_live(h)) return KVD_EINVAL;
+    if (max_new_tokens < 1 || max_new_tokens > KVD_MAX_NEW_TOKENS) return KVD_EINVAL;
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
-    if ((rc = ensure_workspace(h, make_plan(h).splits)) != KVD_OK) return rc;
+    // the workspace a step of T_q tokens needs grows with T_q, but its plan
+    // may pick fewer splits: reserve the largest over 1..max_new_tokens
+    int row_splits = 0;
+    for (int t = 1; t <= max_new_tokens; ++t) {
+        const int r = make_plan(h, t).splits * t;
+        row_splits = r > row_splits ? r : row_splits;
+    }
+    if ((rc = ensure_workspace(h, row_splits)) != KVD_OK) return rc;
     return ensure_events(h);
 }
 

@@ -113,6 +113,8 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_set_unified_max(h, 1, float("nan")) == kvd.KVD_EINVAL
     assert lib.kvdecode_set_unified_max(h, 1, 3.5) == kvd.KVD_OK
     assert lib.kvdecode_set_unified_max(h, 0, float("nan")) == kvd.KVD_OK  # off: phi unused
+    assert lib.kvdecode_reserve(h, 0) == kvd.KVD_EINVAL
+    assert lib.kvdecode_reserve(h, kvd.KVD_MAX_NEW_TOKENS + 1) == kvd.KVD_EINVAL
     assert lib.kvdecode_timing_enable(h, -1, kvd.KVD_TIME_ALL) == kvd.KVD_EINVAL
     assert lib.kvdecode_timing_enable(h, 4, 8) == kvd.KVD_EINVAL
     assert lib.kvdecode_timing_enable(h, 4, kvd.KVD_TIME_ALL) == kvd.KVD_OK
@@ -123,7 +125,7 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_destroy(h) == kvd.KVD_EINVAL
     assert lib.kvdecode_attend(h, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
     assert lib.kvdecode_status(h, None) == kvd.KVD_EINVAL
-    assert lib.kvdecode_reserve(h) == kvd.KVD_EINVAL
+    assert lib.kvdecode_reserve(h, 1) == kvd.KVD_EINVAL
     assert lib.kvdecode_destroy(None) == kvd.KVD_EINVAL
 
 

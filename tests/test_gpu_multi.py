@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS}
 
 
-def multi_step(case, Hq, *, variant="auto", splits=None, page_size=0):
+def multi_step(case, Hq, *, variant="auto", splits=None, page_size=0, reserve=0):
     dev = torch.device("cuda")
     L = case.lengths0.to(dev, torch.int32, copy=True)
     if page_size:
@@ -36,6 +36,8 @@ def multi_step(case, Hq, *, variant="auto", splits=None, page_size=0):
         cache.set_variant(VARIANTS[variant])
         if splits is not None:
             cache.set_num_splits(splits)
+        if reserve:
+            cache.reserve(reserve)
         kn, vn, q = (t.to(dev).contiguous() for t in (case.k_new, case.v_new, case.q))
         out = cache.step_multi(kn, vn, q, scale=case.scale)
         status = cache.status()
@@ -101,6 +103,14 @@ def test_multi_token_fp32_and_paged():
     check_multi(case, 8, "multi fp32 valu")
     case = inputs.make_multi_case(3, 48, 1, 256, 512, [200, 33, 480], 4, "bf16", seed=62)
     check_multi(case, 48, "multi paged", page_size=64)
+
+
+@pytest.mark.parametrize("T_q,reserve", [(4, 4), (4, 16), (16, 16)])
+def test_multi_token_after_reserve(T_q, reserve):
+    """kvdecode_reserve for steps of up to `reserve` new tokens, then a step
+    of T_q: same results as without the reservation."""
+    case = inputs.make_multi_case(3, 48, 1, 256, 1024, [1000, 31, 500], T_q, "bf16", seed=70 + T_q)
+    check_multi(case, 48, f"multi reserve {reserve} T_q={T_q}", reserve=reserve)
 
 
 def test_multi_token_without_room():
