@@ -81,8 +81,14 @@ typedef enum {
  *   MFMA: bf16 matrix-core kernel, one wave per 16 query heads, each wave
  *         loading K/V straight into registers.
  *   LDS:  bf16 matrix-core kernel, four waves per (split, KV head) sharing
- *         K/V tiles staged in LDS by direct global->LDS loads. */
-enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2, KVD_VARIANT_LDS = 3 };
+ *         K/V tiles staged in LDS by direct global->LDS loads (for an fp8
+ *         cache: its fp8 counterpart).
+ *   WAVE: fp8 caches with d >= 128: four waves per (split, KV head[, group
+ *         of up to 48 (d = 256) or 64 (d = 128) query heads]), each
+ *         streaming its own tiles for all of the group's heads, merged in
+ *         LDS at the end. */
+enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2, KVD_VARIANT_LDS = 3,
+       KVD_VARIANT_WAVE = 4 };
 
 typedef struct {
     int32_t batch;        /* B  >= 1                                        */
@@ -305,8 +311,11 @@ int32_t kvdecode_set_unified_max(kvdecode_t h, int32_t enable, float phi);
 
 /*
  * Choose the partial-pass kernel: KVD_VARIANT_AUTO (LDS for bf16, VALU for
- * fp32), KVD_VARIANT_VALU (any dtype), KVD_VARIANT_MFMA or KVD_VARIANT_LDS
- * (bf16 only; KVD_EUNSUPPORTED for fp32).
+ * fp32; for fp8 WAVE when d >= 128 and one workgroup holds the whole query
+ * group -- up to 16 heads per KV head at d = 256, 48 at d = 128 -- else LDS),
+ * KVD_VARIANT_VALU (fp32
+ * or bf16), KVD_VARIANT_MFMA (bf16), KVD_VARIANT_LDS (bf16 or fp8) or
+ * KVD_VARIANT_WAVE (fp8, d >= 128); KVD_EUNSUPPORTED otherwise.
  */
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant);
 

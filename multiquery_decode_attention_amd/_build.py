@@ -40,6 +40,7 @@ CFLAGS = [
 FILE_FLAGS = {
     "kvd_partial_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kvd_partial_lds_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kvd_partial_wave_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

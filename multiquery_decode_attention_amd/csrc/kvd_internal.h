@@ -222,6 +222,23 @@ inline int lds_fp8_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_partial_lds_fp8(const PartialArgs& a, hipStream_t stream);
+
+// fp8 cache, kernel in which each wave streams its own tiles for all rows of
+// a group (kvd_partial_wave_fp8.hip): 16-row blocks per group (each wave
+// holds the whole group's accumulators and queries in its 256 registers: one
+// block at d = 256, three at d = 128) and ring stages per wave (a stage is
+// one tile's K and V codes plus a 1 KB exponent block).
+constexpr int wave_fp8_max_row_blocks(int D) { return D == 256 ? 1 : 3; }
+inline int wave_fp8_row_blocks(int D, int M) {
+    const int b = (M + 15) / 16;
+    return b < wave_fp8_max_row_blocks(D) ? b : wave_fp8_max_row_blocks(D);
+}
+constexpr int wave_fp8_stages(int D) { return D == 256 ? 2 : 2; }
+inline int wave_fp8_groups_per_cu(int D) {
+    const int g = LDS_BYTES_PER_CU / (4 * wave_fp8_stages(D) * (64 * D + 1024));
+    return g < 1 ? 1 : (g > 8 ? 8 : g);
+}
+hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
 // Quantize the new token's bf16 K/V rows into slot lengths[b] and advance it.
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                              int8_t* k_exp, int8_t* v_exp, int32_t* lengths, int* err, int B,

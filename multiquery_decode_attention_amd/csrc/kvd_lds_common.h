@@ -17,6 +17,29 @@ __device__ __forceinline__ void wait_vm_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0) without a barrier: a wave waiting for its
+// own direct loads, whose LDS bytes it then reads (and whose earlier LDS
+// reads have then returned, so their slots may be refilled).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most `stages_after` stages of this wave's own loads (PERW
+// each) are still in flight; no barrier.
+template <int PERW, int MAXA>
+__device__ __forceinline__ void wait_own_stage(int stages_after) {
+    static_assert(MAXA >= 0 && MAXA <= 4, "ring depth");
+    switch (stages_after) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<(MAXA >= 1) * PERW>(); break;
+        case 2: wait_vm<(MAXA >= 2) * 2 * PERW>(); break;
+        case 3: wait_vm<(MAXA >= 3) * 3 * PERW>(); break;
+        default: wait_vm<(MAXA >= 4) * 4 * PERW>(); break;
+    }
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform value.
 __device__ __forceinline__ int wave_index() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));

@@ -68,7 +68,13 @@ bool is_fp8(const kvdecode_s* h) { return h->d.dtype == KVD_FP8_E4M3; }
 
 int resolve_variant(const kvdecode_s* h) {
     if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
-    if (is_fp8(h)) return KVD_VARIANT_LDS;
+    // fp8: the wave kernel when one workgroup holds the whole query group
+    // (MHA and GQA: each tile is widened once instead of once per wave);
+    // larger groups share tiles between waves
+    if (is_fp8(h))
+        return h->d.head_dim >= 128 && h->M <= 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim)
+                   ? KVD_VARIANT_WAVE
+                   : KVD_VARIANT_LDS;
     return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
 }
 
@@ -95,7 +101,11 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
     const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
     const int rows = h->M * T_q;  // query rows per KV head
     Shape sh;
-    if (variant == KVD_VARIANT_LDS) {
+    if (variant == KVD_VARIANT_WAVE) {
+        const int rows_per_group = 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim);
+        sh.units = bkv * ((rows + rows_per_group - 1) / rows_per_group);
+        sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(h->d.head_dim);
+    } else if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((rows + 63) / 64);
         sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
                                                : kvd::lds_groups_per_cu(h->d.head_dim, lds_which));
@@ -273,7 +283,8 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
     const Plan p = make_plan(h, T_q);
-    if (is_fp8(h) ? p.variant != KVD_VARIANT_LDS : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
+    if (is_fp8(h) ? (p.variant != KVD_VARIANT_LDS && p.variant != KVD_VARIANT_WAVE)
+                  : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
         return KVD_EUNSUPPORTED;
     if (T_q > 1 && (is_fp8(h) || p.variant == KVD_VARIANT_MFMA)) return KVD_EUNSUPPORTED;
     int32_t rc = ensure_device(h);
@@ -338,7 +349,8 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
                        h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = is_fp8(h)                       ? kvd::launch_partial_lds_fp8(a, st)
+    hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, st)
+                   : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, st)
                    : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
                                                    : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
@@ -537,10 +549,15 @@ int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
 
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
     if (!is_live(h)) return KVD_EINVAL;
-    if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_LDS) return KVD_EUNSUPPORTED;
-    if (is_fp8(h)) return variant == KVD_VARIANT_AUTO || variant == KVD_VARIANT_LDS
-                              ? (h->variant_req = variant, KVD_OK)
-                              : KVD_EUNSUPPORTED;
+    if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
+    if (is_fp8(h)) {
+        const bool ok = variant == KVD_VARIANT_AUTO || variant == KVD_VARIANT_LDS ||
+                        (variant == KVD_VARIANT_WAVE && h->d.head_dim >= 128);
+        if (!ok) return KVD_EUNSUPPORTED;
+        h->variant_req = variant;
+        return KVD_OK;
+    }
+    if (variant == KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;

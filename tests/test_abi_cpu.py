@@ -249,11 +249,23 @@ def test_create_fp8_rejects(lib, field, value, code):
 def test_fp8_handle(lib):
     h = ctypes.c_void_p()
     assert lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc()), ctypes.byref(h)) == kvd.KVD_OK
-    assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "wave"  # d = 128
     for v in (kvd.KVD_VARIANT_VALU, kvd.KVD_VARIANT_MFMA):
         assert lib.kvdecode_set_variant(h.value, v) == kvd.KVD_EUNSUPPORTED
     assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_LDS) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_WAVE) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "wave"
     assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
+    # d = 64: the wave kernel needs 16-byte code chunks of the value rows
+    assert lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc(head_dim=64)), ctypes.byref(h)) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_WAVE) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
+    # bf16 handles have no wave kernel
+    rc, hb = create(lib, make_desc())
+    assert rc == kvd.KVD_OK and lib.kvdecode_set_variant(hb, kvd.KVD_VARIANT_WAVE) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_destroy(hb) == kvd.KVD_OK
     # the fp8 cache type is only reachable through kvdecode_create_fp8
     rc, h2 = create(lib, make_desc(dtype=kvd.KVD_FP8_E4M3))
     assert rc == kvd.KVD_EUNSUPPORTED and not h2

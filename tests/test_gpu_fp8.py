@@ -19,14 +19,20 @@ from gpu_helpers import say, to_f64
 
 pytestmark = pytest.mark.gpu
 
+# wave: each wave streams its own tiles for all query heads of its group
+# (d >= 128; several row groups share tiles through L2); lds: the four waves
+# share every tile
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "wave": kvd.KVD_VARIANT_WAVE, "lds": kvd.KVD_VARIANT_LDS}
 
-def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None, unified_max=None):
+
+def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None, unified_max=None, variant="auto"):
     dev = torch.device("cuda")
     kc, vc = case.k_codes.to(dev, copy=True), case.v_codes.to(dev, copy=True)
     ke, ve = case.k_exp.to(dev, copy=True), case.v_exp.to(dev, copy=True)
     L = (lengths if lengths is not None else case.lengths0).to(dev, torch.int32, copy=True)
     cache = kvd.KVCache(kc, vc, L, Hq, k_exp=ke, v_exp=ve)
     try:
+        cache.set_variant(VARIANTS[variant])
         if splits is not None:
             cache.set_num_splits(splits)
         if unified_max is not None:
@@ -77,22 +83,31 @@ SHAPES = {  # name: (B, Hq, Hkv, D, T_cap, lengths)
     "ragged_gqa_like": (8, 64, 8, 128, 8192, [64, 8192, 4000, 77, 1024, 5000, 31, 8000]),
     "long_mqa": (1, 48, 1, 256, 16384, [16384]),
     "small_d64": (2, 8, 1, 64, 160, [129, 64]),
+    "gqa48_d128": (2, 96, 2, 128, 1024, [1000, 77]),     # three 16-row blocks per wave
+    "gqa64_d128": (2, 64, 1, 128, 512, [500, 33]),       # two row groups (48 + 16)
 }
 
 
+@pytest.mark.parametrize("variant", ["wave", "lds"])
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", list(SHAPES))
-def test_fp8_shapes(name, fused):
+def test_fp8_shapes(name, fused, variant):
     B, Hq, Hkv, D, T, L = SHAPES[name]
+    if variant == "wave" and D < 128:
+        pytest.skip("the wave kernel needs d >= 128")
     case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=90 + len(name))
-    check_fp8(case, Hq, f"fp8/{name}", fused=fused)
+    check_fp8(case, Hq, f"fp8/{name}/{variant}", fused=fused, variant=variant)
 
 
-@pytest.mark.parametrize("splits", [1, 5])
-def test_fp8_forced_splits(splits):
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("Hq", [16, 48])
+@pytest.mark.parametrize("splits", [1, 2, 5])
+def test_fp8_forced_splits(splits, Hq, variant):
+    """Splits of 1 to 8 tiles: in the wave kernel some waves of a split get
+    no tile at all, and lengths end on and next to tile edges."""
     lengths = [1, 31, 32, 33, 64, 65, 127, 128, 200, 256]
-    case = inputs.make_fp8_case(len(lengths), 16, 2, 128, 256, lengths, seed=95 + splits)
-    check_fp8(case, 16, f"fp8 S={splits}", splits=splits)
+    case = inputs.make_fp8_case(len(lengths), Hq, 2, 128, 256, lengths, seed=95 + splits)
+    check_fp8(case, Hq, f"fp8 S={splits} Hq={Hq} {variant}", splits=splits, variant=variant)
 
 
 def test_fp8_append_extremes():
@@ -111,6 +126,19 @@ def test_fp8_append_extremes():
     check_fp8(case, Hq, "fp8 append extremes")
 
 
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,variant", [("mha", 2, 8, 8, 128, "wave"), ("gqa", 2, 64, 8, 128, "wave"),
+                                                      ("mqa48_d128", 2, 48, 1, 128, "wave"),
+                                                      ("mqa48_d256", 2, 48, 1, 256, "lds"),
+                                                      ("mqa16_d256", 2, 16, 1, 256, "wave"),
+                                                      ("d64", 2, 8, 1, 64, "lds")])
+def test_fp8_auto_picks(name, B, Hq, Hkv, D, variant):
+    """The automatic choice: the wave kernel when one workgroup holds the
+    whole query group at d >= 128, the shared-tile kernel otherwise."""
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, 256, [200, 100], seed=77)
+    out, plan = check_fp8(case, Hq, f"fp8 auto {name}")
+    assert plan["variant"] == variant
+
+
 def test_fp8_capacity_overflow():
     case = inputs.make_fp8_case(2, 8, 1, 128, 64, [64, 10], seed=98)
     L0 = torch.tensor([64, 9], dtype=torch.int32)
@@ -122,8 +150,9 @@ def test_fp8_capacity_overflow():
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("variant", ["wave", "lds"])
 @pytest.mark.parametrize("phi", [0.0, -40.0, 1e4])
-def test_fp8_unified_max(phi):
+def test_fp8_unified_max(phi, variant):
     B, Hq, Hkv, D, T, L = SHAPES["palm_like"]
     case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=99)
-    check_fp8(case, Hq, f"fp8 unified max {phi}", unified_max=phi)
+    check_fp8(case, Hq, f"fp8 unified max {phi} {variant}", unified_max=phi, variant=variant)
