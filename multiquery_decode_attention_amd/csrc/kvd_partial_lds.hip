@@ -1,11 +1,16 @@
 // kvd_partial_lds.hip -- bf16 split-KV partial pass with LDS-shared K/V tiles.
 //
 // Work unit: (split s, KV head g, sequence b[, block of 64 query heads]) ->
-// one workgroup of 4 waves.  The group's M query heads are dealt out to the
-// four waves (ceil(M/4) each, at most 16); every wave runs the same score /
-// online-softmax / value products as the register kernel on its heads, but
-// all four read one shared copy of each 32-token K/V tile from LDS, so a tile
-// crosses HBM and the cache hierarchy once for all M heads.
+// one workgroup of 4 waves.  The group's M query heads fill the waves' 16-row
+// matrix-core blocks in turn (16 heads per wave; a group of at most 16 lives
+// in wave 0); every wave with heads runs the same score / online-softmax /
+// value products as the register kernel on them, but all read one shared
+// copy of each 32-token K/V tile from LDS, so a tile crosses HBM and the
+// cache hierarchy once for all M heads.  A wave without heads only loads its
+// share of every stage: spreading a small group over all four waves made
+// each wave read every tile from LDS for two or three heads (ragged GQA
+// with 8 heads per KV head: 366 us packed into one wave against 383 us
+// spread).
 //
 // Tiles arrive through a ring of NS LDS stages filled by gfx950's direct
 // global->LDS 16-byte loads (no registers held while in flight): stage i+NS-1
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, gq = lane >> 4;
     const int mg = min(a.M - hg * 64, 64);   // heads of this workgroup
-    const int hpw = (mg + 3) / 4;             // heads per wave
+    const int hpw = mg < 16 ? mg : 16;        // heads per wave
     const int hw0 = hg * 64 + wave * hpw;     // first head (within the KV group) of this wave
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;

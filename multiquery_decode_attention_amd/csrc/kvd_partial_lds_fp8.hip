@@ -69,7 +69,10 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, gq = lane >> 4;
     const int mg = min(a.M - hg * 64, 64);
-    const int hpw = (mg + 3) / 4;
+    // heads fill the waves' 16-row blocks in turn: each wave with heads
+    // widens every tile, so fewer such waves do less of it (48 heads: three
+    // widening waves instead of four)
+    const int hpw = mg < 16 ? mg : 16;
     const int hw0 = hg * 64 + wave * hpw;
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;
