@@ -233,7 +233,9 @@ inline int wave_fp8_row_blocks(int D, int M) {
     const int b = (M + 15) / 16;
     return b < wave_fp8_max_row_blocks(D) ? b : wave_fp8_max_row_blocks(D);
 }
-constexpr int wave_fp8_stages(int D) { return D == 256 ? 2 : 2; }
+// Two stages per wave: at d = 256 four waves' rings take 136 KB of the CU's
+// 160 KB; at d = 128 (72 KB) two workgroups fit per CU.
+constexpr int wave_fp8_stages(int) { return 2; }
 inline int wave_fp8_groups_per_cu(int D) {
     const int g = LDS_BYTES_PER_CU / (4 * wave_fp8_stages(D) * (64 * D + 1024));
     return g < 1 ? 1 : (g > 8 ? 8 : g);

@@ -83,7 +83,9 @@ int resolve_variant(const kvdecode_s* h) {
 // with no tile of a sequence exit at once.  For every candidate split count
 // S the cost model charges
 //   rounds(S) * (bytes of the busiest split + a fixed fill cost) * slots
-//     + fp32 partial traffic (written by the partial pass, read by combine)
+//     + partial traffic (written by the partial pass, read by the combine),
+//       charged at 4 bytes per value although bf16 outputs keep bf16
+//       partials: the fill constant was tuned with this charge
 // where rounds(S) = ceil(work units * S / resident slots): a launch whose
 // last round is partly empty wastes the rest of that round.  Among plans
 // within 2% of the cheapest, the one with most splits wins (shorter splits

@@ -33,7 +33,7 @@ def attend_bytes(B: int, Hq: int, Hkv: int, D: int, elem: int, lengths: Sequence
 
 def partial_pass_bytes(B: int, Hq: int, Hkv: int, D: int, elem: int, lengths: Sequence[int]) -> int:
     """The split-KV partial kernel's algorithmic reads: K/V of the valid
-    prefixes plus the queries (its fp32 partial outputs are implementation
+    prefixes plus the queries (its partial outputs are implementation
     overhead, not counted)."""
     return kv_read_bytes(Hkv, D, elem, lengths) + B * Hq * D * elem
 
