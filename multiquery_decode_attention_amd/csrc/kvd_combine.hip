@@ -59,15 +59,66 @@ __device__ inline float4 load4_once(const uint16_t* p) {
                        __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u));
 }
 
+// Sequences by this step's attended length, longest first (ties by
+// index), for the next partial pass: a bitonic sort of (length, ~index)
+// keys in LDS, N = the next power of two >= B <= COMBINE_SORT_MAX (padding
+// keys are 0 and sort last).  Only the dispatch order of the next pass
+// depends on it.
+__device__ void sort_by_length(const CombineArgs& a, unsigned long long* keys) {
+    const int n = a.B;
+    bool differs = false;
+    const int l_first = a.len_att[0];
+    for (int i = threadIdx.x; i < n; i += THREADS) differs |= a.len_att[i] != l_first;
+    if (!__syncthreads_or(differs)) {
+        if (threadIdx.x == 0) a.order[n] = 0;  // equal lengths: any order serves
+        return;
+    }
+    int N = 1;
+    while (N < n) N <<= 1;
+    for (int i = threadIdx.x; i < N; i += THREADS) {
+        const int len = i < n ? a.len_att[i] : 0;
+        keys[i] = i < n ? ((unsigned long long)(unsigned)(len > 0 ? len : 0) << 32) | (unsigned)~i : 0ull;
+    }
+    __syncthreads();
+    for (int k = 2; k <= N; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < N; i += THREADS) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const unsigned long long x = keys[i], y = keys[l];
+                    // runs with (i & k) == 0 descend, the others ascend
+                    if ((i & k) == 0 ? x < y : x > y) {
+                        keys[i] = y;
+                        keys[l] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = threadIdx.x; i < n; i += THREADS) a.order[i] = (int)~(unsigned)keys[i];
+    if (threadIdx.x == 0) a.order[n] = 1;  // valid from the next launch on
+}
+
+constexpr int SMEM_BYTES = THREADS * (16 + 8) > COMBINE_SORT_MAX * 8 ? THREADS * (16 + 8) : COMBINE_SORT_MAX * 8;
+
 template <typename T, int U>
 __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM_BYTES];
+    // the extra workgroup is the first, so its sort runs beside the merges
+    // instead of after them
+    if (a.order != nullptr && blockIdx.x == 0) {
+        sort_by_length(a, reinterpret_cast<unsigned long long*>(smem));
+        return;
+    }
+    const int blk = (int)blockIdx.x - (a.order != nullptr ? 1 : 0);
     const int tid = threadIdx.x;
     const int nvec = a.D / 4;          // column vectors per row (16, 32 or 64)
     const int G = a.groups;            // split groups per row
     const int row_threads = nvec * G;
     const int rt = tid % row_threads;  // thread within its row
     const int v = rt % nvec, sg = rt / nvec;
-    const int row = blockIdx.x * (THREADS / row_threads) + tid / row_threads;
+    const int row = blk * (THREADS / row_threads) + tid / row_threads;
     const bool live = row < a.B * a.Hq;  // the last workgroup may hold fewer rows
     const int b = live ? row / a.Hq : 0, h = row % a.Hq;
     const size_t prow = ((size_t)b * a.Hq + h) * a.S;
@@ -124,8 +175,8 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
         if (l0 >= 0 && l0 < a.T_cap) a.lengths[b] = l0 + 1;
     }
 
-    __shared__ float4 part[THREADS];
-    __shared__ float2 mz[THREADS];
+    float4* part = reinterpret_cast<float4*>(smem);
+    float2* mz = reinterpret_cast<float2*>(smem + THREADS * sizeof(float4));
     if (G > 1) {
         part[tid] = acc;
         mz[tid] = make_float2(m, z);
@@ -187,6 +238,7 @@ hipError_t launch_combine(const CombineArgs& args, bool bf16, hipStream_t stream
     // the splits in one round, and a row no wider than a workgroup; then
     // the smallest power-of-two unroll that covers them
     CombineArgs a = args;
+    if (a.B > COMBINE_SORT_MAX) a.order = nullptr;  // no order: the next pass keeps the batch's
     const int nvec = a.D / 4;
     int G = 1;
     while (G * MAX_UNROLL < a.S && nvec * G * 2 <= THREADS) G *= 2;
@@ -195,7 +247,7 @@ hipError_t launch_combine(const CombineArgs& args, bool bf16, hipStream_t stream
     while (U < MAX_UNROLL && U * G < a.S) U *= 2;
     const int rows = a.B * a.Hq;
     const int per_block = THREADS / (nvec * G);
-    dim3 grid((rows + per_block - 1) / per_block);
+    dim3 grid((rows + per_block - 1) / per_block + (a.order != nullptr ? 1 : 0));
     return bf16 ? launch_t<uint16_t>(a, U, grid, stream) : launch_t<float>(a, U, grid, stream);
 }
 

@@ -92,6 +92,11 @@ struct PartialArgs {
     // which it is raised (8; 64 with a unified maximum).
     float m_init;
     float tau;
+    // LDS kernel: sequences in dispatch order, longest first, as the last
+    // combine left them ([B] then a flag word, set once the order is valid;
+    // see CombineArgs::order).  A hint only: any permutation gives the same
+    // results.
+    const int* order;
 };
 
 struct CombineArgs {
@@ -105,7 +110,14 @@ struct CombineArgs {
     int B, Hq, D, T_cap;
     int tile;               // tokens per tile of the partial kernel that ran
     int S;
+    // [B] + flag: one extra workgroup of the combine sorts the sequences by
+    // this step's attended length, longest first, for the next partial pass
+    // (which then starts the longest workgroups first).  Equal lengths clear
+    // the flag (no order: the next pass keeps the batch's); so does a batch
+    // above COMBINE_SORT_MAX sequences, never sorted.
+    int* order;
 };
+constexpr int COMBINE_SORT_MAX = 2048;
 
 // Token tiles of a sequence are dealt round-robin to its S splits: split s
 // owns tiles s, s+S, s+2S, ...  At any moment the S workgroups of a
@@ -124,9 +136,8 @@ struct SeqLen {
     int slot;      // slot of the appended token (when appended)
     bool appended;
 };
-__device__ __forceinline__ SeqLen sequence_length(const int32_t* lengths, int* err, int* len_att,
-                                                  int b, int T_cap, bool fused, bool lead) {
-    const int l0 = lengths[b];
+__device__ __forceinline__ SeqLen sequence_length_of(int l0, int* err, int* len_att, int b, int T_cap, bool fused,
+                                                     bool lead) {
     SeqLen r;
     r.slot = l0;
     r.appended = false;
@@ -142,6 +153,10 @@ __device__ __forceinline__ SeqLen sequence_length(const int32_t* lengths, int* e
     }
     if (lead) len_att[b] = r.len;
     return r;
+}
+__device__ __forceinline__ SeqLen sequence_length(const int32_t* lengths, int* err, int* len_att,
+                                                  int b, int T_cap, bool fused, bool lead) {
+    return sequence_length_of(lengths[b], err, len_att, b, T_cap, fused, lead);
 }
 
 // Tokens query row r attends to (see PartialArgs::T_q).
@@ -171,6 +186,60 @@ __device__ __forceinline__ BlockCoord block_coord(int units) {
     c.split = L / units;
     c.unit = L - c.split * units;
     return c;
+}
+
+// The LDS kernel's grid deals work units to the eight XCDs in turn (block L
+// runs on XCD L mod 8) and, on each XCD, runs them unit after unit, longest
+// first: the k-th block of XCD x is head group k mod G of split (k / G) mod S
+// of unit slot k / (G * S), i.e. unit = slot * 8 + x, with units numbered in
+// dispatch order (sequence order[p] at position p once the combine has
+// sorted the lengths).  Every split of a unit stays on one XCD, as in the
+// split-major grid (which measured 8% faster at long context than splits
+// spread over the XCDs), its head groups are dispatched one after another
+// (their loads of the same tiles meet in that XCD's L2), and the longest
+// workgroups start first (ragged GQA: 333 us against 366 us).  Blocks of
+// padding slots past the last unit exit at once.
+struct LdsCoord {
+    int split, hg, p, g;  // p: dispatch position of the sequence
+    bool live;
+};
+__device__ __forceinline__ LdsCoord lds_coord(int S, int groups, int Hkv, int B) {
+    const int L = (int)blockIdx.x;
+    const int k = L >> 3;
+    LdsCoord c;
+    c.hg = k % groups;
+    const int k2 = k / groups;
+    c.split = k2 % S;
+    const int unit = (k2 / S) * 8 + (L & 7);
+    c.live = unit < B * Hkv;
+    c.g = unit % Hkv;
+    c.p = c.live ? unit / Hkv : 0;
+    return c;
+}
+// Sequence at dispatch position p and its length word: order[p] when the
+// order is valid (its length then loads after it), else p, whose length is
+// requested together with the order words, so a batch the combine left
+// unsorted pays no extra memory round trip.
+struct SeqAt {
+    int b, len0;
+};
+__device__ __forceinline__ SeqAt seq_at(int p, int B, const int* order, const int32_t* lengths) {
+    const int flag = order != nullptr ? order[B] : 0;
+    const int o = order != nullptr ? order[p] : p;
+    const int len_p = lengths[p];
+    SeqAt r;
+    if (flag == 1) {
+        r.b = o < 0 ? 0 : (o >= B ? B - 1 : o);  // memory-safe whatever the hint holds
+        r.len0 = lengths[r.b];
+    } else {
+        r.b = p;
+        r.len0 = len_p;
+    }
+    return r;
+}
+// blocks of the LDS kernel's grid: units padded to whole rounds of the XCDs
+inline unsigned lds_grid_blocks(int S, int groups, int Hkv, int B) {
+    return (unsigned)(((long long)B * Hkv + 7) / 8 * 8 * S * groups);
 }
 
 // Each launcher returns the hipError_t of its launch.

@@ -81,33 +81,17 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                   "waves 0-1 load K, waves 2-3 load V");
     __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
 
-    // unit = (sequence b, KV head g[, head group hg])
-    int s, hg, g, b;
-    if constexpr (!GROUPED) {
-        const BlockCoord bc = block_coord(a.B * a.Hkv);
-        s = bc.split;
-        hg = 0;
-        g = bc.unit % a.Hkv;
-        b = bc.unit / a.Hkv;
-    } else {
-        // More than 64 query rows per KV head take several workgroups, and
-        // each streams the same K/V tiles.  Blocks L, L+8, L+16, ... (same
-        // L mod 8, so the same XCD, and dispatched one after another) are
-        // the head groups of one (split, sequence, KV head): they walk the
-        // same tiles at about the same pace, and the loads of all but the
-        // first meet that XCD's L2.  Base units past the last exit at once.
-        const int L = (int)blockIdx.x;
-        hg = (L >> 3) % head_groups;
-        const int base = (L / (8 * head_groups)) * 8 + (L & 7);
-        const int base_units = a.B * a.Hkv;
-        if (base >= a.S * base_units) return;
-        s = base / base_units;
-        const int u = base - s * base_units;
-        g = u % a.Hkv;
-        b = u / a.Hkv;
-    }
-    const SeqLen sl = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
-                                      s == 0 && g == 0 && hg == 0 && threadIdx.x == 0);
+    // unit = (sequence b, KV head g[, head group hg]).  More than 64 query
+    // rows per KV head take several workgroups (head groups), and each
+    // streams the same K/V tiles: dispatched one after another on one XCD,
+    // they walk the same tiles at about the same pace, and the loads of all
+    // but the first meet that XCD's L2.
+    const LdsCoord lc = lds_coord(a.S, head_groups, a.Hkv, a.B);
+    if (!lc.live) return;  // padding, before any barrier
+    const SeqAt sa = seq_at(lc.p, a.B, a.order, a.lengths);
+    const int s = lc.split, hg = lc.hg, g = lc.g, b = sa.b;
+    const SeqLen sl = sequence_length_of(sa.len0, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
+                                         s == 0 && g == 0 && hg == 0 && threadIdx.x == 0);
     const int len = sl.len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
     if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
@@ -446,17 +430,13 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 template <int D, int NS, int VL>
 hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 63) / 64;
-    const unsigned base = (unsigned)a.S * a.B * a.Hkv;
-    const dim3 block(256);
+    const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
     if (groups == 1) {
-        const dim3 grid(base);
         if (a.kv.block_table)
             hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, true, false>), grid, block, 0, stream, a, 1);
         else
             hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, false, false>), grid, block, 0, stream, a, 1);
     } else {
-        // base units padded to whole rounds of the eight XCDs
-        const dim3 grid((base + 7) / 8 * 8 * groups);
         if (a.kv.block_table)
             hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, true, true>), grid, block, 0, stream, a, groups);
         else

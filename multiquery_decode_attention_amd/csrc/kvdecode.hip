@@ -190,9 +190,10 @@ int32_t ensure_device(kvdecode_s* h) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return KVD_EHIP;
     if (h->device >= 0) return dev == h->device ? KVD_OK : KVD_EINVAL;
-    // err word, then per sequence the attended length of the last step and
-    // the rows its last append added
-    const size_t words = 1 + 2 * (size_t)h->d.batch;
+    // err word; per sequence the attended length of the last step and the
+    // rows its last append added; then the dispatch order the combine leaves
+    // for the next partial pass (B entries and a flag, zero: not yet valid)
+    const size_t words = 2 + 3 * (size_t)h->d.batch;
     e = hipMalloc(reinterpret_cast<void**>(&h->err), words * sizeof(int));
     if (e != hipSuccess) return hip_fail(e);
     e = hipMemset(h->err, 0, words * sizeof(int));
@@ -318,6 +319,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.M = h->M * T_q;
     a.T_q = T_q;
     a.n_new = T_q > 1 ? h->err + 1 + h->d.batch : nullptr;
+    a.order = h->err + 1 + 2 * h->d.batch;
     a.D = h->d.head_dim;
     a.T_cap = h->d.capacity;
     a.S = p.splits;
@@ -333,6 +335,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     c.o_part = h->o_part;
     c.lse_part = h->lse_part;
     c.len_att = h->err + 1;
+    c.order = h->err + 1 + 2 * h->d.batch;
     c.lengths = h->d.lengths;
     c.fused_append = fused ? 1 : 0;
     c.out = out;

@@ -15,6 +15,7 @@ import torch
 import multiquery_decode_attention_amd as kvd
 from multiquery_decode_attention_amd import inputs
 from conftest import TOL_BF16, TOL_F32, rel_err_rows
+import oracle
 from gpu_helpers import gpu_step, oracle_step, say, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -305,3 +306,43 @@ def test_timing_brackets(what):
         assert t["combine_ms"] > 0 and t["append_ms"] > 0 and t["n_append"] == 1
     else:
         assert t["combine_ms"] == 0 and t["append_ms"] == 0 and t["n_append"] == 0
+
+
+@pytest.mark.parametrize("variant", ["lds", "valu"])
+@pytest.mark.parametrize("Hq,Hkv,D", [(16, 2, 128), (96, 1, 256)])
+def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D):
+    """Several steps on one handle over a ragged batch.  From the second
+    step on, the LDS kernel dispatches the sequences in the length order the
+    previous combine sorted (and 96 heads take two head groups); every
+    step's output and appended cache must match the oracle run step by
+    step."""
+    B, T_cap, steps = 37, 512, 4
+    g = torch.Generator().manual_seed(31 + D)
+    lengths = torch.randint(1, T_cap - steps, (B,), generator=g).to(torch.int32)
+    lengths[3] = 0                      # an empty sequence
+    lengths[5] = T_cap - steps          # the longest one
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, lengths + 1, "bf16", seed=77 + D)
+    dev = torch.device("cuda")
+    kc, vc = case.k_cache.to(dev, copy=True), case.v_cache.to(dev, copy=True)
+    L = lengths.to(dev, copy=True)
+    cache = kvd.KVCache(kc, vc, L, Hq)
+    cache.set_variant(VARIANTS[variant])
+    k_ref, v_ref = inputs.host_array(case.k_cache), inputs.host_array(case.v_cache)
+    L_ref = lengths.numpy().copy()
+    try:
+        for step in range(steps):
+            gs = torch.Generator().manual_seed(1000 * step + D)
+            kn = torch.randn(B, Hkv, D, generator=gs).to(torch.bfloat16)
+            vn = torch.randn(B, Hkv, D, generator=gs).to(torch.bfloat16)
+            q = torch.randn(B, Hq, D, generator=gs).to(torch.bfloat16)
+            say(f"consecutive steps {variant} Hq={Hq} D={D}: step {step}")
+            out = cache.step(kn.to(dev), vn.to(dev), q.to(dev), scale=D ** -0.5)
+            k_ref, v_ref, L_ref, _ = oracle.append(k_ref, v_ref, L_ref, inputs.host_array(kn), inputs.host_array(vn))
+            ref = oracle.decode_attention(inputs.host_array(q), k_ref, v_ref, L_ref, D ** -0.5, oracle.BF16)
+            assert rel_err_rows(to_f64(out), ref) <= TOL_BF16, step
+        assert cache.status() == kvd.KVD_OK
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    assert np.array_equal(L.cpu().numpy(), L_ref)
+    assert np.array_equal(inputs.host_array(kc), k_ref) and np.array_equal(inputs.host_array(vc), v_ref)
