@@ -59,30 +59,16 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
     __shared__ __attribute__((aligned(16))) unsigned char lds[4 * NSW * STAGE];
     const float TAU = a.tau;
 
-    // unit = (sequence b, KV head g[, row group hg])
-    int s, hg, g, b;
-    if constexpr (!GROUPED) {
-        const BlockCoord bc = block_coord(a.B * a.Hkv);
-        s = bc.split;
-        hg = 0;
-        g = bc.unit % a.Hkv;
-        b = bc.unit / a.Hkv;
-    } else {
-        // the row groups of one (split, sequence, KV head) get blocks L,
-        // L+8, ...: one XCD, dispatched one after another, so their loads
-        // of the same tiles meet in that XCD's L2
-        const int L = (int)blockIdx.x;
-        hg = (L >> 3) % head_groups;
-        const int base = (L / (8 * head_groups)) * 8 + (L & 7);
-        const int base_units = a.B * a.Hkv;
-        if (base >= a.S * base_units) return;
-        s = base / base_units;
-        const int u = base - s * base_units;
-        g = u % a.Hkv;
-        b = u / a.Hkv;
-    }
-    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
-                                    s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
+    // unit = (sequence b, KV head g[, row group hg]), dealt to the XCDs and
+    // run longest first as in the bf16 LDS kernel; the row groups of one
+    // (split, unit) run one after another on one XCD, so their loads of the
+    // same tiles meet in that XCD's L2
+    const LdsCoord lc = lds_coord(a.S, head_groups, a.Hkv, a.B);
+    if (!lc.live) return;  // padding, before any barrier
+    const SeqAt sa = seq_at(lc.p, a.B, a.order, a.lengths);
+    const int s = lc.split, hg = lc.hg, g = lc.g, b = sa.b;
+    const int len = sequence_length_of(sa.len0, a.err, a.len_att, b, a.T_cap, false,
+                                       s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
     if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
     const int t_end = len;
@@ -412,15 +398,11 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
 template <int D, int RB, int NSW>
 hipError_t launch_rb(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 16 * RB - 1) / (16 * RB);
-    const unsigned base = (unsigned)a.S * a.B * a.Hkv;
-    const dim3 block(256);
-    if (groups == 1) {
-        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false>), dim3(base), block, 0, stream, a, 1);
-    } else {
-        // base units padded to whole rounds of the eight XCDs
-        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true>), dim3((base + 7) / 8 * 8 * groups), block, 0,
-                           stream, a, groups);
-    }
+    const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
+    if (groups == 1)
+        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false>), grid, block, 0, stream, a, 1);
+    else
+        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true>), grid, block, 0, stream, a, groups);
     return hipGetLastError();
 }
 

@@ -156,3 +156,41 @@ def test_fp8_unified_max(phi, variant):
     B, Hq, Hkv, D, T, L = SHAPES["palm_like"]
     case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=99)
     check_fp8(case, Hq, f"fp8 unified max {phi} {variant}", unified_max=phi, variant=variant)
+
+
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+def test_fp8_consecutive_steps_ragged_batch(variant):
+    """Several steps on one handle over a ragged batch: from the second step
+    on the wave kernel dispatches sequences in the length order the previous
+    combine sorted.  Each step's codes, exponents, lengths and output match
+    the oracle run step by step."""
+    B, Hq, Hkv, D, T, steps = 29, 64, 8, 128, 512, 3
+    g = torch.Generator().manual_seed(123)
+    L_att = torch.randint(1, T - steps, (B,), generator=g)
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L_att.tolist(), seed=124)
+    dev = torch.device("cuda")
+    kc, vc = case.k_codes.to(dev, copy=True), case.v_codes.to(dev, copy=True)
+    ke, ve = case.k_exp.to(dev, copy=True), case.v_exp.to(dev, copy=True)
+    L = case.lengths0.to(dev, torch.int32, copy=True)
+    cache = kvd.KVCache(kc, vc, L, Hq, k_exp=ke, v_exp=ve)
+    cache.set_variant(VARIANTS[variant])
+    r_kc, r_ke, r_vc, r_ve = (t.numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp))
+    r_L = case.lengths0.numpy().astype(np.int32)
+    try:
+        for step in range(steps):
+            gs = torch.Generator().manual_seed(500 + step)
+            kn, vn = (torch.randn(B, Hkv, D, generator=gs).to(torch.bfloat16) for _ in range(2))
+            q = torch.randn(B, Hq, D, generator=gs).to(torch.bfloat16)
+            say(f"fp8 consecutive steps {variant}: step {step}")
+            out = cache.step(kn.to(dev), vn.to(dev), q.to(dev), scale=D ** -0.5)
+            r_kc, r_ke, r_vc, r_ve, r_L, _ = oracle.append_fp8(r_kc, r_ke, r_vc, r_ve, r_L, kn.float().numpy(),
+                                                               vn.float().numpy())
+            ref = oracle.decode_attention_fp8(q.float().numpy(), r_kc, r_ke, r_vc, r_ve, r_L, D ** -0.5)
+            assert rel_err_rows(to_f64(out), ref) <= TOL_BF16, step
+        assert cache.status() == kvd.KVD_OK
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    assert np.array_equal(L.cpu().numpy(), r_L)
+    assert np.array_equal(kc.cpu().numpy(), r_kc) and np.array_equal(ke.cpu().numpy(), r_ke)
+    assert np.array_equal(vc.cpu().numpy(), r_vc) and np.array_equal(ve.cpu().numpy(), r_ve)
