@@ -294,10 +294,20 @@ def main():
                      "traffic": measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype, tq), kvariant),
                      "kernel": f"partial_{kvariant}_kernel"},
         "cpu_baseline": cpu,
+        "device": device_info(),
     }
     for c in copies:
         c["cache"].close()
     print(json.dumps(result), flush=True)
+
+
+def device_info() -> dict:
+    """The GPU the run used, as the runtime reports it (peak figures are
+    MI355X's: an arch other than gfx950 makes them meaningless)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1)}
 
 
 def calibrate_copy(mib: int, reps: int):
