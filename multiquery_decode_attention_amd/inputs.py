@@ -217,17 +217,12 @@ def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu") ->
     return Fp8Case(q, k_codes, k_exp, v_codes, v_exp, lengths0, k_new, v_new, float(D) ** -0.5)
 
 
-def make_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, seed: int,
-               spare_pages: Optional[int] = None):
-    """Lay contiguous caches [B, Hkv, T_cap, D] out as a page pool.
-
-    Block j (tokens j*P .. j*P+P-1) of sequence b goes to a distinct page
-    drawn by a seeded permutation; ``spare_pages`` more pages (default: one
-    sequence's worth) are filled with NaN and never listed.  Returns
-    (k_pages, v_pages, block_table) with pools [num_pages, Hkv, P, D] on the
-    caches' device and block_table [B, T_cap / P] int32 on the CPU.
-    """
-    B, Hkv, T_cap, D = k_cache.shape
+def paged_layout(B: int, T_cap: int, page_size: int, seed: int, spare_pages: Optional[int] = None):
+    """Seeded block table for B sequences of capacity T_cap in pages of
+    page_size tokens: block j of sequence b gets a distinct page drawn by a
+    permutation, and ``spare_pages`` more pages (default: one sequence's
+    worth) are never listed.  Returns (block_table [B, T_cap / P] int32 on
+    the CPU, num_pages)."""
     P = int(page_size)
     assert T_cap % P == 0, "capacity must be a whole number of pages"
     nb = T_cap // P
@@ -235,13 +230,35 @@ def make_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, see
     num_pages = B * nb + spare
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
     table = torch.randperm(num_pages, generator=gen)[:B * nb].view(B, nb).to(torch.int32)
-    pools = []
-    for c in (k_cache, v_cache):
-        pool = torch.full((num_pages, Hkv, P, D), float("nan"), dtype=c.dtype, device=c.device)
-        blocks = c.view(B, Hkv, nb, P, D).permute(0, 2, 1, 3, 4)  # [B, nb, Hkv, P, D]
-        pool[table.view(-1).long().to(c.device)] = blocks.reshape(B * nb, Hkv, P, D)
-        pools.append(pool)
-    return pools[0], pools[1], table
+    return table, num_pages
+
+
+def to_pages(x: torch.Tensor, table: torch.Tensor, page_size: int, num_pages: int) -> torch.Tensor:
+    """Scatter per-token rows x [B, Hkv, T_cap, ...] into a pool
+    [num_pages, Hkv, P, ...] under ``table``.  Pages no sequence lists hold
+    a poison value: NaN for floats, the E4M3 NaN code 0x7F for uint8 codes,
+    127 for int8 exponents."""
+    B, Hkv, T_cap = x.shape[:3]
+    rest = tuple(x.shape[3:])
+    P = int(page_size)
+    nb = T_cap // P
+    fill = float("nan") if x.dtype.is_floating_point else (0x7F if x.dtype == torch.uint8 else 127)
+    pool = torch.full((num_pages, Hkv, P) + rest, fill, dtype=x.dtype, device=x.device)
+    blocks = x.reshape((B, Hkv, nb, P) + rest).transpose(1, 2)  # [B, nb, Hkv, P, ...]
+    pool[table.view(-1).long().to(x.device)] = blocks.reshape((B * nb, Hkv, P) + rest)
+    return pool
+
+
+def make_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, page_size: int, seed: int,
+               spare_pages: Optional[int] = None):
+    """Lay contiguous caches [B, Hkv, T_cap, D] out as a page pool
+    (``paged_layout`` + ``to_pages``).  Returns (k_pages, v_pages,
+    block_table) with pools [num_pages, Hkv, P, D] on the caches' device and
+    block_table [B, T_cap / P] int32 on the CPU."""
+    B, Hkv, T_cap, D = k_cache.shape
+    table, num_pages = paged_layout(B, T_cap, page_size, seed, spare_pages)
+    return (to_pages(k_cache, table, page_size, num_pages), to_pages(v_cache, table, page_size, num_pages),
+            table)
 
 
 def bf16_bits(t: torch.Tensor):

@@ -330,6 +330,44 @@ def decode_attention_fp8(q, k_codes, k_exps, v_codes, v_exps, lengths, scale, **
     return decode_attention(np.asarray(q, dtype=np.float32), k32, v32, L, scale, F32, **kw)
 
 
+def append_fp8_paged(kc_pages, ke_pages, vc_pages, ve_pages, block_table, lengths, k_new, v_new):
+    """``append_fp8`` on page pools: code pools [num_pages, Hkv, P, D] uint8
+    and exponent pools [num_pages, Hkv, P] int8; slot n = lengths[b] of
+    sequence b is offset n % P of page block_table[b, n // P] (as in
+    ``append_paged``), and the capacity is max_pages * P."""
+    kc, ke = np.array(kc_pages, copy=True), np.array(ke_pages, copy=True)
+    vc, ve = np.array(vc_pages, copy=True), np.array(ve_pages, copy=True)
+    bt = np.asarray(block_table)
+    n = np.array(lengths, dtype=np.int64, copy=True)
+    P = kc.shape[2]
+    cap = bt.shape[1] * P
+    qk, ek = quantize_rows(k_new)
+    qv, ev = quantize_rows(v_new)
+    overflow = np.zeros(n.shape, dtype=bool)
+    for b in range(bt.shape[0]):
+        if n[b] >= cap:
+            overflow[b] = True
+            continue
+        page, off = int(bt[b, n[b] // P]), n[b] % P
+        kc[page, :, off, :], ke[page, :, off] = qk[b], ek[b]
+        vc[page, :, off, :], ve[page, :, off] = qv[b], ev[b]
+        n[b] += 1
+    return kc, ke, vc, ve, n.astype(np.int32), overflow
+
+
+def gather_exponent_pages(exp_pages, block_table):
+    """Contiguous exponents [B, Hkv, max_pages * P] of an exponent pool
+    [num_pages, Hkv, P] (``gather_pages`` on a trailing axis of one)."""
+    return gather_pages(np.asarray(exp_pages)[..., None], block_table)[..., 0]
+
+
+def decode_attention_fp8_paged(q, kc_pages, ke_pages, vc_pages, ve_pages, block_table, lengths, scale, **kw):
+    """``decode_attention_fp8`` over the contiguous cache the pools stand for."""
+    g = lambda x: gather_pages(x, block_table)
+    return decode_attention_fp8(q, g(kc_pages), gather_exponent_pages(ke_pages, block_table), g(vc_pages),
+                                gather_exponent_pages(ve_pages, block_table), lengths, scale, **kw)
+
+
 # --- several new tokens per sequence -----------------------------------------
 
 def append_multi(k_cache, v_cache, lengths, k_new, v_new):
