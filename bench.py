@@ -127,8 +127,8 @@ def main():
     if tq < 1 or tq > kvd.KVD_MAX_NEW_TOKENS or (tq > 1 and fp8):
         print(f"--new-tokens must be 1..{kvd.KVD_MAX_NEW_TOKENS} (1 with --kv-dtype fp8)", file=sys.stderr)
         sys.exit(2)
-    if fp8 and (args.page_size or w.dtype != "bf16"):
-        print("--kv-dtype fp8 takes a bf16 workload and a contiguous cache", file=sys.stderr)
+    if fp8 and w.dtype != "bf16":
+        print("--kv-dtype fp8 takes a bf16 workload", file=sys.stderr)
         sys.exit(2)
     kv_bytes_one = (traffic.kv_read_bytes_fp8(w.Hkv, w.D, [w.T_cap] * w.B) if fp8 else
                     traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, [w.T_cap] * w.B))
@@ -153,8 +153,18 @@ def main():
         if fp8:
             case = inputs.make_fp8_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, seed=w.seed + 1000 * r,
                                         device=dev)
-            cache = kvd.KVCache(case.k_codes, case.v_codes, case.lengths0, w.Hq, k_exp=case.k_exp,
-                                v_exp=case.v_exp)
+            if args.page_size:
+                # codes and exponents in shuffled pages under one block table
+                bt, num_pages = inputs.paged_layout(w.B, T_cap, args.page_size, seed=w.seed + 1000 * r + 1)
+                keep = {n: inputs.to_pages(x, bt, args.page_size, num_pages)
+                        for n, x in (("kc", case.k_codes), ("ke", case.k_exp), ("vc", case.v_codes),
+                                     ("ve", case.v_exp))}
+                keep["block_table"] = bt.to(dev)
+                cache = kvd.KVCache(keep["kc"], keep["vc"], case.lengths0, w.Hq, block_table=keep["block_table"],
+                                    k_exp=keep["ke"], v_exp=keep["ve"])
+            else:
+                cache = kvd.KVCache(case.k_codes, case.v_codes, case.lengths0, w.Hq, k_exp=case.k_exp,
+                                    v_exp=case.v_exp)
         elif tq > 1:
             case = inputs.make_multi_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended - tq, tq, w.dtype,
                                           seed=w.seed + 1000 * r, device=dev)

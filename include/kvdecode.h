@@ -172,9 +172,9 @@ typedef struct {
  * an all-zero row) and each value becomes the code nearest to x * 2^-e
  * (ties to the even code).  Attention reads code * 2^e: exact in bf16 for
  * every e that keeps the values within bf16's normal range.  Callers that
- * write the cache themselves (prefill) must follow the same format.
- * Contiguous caches only; the partial pass runs on the LDS kernel
- * (KVD_VARIANT_AUTO or KVD_VARIANT_LDS).
+ * write the cache themselves (prefill) must follow the same format.  The
+ * partial pass runs on the fp8 WAVE or LDS kernel (kvdecode_set_variant);
+ * kvdecode_create_fp8_paged takes the same format in page pools.
  */
 typedef struct {
     kvdecode_desc_t cache; /* dtype KVD_FP8_E4M3; caches hold the codes              */
@@ -190,6 +190,25 @@ typedef struct {
  * KVD_EUNSUPPORTED for dtype KVD_FP8_E4M3.
  */
 int32_t kvdecode_create_fp8(const kvdecode_fp8_desc_t* desc, kvdecode_t* out);
+
+/*
+ * fp8 cache in page pools: the paged layout of kvdecode_create_paged (codes
+ * in the pools, token t of sequence b at row (block_table[b][t / P] * Hkv +
+ * g) * P + t mod P) with the exponents in pools of the same shape without
+ * the last axis, so a token's exponent sits at the same row index.  Paging
+ * after "All About Transformer Inference" (tricks for generation
+ * throughput: paged attention), the format as for kvdecode_create_fp8.
+ * Validation as for kvdecode_create_paged, KVD_EUNSUPPORTED unless dtype is
+ * KVD_FP8_E4M3, KVD_EINVAL / KVD_EALIGN for a null or unaligned exponent
+ * pool.
+ */
+typedef struct {
+    kvdecode_paged_desc_t pages; /* dtype KVD_FP8_E4M3; the pools hold the codes        */
+    int8_t* k_exp;               /* [num_pages, Hkv, page_size] key-row exponents      */
+    int8_t* v_exp;               /* [num_pages, Hkv, page_size] value-row exponents    */
+} kvdecode_fp8_paged_desc_t;
+
+int32_t kvdecode_create_fp8_paged(const kvdecode_fp8_paged_desc_t* desc, kvdecode_t* out);
 
 /*
  * Create a handle over a caller-owned paged cache.  Same validation and

@@ -23,7 +23,7 @@ __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KVD_VARIANT_WAVE", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
-    "kvdecode_create_fp8",
+    "kvdecode_create_fp8", "kvdecode_create_fp8_paged", "kvdecode_fp8_paged_desc_t",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
     "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
     "KVD_TIME_APPEND", "KVD_TIME_ALL",
@@ -45,7 +45,8 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
                                                          "libkvdecode.so")
 
 EXPORTS = (
-    "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_append", "kvdecode_attend",
+    "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_create_fp8_paged",
+    "kvdecode_append", "kvdecode_attend",
     "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
@@ -87,6 +88,10 @@ class kvdecode_fp8_desc_t(ctypes.Structure):
     _fields_ = [("cache", kvdecode_desc_t), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
 
 
+class kvdecode_fp8_paged_desc_t(ctypes.Structure):
+    _fields_ = [("pages", kvdecode_paged_desc_t), ("k_exp", ctypes.c_void_p), ("v_exp", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -104,6 +109,7 @@ def library():
         "kvdecode_create": (I, [ctypes.POINTER(kvdecode_desc_t), ctypes.POINTER(P)]),
         "kvdecode_create_paged": (I, [ctypes.POINTER(kvdecode_paged_desc_t), ctypes.POINTER(P)]),
         "kvdecode_create_fp8": (I, [ctypes.POINTER(kvdecode_fp8_desc_t), ctypes.POINTER(P)]),
+        "kvdecode_create_fp8_paged": (I, [ctypes.POINTER(kvdecode_fp8_paged_desc_t), ctypes.POINTER(P)]),
         "kvdecode_append": (I, [P, P, P, P]),
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
@@ -226,6 +232,37 @@ def kvdecode_create_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, block_ta
     return h.value
 
 
+def kvdecode_create_fp8_paged(k_pages: torch.Tensor, v_pages: torch.Tensor, k_exp: torch.Tensor,
+                              v_exp: torch.Tensor, block_table: torch.Tensor, lengths: torch.Tensor,
+                              num_q_heads: int) -> int:
+    """Handle over an fp8 cache in page pools: E4M3 code pools
+    [num_pages, Hkv, page_size, d] uint8, exponent pools [num_pages, Hkv,
+    page_size] int8, block table [B, max_pages] int32, lengths [B] int32."""
+    for t in (k_pages, v_pages):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.uint8:
+            raise ValueError("fp8 page pools must be contiguous uint8 [num_pages, Hkv, page_size, d] tensors")
+    if k_pages.shape != v_pages.shape:
+        raise ValueError("k and v pools must match in shape")
+    for t in (k_exp, v_exp):
+        if t.dtype != torch.int8 or tuple(t.shape) != tuple(k_pages.shape[:3]) or not t.is_contiguous():
+            raise ValueError("exponent pools must be contiguous int8 [num_pages, Hkv, page_size] tensors")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] tensor")
+    B = block_table.shape[0]
+    if lengths.dtype != torch.int32 or lengths.dim() != 1 or lengths.shape[0] != B:
+        raise ValueError("lengths must be an int32 [B] tensor")
+    if not all(t.is_cuda for t in (k_pages, v_pages, k_exp, v_exp, block_table, lengths)):
+        raise ValueError("pools, exponents, block table and lengths must be device tensors")
+    num_pages, Hkv, page_size, D = k_pages.shape
+    desc = kvdecode_fp8_paged_desc_t(
+        kvdecode_paged_desc_t(B, num_q_heads, Hkv, D, page_size, num_pages, block_table.shape[1], KVD_FP8_E4M3,
+                              k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), lengths.data_ptr()),
+        k_exp.data_ptr(), v_exp.data_ptr())
+    h = ctypes.c_void_p()
+    _check(library().kvdecode_create_fp8_paged(ctypes.byref(desc), ctypes.byref(h)), "kvdecode_create_fp8_paged")
+    return h.value
+
+
 def kvdecode_append(h: int, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
     _check(library().kvdecode_append(h, _ptr(k_new), _ptr(v_new), _stream_ptr(stream)),
            "kvdecode_append")
@@ -323,13 +360,20 @@ class KVCache:
         """Contiguous caches [B, Hkv, T_cap, d]; or -- with ``block_table``
         [B, max_pages] -- page pools [num_pages, Hkv, page_size, d]; or --
         with ``k_exp``/``v_exp`` [B, Hkv, T_cap] int8 -- an fp8 cache of
-        uint8 E4M3 codes, whose queries and outputs are bf16."""
+        uint8 E4M3 codes, whose queries and outputs are bf16 (with both, fp8
+        page pools and exponent pools [num_pages, Hkv, page_size])."""
         self.k_cache, self.v_cache, self.lengths = k_cache, v_cache, lengths
         self.block_table = block_table
         self.k_exp, self.v_exp = k_exp, v_exp
         self.Hq = num_q_heads
         self.dtype = torch.bfloat16 if k_exp is not None else k_cache.dtype
-        if k_exp is not None:
+        if k_exp is not None and block_table is not None:
+            _, self.Hkv, page_size, self.D = k_cache.shape
+            self.B = block_table.shape[0]
+            self.T_cap = block_table.shape[1] * page_size
+            self.handle = kvdecode_create_fp8_paged(k_cache, v_cache, k_exp, v_exp, block_table, lengths,
+                                                    num_q_heads)
+        elif k_exp is not None:
             self.B, self.Hkv, self.T_cap, self.D = k_cache.shape
             self.handle = kvdecode_create_fp8(k_cache, v_cache, k_exp, v_exp, lengths, num_q_heads)
         elif block_table is None:

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint16_t* __restr
                                                          uint8_t* __restrict__ v_cache,
                                                          int8_t* __restrict__ k_exp,
                                                          int8_t* __restrict__ v_exp,
-                                                         int32_t* __restrict__ lengths,
+                                                         KvLayout kvl, int32_t* __restrict__ lengths,
                                                          int* __restrict__ err, int Hkv, int T_cap) {
     constexpr int PER = D / 64;  // values per lane
     const int b = blockIdx.x;
@@ -114,10 +114,13 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint16_t* __restr
         if (threadIdx.x == 0) atomicOr(err, n < 0 ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
         return;
     }
+    // page of the slot (paged pools; a bad entry writes page 0 and is flagged)
+    const int page = kvl.block_table ? kv_page(kvl, b, n >> kvl.page_shift, err) : 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int g = wave; g < Hkv; g += 4) {
         const size_t src = ((size_t)b * Hkv + g) * D;
-        const size_t row = kv_row_contiguous(b, g, Hkv, T_cap, n);
+        // the exponent of a row sits at the row's index in the exponent array
+        const size_t row = kvl.block_table ? kv_row_paged(kvl, page, g, Hkv, n) : kv_row_contiguous(b, g, Hkv, T_cap, n);
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
             const uint16_t* x = (kv ? v_new : k_new) + src;
@@ -145,12 +148,12 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint16_t* __restr
 }  // namespace
 
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                             int8_t* k_exp, int8_t* v_exp, int32_t* lengths, int* err, int B,
-                             int Hkv, int D, int T_cap, hipStream_t stream) {
+                             int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
+                             int B, int Hkv, int D, int T_cap, hipStream_t stream) {
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(B), dim3(256), 0, stream, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), static_cast<uint8_t*>(k_cache),
-                           static_cast<uint8_t*>(v_cache), k_exp, v_exp, lengths, err, Hkv, T_cap);
+                           static_cast<uint8_t*>(v_cache), k_exp, v_exp, kv, lengths, err, Hkv, T_cap);
     };
     switch (D) {
         case 64: go(append_fp8_kernel<64>); break;

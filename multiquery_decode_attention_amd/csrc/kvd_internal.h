@@ -310,10 +310,11 @@ inline int wave_fp8_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
-// Quantize the new token's bf16 K/V rows into slot lengths[b] and advance it.
+// Quantize the new token's bf16 K/V rows into slot lengths[b] (contiguous
+// or paged, the exponent at the row's index) and advance it.
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                             int8_t* k_exp, int8_t* v_exp, int32_t* lengths, int* err, int B,
-                             int Hkv, int D, int T_cap, hipStream_t stream);
+                             int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
+                             int B, int Hkv, int D, int T_cap, hipStream_t stream);
 
 
 // Waves per work unit of the MFMA partial pass for group size M.

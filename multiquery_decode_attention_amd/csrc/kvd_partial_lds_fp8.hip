@@ -35,7 +35,7 @@ using namespace mfma;
 using namespace lds;
 using namespace fp8;
 
-template <int D, int NS>
+template <int D, int NS, bool PAGED>
 __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int head_groups) {
     constexpr int CH = D / 16;                   // 16-byte chunks per row of codes
     constexpr int SWZ = CH - 1;                  // K chunk swizzle mask
@@ -51,13 +51,13 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     static_assert(NS >= 2 && NS - 2 <= 6 && (NS - 2) * PERW < 64, "ring depth");
     __shared__ __attribute__((aligned(16))) unsigned char lds[NS * STAGE];
 
-    const BlockCoord bc = block_coord(a.B * a.Hkv * head_groups);
-    const int s = bc.split;
-    const int hg = bc.unit % head_groups;
-    const int g = (bc.unit / head_groups) % a.Hkv;
-    const int b = bc.unit / (head_groups * a.Hkv);
-    const int len = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, false,
-                                    s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
+    // units dealt to the XCDs and run longest first, as in the bf16 kernel
+    const LdsCoord lc = lds_coord(a.S, head_groups, a.Hkv, a.B);
+    if (!lc.live) return;  // padding, before any barrier
+    const SeqAt sa = seq_at(lc.p, a.B, a.order, a.lengths);
+    const int s = lc.split, hg = lc.hg, g = lc.g, b = sa.b;
+    const int len = sequence_length_of(sa.len0, a.err, a.len_att, b, a.T_cap, false,
+                                       s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
     if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
     const int t_end = len;
@@ -77,11 +77,33 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;
 
-    const size_t slab = kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
+    // Rows are counted from kb/vb (codes) and ke/ve (exponents, one byte
+    // per row): the (b, g) slab of a contiguous cache, or the page pools.
+    const size_t slab = PAGED ? 0 : kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
     const char* kb = static_cast<const char*>(a.k_cache) + slab * D;
     const char* vb = static_cast<const char*>(a.v_cache) + slab * D;
     const char* ke = reinterpret_cast<const char*>(a.k_exp) + slab;
     const char* ve = reinterpret_cast<const char*>(a.v_exp) + slab;
+    // Paged: every wave issues the stages in order and fetches the page of
+    // its next tile while issuing the current one (block table through the
+    // constant address space, as in the bf16 kernel).
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr bt_row = PAGED ? (const_i32_ptr)(a.kv.block_table + (size_t)b * a.kv.max_pages) : nullptr;
+    int next_entry = 0;
+    if constexpr (PAGED) next_entry = bt_row[t_first >> a.kv.page_shift];
+    auto tile_row = [&](int st, int t0) -> size_t {
+        if constexpr (!PAGED) {
+            return (size_t)t0;
+        } else {
+            int page = next_entry;
+            if (st + 1 < n_tiles) next_entry = bt_row[(t0 + tstride) >> a.kv.page_shift];
+            if ((unsigned)page >= (unsigned)a.kv.num_pages) {
+                if (threadIdx.x % 64 == 0) atomicOr(a.err, ERRBIT_PAGE);
+                page = 0;
+            }
+            return kv_row_paged(a.kv, page, g, a.Hkv, t0);
+        }
+    };
 
     // Queries (bf16), as in the bf16 kernel: lanes past the wave's last head
     // load a copy of its last row.
@@ -126,7 +148,8 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
             return;
         }
         const int t0 = t_first + st * tstride;
-        const char* base = tbase + (size_t)t0 * D;
+        const size_t r0 = tile_row(st, t0);
+        const char* base = tbase + r0 * D;
         if (t0 + MFMA_TILE <= t_end) {
 #pragma unroll
             for (int n = 0; n < PERWD; ++n) {
@@ -144,7 +167,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
                                                  (lds_void_t*)(stage + j0 * 16), 16, 0, 2);
             }
         }
-        const char* xsrc = (xl < 2 ? ke : ve) + t0 + 16 * (xl & 1);
+        const char* xsrc = (xl < 2 ? ke : ve) + r0 + 16 * (xl & 1);
         __builtin_amdgcn_global_load_lds((const void*)xsrc, (lds_void_t*)(stage + 2 * REGION), 16, 0, 0);
     };
 
@@ -292,8 +315,13 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
 template <int D>
 hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 63) / 64;
-    dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
-    hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D)>), grid, dim3(256), 0, stream, a, groups);
+    const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B));
+    if (a.kv.block_table)
+        hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D), true>), grid, dim3(256), 0, stream, a,
+                           groups);
+    else
+        hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D), false>), grid, dim3(256), 0, stream, a,
+                           groups);
     return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ using namespace mfma;
 using namespace lds;
 using namespace fp8;
 
-template <int D, int RB, int NSW, bool GROUPED>
+template <int D, int RB, int NSW, bool GROUPED, bool PAGED>
 __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, int head_groups) {
     constexpr int CH = D / 16;                 // 16-byte chunks per row of codes
     constexpr int SWZ = CH - 1;                // K chunk swizzle mask
@@ -82,11 +82,41 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
     const int n_my = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;  // this wave's tiles
     const int mg = min(a.M - hg * ROWS, ROWS);                        // rows of the group
 
-    const size_t slab = kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
+    // Rows below are counted from kb/vb (codes) and ke/ve (exponents, one
+    // byte per row): the (b, g) slab of a contiguous cache, or the start of
+    // the page pools.
+    const size_t slab = PAGED ? 0 : kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
     const char* kb = static_cast<const char*>(a.k_cache) + slab * D;
     const char* vb = static_cast<const char*>(a.v_cache) + slab * D;
     const char* ke = reinterpret_cast<const char*>(a.k_exp) + slab;
     const char* ve = reinterpret_cast<const char*>(a.v_exp) + slab;
+    // Paged: the wave issues its tiles in order, so the page of its next
+    // tile is fetched while the current one is issued; the block table is
+    // read through the constant address space (scalar loads, tracked apart
+    // from the direct loads in flight), and an entry is range-checked when
+    // used (outside the pool: page 0, flagged).
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const const_i32_ptr bt_row = PAGED ? (const_i32_ptr)(a.kv.block_table + (size_t)b * a.kv.max_pages) : nullptr;
+    auto tile_t0 = [&](int k) { return t_first + (wave + 4 * k) * tstride; };
+    int next_entry = 0;
+    if constexpr (PAGED) {
+        if (n_my > 0) next_entry = bt_row[tile_t0(0) >> a.kv.page_shift];
+    }
+    // first row of the wave's tile k (its 32 rows are consecutive: pages
+    // hold whole tiles); called for k = 0, 1, ... in order
+    auto tile_row = [&](int k, int t0) -> size_t {
+        if constexpr (!PAGED) {
+            return (size_t)t0;
+        } else {
+            int page = next_entry;
+            if (k + 1 < n_my) next_entry = bt_row[tile_t0(k + 1) >> a.kv.page_shift];
+            if ((unsigned)page >= (unsigned)a.kv.num_pages) {
+                if (threadIdx.x % 64 == 0) atomicOr(a.err, ERRBIT_PAGE);
+                page = 0;
+            }
+            return kv_row_paged(a.kv, page, g, a.Hkv, t0);
+        }
+    };
 
     // Queries of every row block: B operands of the score product.  Lanes
     // past the group's last row load a copy of it (never stored).
@@ -126,9 +156,10 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
             __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)(stage + 2 * REGION), 16, 0, 0);
             return;
         }
-        const int t0 = t_first + (wave + 4 * k) * tstride;
-        const char* kt = kb + (size_t)t0 * D;
-        const char* vt = vb + (size_t)t0 * D;
+        const int t0 = tile_t0(k);
+        const size_t r0 = tile_row(k, t0);
+        const char* kt = kb + r0 * D;
+        const char* vt = vb + r0 * D;
         if (t0 + MFMA_TILE <= t_end) {
 #pragma unroll
             for (int n = 0; n < PERC; ++n)
@@ -157,9 +188,9 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
             }
         }
         // lane l: K exponents of tokens 16(l&1).. for (l&3) < 2, else V
-        // exponents, at byte 16 l: bytes 0-31 K, 32-63 V (T_cap is a
-        // multiple of the tile, so all 32 lie inside the cache row)
-        __builtin_amdgcn_global_load_lds((const void*)((xl < 2 ? ke : ve) + t0 + 16 * (xl & 1)),
+        // exponents, at byte 16 l: bytes 0-31 K, 32-63 V (T_cap, and a page,
+        // is a multiple of the tile, so all 32 lie inside the cache row)
+        __builtin_amdgcn_global_load_lds((const void*)((xl < 2 ? ke : ve) + r0 + 16 * (xl & 1)),
                                          (lds_void_t*)(stage + 2 * REGION), 16, 0, 0);
     };
 
@@ -205,7 +236,7 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
             const unsigned char* Kl = ring + (it % NSW) * STAGE;
             const unsigned char* Vl = Kl + REGION;
             const signed char* X = reinterpret_cast<const signed char*>(Kl + 2 * REGION);
-            const int t0 = t_first + (wave + 4 * it) * tstride;
+            const int t0 = tile_t0(it);
 
             // scores of every row block: K rows c and 16+c widened once,
             // with their own 2^e
@@ -399,10 +430,19 @@ template <int D, int RB, int NSW>
 hipError_t launch_rb(const PartialArgs& a, hipStream_t stream) {
     const int groups = (a.M + 16 * RB - 1) / (16 * RB);
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
-    if (groups == 1)
-        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false>), grid, block, 0, stream, a, 1);
-    else
-        hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true>), grid, block, 0, stream, a, groups);
+    const bool paged = a.kv.block_table != nullptr;
+    if (groups == 1) {
+        if (paged)
+            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false, true>), grid, block, 0, stream, a, 1);
+        else
+            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false, false>), grid, block, 0, stream, a, 1);
+    } else {
+        if (paged)
+            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true, true>), grid, block, 0, stream, a, groups);
+        else
+            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true, false>), grid, block, 0, stream, a,
+                               groups);
+    }
     return hipGetLastError();
 }
 

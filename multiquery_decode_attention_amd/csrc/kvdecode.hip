@@ -260,7 +260,7 @@ int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new,
     const bool timed = (h->timing_what & KVD_TIME_APPEND) && h->timing_cap > 0 && h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
     hipError_t e =
-        is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp,
+        is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp, h->kv,
                                            h->d.lengths, h->err, h->d.batch, h->d.num_kv_heads,
                                            h->d.head_dim, h->d.capacity, st)
                   : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths,
@@ -442,31 +442,58 @@ int32_t kvdecode_create_fp8(const kvdecode_fp8_desc_t* desc, kvdecode_t* out) {
     return rc;
 }
 
-int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out) {
-    if (!desc || !out) return KVD_EINVAL;
-    *out = nullptr;
-    const kvdecode_paged_desc_t& p = *desc;
+// The contiguous-equivalent descriptor and block-table layout of a paged
+// descriptor, validated (dtype aside).
+int32_t paged_desc(const kvdecode_paged_desc_t& p, kvdecode_desc_t* d, kvd::KvLayout* kv) {
     if (p.page_size < 32 || p.page_size > 65536 || (p.page_size & (p.page_size - 1))) return KVD_EINVAL;
     if (p.num_pages < 1 || p.max_pages < 1 || p.num_kv_heads < 1) return KVD_EINVAL;
     if ((long long)p.max_pages * p.page_size > (1 << 24)) return KVD_EINVAL;
     // every row index of the pool fits the kernels' 32-bit row arithmetic
     if ((long long)p.num_pages * p.num_kv_heads * p.page_size > (1LL << 31)) return KVD_EINVAL;
     if (!p.block_table) return KVD_EINVAL;
-    if (p.dtype == KVD_FP8_E4M3) return KVD_EUNSUPPORTED;  // fp8 caches are contiguous
     if (reinterpret_cast<uintptr_t>(p.block_table) & 3u) return KVD_EALIGN;
-    kvdecode_desc_t d;
-    d.batch = p.batch;
-    d.num_q_heads = p.num_q_heads;
-    d.num_kv_heads = p.num_kv_heads;
-    d.head_dim = p.head_dim;
-    d.capacity = p.max_pages * p.page_size;
-    d.dtype = p.dtype;
-    d.k_cache = p.k_pages;
-    d.v_cache = p.v_pages;
-    d.lengths = p.lengths;
+    d->batch = p.batch;
+    d->num_q_heads = p.num_q_heads;
+    d->num_kv_heads = p.num_kv_heads;
+    d->head_dim = p.head_dim;
+    d->capacity = p.max_pages * p.page_size;
+    d->dtype = p.dtype;
+    d->k_cache = p.k_pages;
+    d->v_cache = p.v_pages;
+    d->lengths = p.lengths;
     int shift = 0;
     while ((1 << shift) < p.page_size) ++shift;
-    return make_handle(d, kvd::KvLayout{p.block_table, shift, p.max_pages, p.num_pages}, out);
+    *kv = kvd::KvLayout{p.block_table, shift, p.max_pages, p.num_pages};
+    return KVD_OK;
+}
+
+int32_t kvdecode_create_paged(const kvdecode_paged_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    *out = nullptr;
+    kvdecode_desc_t d;
+    kvd::KvLayout kv;
+    const int32_t rc = paged_desc(*desc, &d, &kv);
+    if (rc != KVD_OK) return rc;
+    if (d.dtype == KVD_FP8_E4M3) return KVD_EUNSUPPORTED;  // kvdecode_create_fp8_paged
+    return make_handle(d, kv, out);
+}
+
+int32_t kvdecode_create_fp8_paged(const kvdecode_fp8_paged_desc_t* desc, kvdecode_t* out) {
+    if (!desc || !out) return KVD_EINVAL;
+    *out = nullptr;
+    kvdecode_desc_t d;
+    kvd::KvLayout kv;
+    int32_t rc = paged_desc(desc->pages, &d, &kv);
+    if (rc != KVD_OK) return rc;
+    if (d.dtype != KVD_FP8_E4M3) return KVD_EUNSUPPORTED;
+    if (!desc->k_exp || !desc->v_exp) return KVD_EINVAL;
+    if (!aligned16(desc->k_exp) || !aligned16(desc->v_exp)) return KVD_EALIGN;
+    rc = make_handle(d, kv, out);
+    if (rc == KVD_OK) {
+        (*out)->k_exp = desc->k_exp;
+        (*out)->v_exp = desc->v_exp;
+    }
+    return rc;
 }
 
 int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void* stream) {

@@ -271,3 +271,38 @@ def test_fp8_handle(lib):
     assert rc == kvd.KVD_EUNSUPPORTED and not h2
     rc, h3 = create_paged(lib, make_paged_desc(dtype=kvd.KVD_FP8_E4M3))
     assert rc == kvd.KVD_EUNSUPPORTED and not h3
+
+
+def make_fp8_paged_desc(**kw):
+    exps = dict(k_exp=FAKE * 5, v_exp=FAKE * 6)
+    pages = dict(dtype=kvd.KVD_FP8_E4M3)
+    for k, v in kw.items():
+        (exps if k in exps else pages)[k] = v
+    return kvd.kvdecode_fp8_paged_desc_t(make_paged_desc(**pages), exps["k_exp"], exps["v_exp"])
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("page_size", 16, kvd.KVD_EINVAL), ("num_pages", 0, kvd.KVD_EINVAL),
+    ("block_table", FAKE + 2, kvd.KVD_EALIGN), ("k_exp", 0, kvd.KVD_EINVAL),
+    ("v_exp", FAKE + 4, kvd.KVD_EALIGN), ("dtype", kvd.KVD_BF16, kvd.KVD_EUNSUPPORTED),
+    ("head_dim", 96, kvd.KVD_EUNSUPPORTED),
+])
+def test_create_fp8_paged_rejects(lib, field, value, code):
+    h = ctypes.c_void_p()
+    rc = lib.kvdecode_create_fp8_paged(ctypes.byref(make_fp8_paged_desc(**{field: value})), ctypes.byref(h))
+    assert rc == code and not h.value
+
+
+def test_fp8_paged_handle(lib):
+    h = ctypes.c_void_p()
+    assert lib.kvdecode_create_fp8_paged(ctypes.byref(make_fp8_paged_desc()), ctypes.byref(h)) == kvd.KVD_OK
+    p = kvd.kvdecode_get_plan(h.value)
+    assert p["variant"] == "wave" and p["num_splits"] * p["split_tokens"] >= 4 * 64
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_LDS) == kvd.KVD_OK
+    for v in (kvd.KVD_VARIANT_VALU, kvd.KVD_VARIANT_MFMA):
+        assert lib.kvdecode_set_variant(h.value, v) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
+    # the fp8 dtype needs the fp8 create call, and that call the fp8 dtype
+    rc, h2 = create_paged(lib, make_paged_desc(dtype=kvd.KVD_FP8_E4M3))
+    assert rc == kvd.KVD_EUNSUPPORTED and not h2
+    assert lib.kvdecode_create_fp8_paged(None, ctypes.byref(ctypes.c_void_p())) == kvd.KVD_EINVAL

@@ -194,3 +194,92 @@ def test_fp8_consecutive_steps_ragged_batch(variant):
     assert np.array_equal(L.cpu().numpy(), r_L)
     assert np.array_equal(kc.cpu().numpy(), r_kc) and np.array_equal(ke.cpu().numpy(), r_ke)
     assert np.array_equal(vc.cpu().numpy(), r_vc) and np.array_equal(ve.cpu().numpy(), r_ve)
+
+
+def fp8_paged_step(case, Hq, page_size, *, variant="wave", seed=5, fused=True, table_edit=None):
+    """One step on fresh device copies of an fp8 case laid out in pages
+    (codes and exponents under one seeded block table).  Returns (out,
+    pools [kc, ke, vc, ve] after the step, pools before, table, lengths,
+    status, plan)."""
+    dev = torch.device("cuda")
+    B, Hkv, T = case.k_codes.shape[:3]
+    table, num_pages = inputs.paged_layout(B, T, page_size, seed)
+    pools = [inputs.to_pages(x, table, page_size, num_pages) for x in (case.k_codes, case.k_exp, case.v_codes,
+                                                                         case.v_exp)]
+    before = [p.numpy().copy() for p in pools]
+    kc, ke, vc, ve = (p.to(dev, copy=True) for p in pools)
+    bt = table.clone()
+    if table_edit is not None:  # the device's table only; the pools keep the layout of `table`
+        table_edit(bt)
+    bt = bt.to(dev)
+    L = case.lengths0.to(dev, torch.int32, copy=True)
+    cache = kvd.KVCache(kc, vc, L, Hq, block_table=bt, k_exp=ke, v_exp=ve)
+    try:
+        cache.set_variant(VARIANTS[variant])
+        plan = cache.plan()
+        kn, vn, q = (t.to(dev).contiguous() for t in (case.k_new, case.v_new, case.q))
+        if fused:
+            out = cache.step(kn, vn, q, scale=case.scale)
+        else:
+            cache.append(kn, vn)
+            out = cache.attend(q, scale=case.scale)
+        status = cache.status()
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    after = [t.cpu().numpy() for t in (kc, ke, vc, ve)]
+    return out, after, before, table.numpy(), L.cpu().numpy(), status, plan
+
+
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("name,page", [("ragged_gqa_like", 64), ("mha_like", 256), ("palm_like", 128),
+                                       ("gqa48_d128", 32), ("small_d64", 32)])
+def test_fp8_paged(name, page, variant):
+    """fp8 codes and exponents in shuffled pages: the append (through the
+    block table) is bit-exact on every pool, spare pages included, and the
+    attention matches the oracle over the gathered cache."""
+    B, Hq, Hkv, D, T, L = SHAPES[name]
+    if variant == "wave" and D < 128:
+        pytest.skip("the wave kernel needs d >= 128")
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=130 + len(name))
+    say(f"fp8 paged {name} page={page} {variant}")
+    out, after, before, bt, L_gpu, status, plan = fp8_paged_step(case, Hq, page, variant=variant)
+    assert plan["variant"] == variant
+    kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8_paged(*before, bt, case.lengths0.numpy(),
+                                                        case.k_new.float().numpy(), case.v_new.float().numpy())
+    assert status == kvd.KVD_OK
+    assert np.array_equal(L_gpu, L2)
+    for got, want, what in zip(after, (kc2, ke2, vc2, ve2), ("K codes", "K exponents", "V codes", "V exponents")):
+        assert np.array_equal(got, want), what
+    ref = oracle.decode_attention_fp8_paged(case.q.float().numpy(), kc2, ke2, vc2, ve2, bt, L2, case.scale)
+    err = rel_err_rows(to_f64(out), ref)
+    say(f"fp8 paged {name}: max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+
+
+def test_fp8_paged_equals_contiguous_bitwise():
+    """Same plan, same arithmetic: the paged step's output equals the
+    contiguous step's bit for bit."""
+    B, Hq, Hkv, D, T, L = SHAPES["ragged_gqa_like"]
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=140)
+    out_c, *_ = fp8_step(case, Hq, variant="wave")
+    out_p, *_ = fp8_paged_step(case, Hq, 64, variant="wave")
+    assert torch.equal(out_c.cpu().view(torch.int16), out_p.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+def test_fp8_paged_bad_entry_is_reported(variant):
+    """A block-table entry in use outside the pool reads page 0 (memory
+    safe) and is reported; the other sequences are unaffected."""
+    case = inputs.make_fp8_case(2, 8, 1, 128, 128, [100, 70], seed=141)
+
+    def corrupt(table):
+        table[0, 1] = 10_000  # tokens 32..63 of sequence 0
+
+    out, after, before, bt, L_gpu, status, plan = fp8_paged_step(case, 8, 32, variant=variant, table_edit=corrupt)
+    assert status == kvd.KVD_EPAGE
+    # (the table returned is the pools' layout; only sequence 0 read the bad entry)
+    kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8_paged(*before, bt, case.lengths0.numpy(),
+                                                        case.k_new.float().numpy(), case.v_new.float().numpy())
+    ref = oracle.decode_attention_fp8_paged(case.q.float().numpy(), kc2, ke2, vc2, ve2, bt, L2, case.scale)
+    assert rel_err_rows(to_f64(out)[1:], ref[1:]) <= TOL_BF16
