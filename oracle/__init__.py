@@ -407,3 +407,38 @@ def decode_attention_multi(q, k_cache, v_cache, lengths, appended, scale, dtype,
         out[:, :, i, :] = decode_attention(np.ascontiguousarray(q[:, :, i, :]), k_cache, v_cache, Li, scale,
                                            dtype, **kw)
     return out
+
+
+# --- fp8 cache, several new tokens per sequence -------------------------------
+
+def append_fp8_multi(k_codes, k_exps, v_codes, v_exps, lengths, k_new, v_new):
+    """``append_multi`` on an fp8 cache: every new row of k_new, v_new
+    [B, Hkv, T_q, D] (any float array) is quantized (``quantize_rows``) into
+    slots lengths[b] .. lengths[b] + T_q - 1; a sequence they do not fit is
+    left unchanged.  Returns (k_codes', k_exps', v_codes', v_exps', lengths',
+    appended) with appended[b] = T_q or 0."""
+    kc, ke = np.array(k_codes, copy=True), np.array(k_exps, copy=True)
+    vc, ve = np.array(v_codes, copy=True), np.array(v_exps, copy=True)
+    n = np.array(lengths, dtype=np.int64, copy=True)
+    T_cap = kc.shape[2]
+    T_q = np.asarray(k_new).shape[2]
+    qk, ek = quantize_rows(k_new)
+    qv, ev = quantize_rows(v_new)
+    appended = np.zeros(n.shape, dtype=np.int32)
+    for b in range(kc.shape[0]):
+        if n[b] < 0 or T_cap - n[b] < T_q:  # no room for all T_q rows
+            continue
+        for i in range(T_q):
+            kc[b, :, n[b] + i, :], ke[b, :, n[b] + i] = qk[b, :, i], ek[b, :, i]
+            vc[b, :, n[b] + i, :], ve[b, :, n[b] + i] = qv[b, :, i], ev[b, :, i]
+        n[b] += T_q
+        appended[b] = T_q
+    return kc, ke, vc, ve, n.astype(np.int32), appended
+
+
+def decode_attention_fp8_multi(q, k_codes, k_exps, v_codes, v_exps, lengths, appended, scale, **kw):
+    """``decode_attention_multi`` over the dequantized fp8 cache; q
+    [B, Hq, T_q, D] float32 (bf16 queries widened exactly)."""
+    k = dequantize(k_codes, k_exps).astype(np.float32)
+    v = dequantize(v_codes, v_exps).astype(np.float32)
+    return decode_attention_multi(np.asarray(q, dtype=np.float32), k, v, lengths, appended, scale, F32, **kw)

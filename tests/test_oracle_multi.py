@@ -104,3 +104,85 @@ def test_multi_mutant_is_caught(name, monkeypatch):
             except (AssertionError, IndexError, ValueError):
                 failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
+
+
+# --- fp8 cache ------------------------------------------------------------------
+
+def _fp8_cache(rng, B, Hkv, T, D):
+    codes = [rng.integers(0, 0x7E, (B, Hkv, T, D)).astype(np.uint8) for _ in range(2)]
+    exps = [rng.integers(-9, -4, (B, Hkv, T)).astype(np.int8) for _ in range(2)]
+    return codes[0], exps[0], codes[1], exps[1]
+
+
+def test_fp8_one_new_token_is_the_single_token_fp8_step():
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, T, D = 3, 4, 2, 12, 8
+    cache = _fp8_cache(rng, B, Hkv, T, D)
+    kn, vn = rng.standard_normal((B, Hkv, D)), rng.standard_normal((B, Hkv, D)) * 30
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    L = np.array([0, 5, 12])
+    one = oracle.append_fp8(*cache, L, kn, vn)
+    multi = oracle.append_fp8_multi(*cache, L, kn[:, :, None], vn[:, :, None])
+    for a, b in zip(one[:5], multi[:5]):
+        assert np.array_equal(a, b)
+    assert multi[5].tolist() == [1, 1, 0]
+    want = oracle.decode_attention_fp8(q, *one[:5], 0.4)
+    got = oracle.decode_attention_fp8_multi(q[:, :, None], *multi[:5], multi[5], 0.4)[:, :, 0]
+    assert np.array_equal(got, want)
+
+
+def test_fp8_several_tokens_are_successive_single_appends():
+    """T_q rows appended at once equal T_q single-token fp8 appends, and
+    query i sees the cache up to its own token only."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, T, D, T_q = 3, 4, 1, 16, 8, 4
+    cache = _fp8_cache(rng, B, Hkv, T, D)
+    kn, vn = rng.standard_normal((B, Hkv, T_q, D)), rng.standard_normal((B, Hkv, T_q, D))
+    q = rng.standard_normal((B, Hq, T_q, D)).astype(np.float32)
+    L = np.array([3, 12, 14])  # the last has no room for 4
+    multi = oracle.append_fp8_multi(*cache, L, kn, vn)
+    assert multi[5].tolist() == [4, 4, 0] and multi[4].tolist() == [7, 16, 14]
+    state, n = [x[:2] for x in cache], L[:2]  # the two sequences with room, one token at a time
+    for i in range(T_q):
+        *state, n, _ = oracle.append_fp8(*state, n, kn[:2, :, i], vn[:2, :, i])
+    assert n.tolist() == [7, 16]
+    for a, b in zip(state, multi[:4]):
+        assert np.array_equal(a, b[:2])
+    for x, c in zip(multi[:4], cache):
+        assert np.array_equal(x[2], c[2])  # the full sequence is unchanged
+    out = oracle.decode_attention_fp8_multi(q, *multi[:5], multi[5], 0.5)
+    for i in range(T_q):
+        Li = np.array([3 + i + 1, 12 + i + 1, 14])
+        want = oracle.decode_attention_fp8(np.ascontiguousarray(q[:, :, i]), *multi[:4], Li, 0.5)
+        assert np.array_equal(out[:, :, i], want)
+
+
+FP8_MULTI_MUTANTS = {
+    "fp8_rows_reversed": ("kc[b, :, n[b] + i, :], ke[b, :, n[b] + i] = qk[b, :, i], ek[b, :, i]",
+                          "kc[b, :, n[b] + i, :], ke[b, :, n[b] + i] = qk[b, :, T_q - 1 - i], ek[b, :, T_q - 1 - i]"),
+    "fp8_partial_append": ("if n[b] < 0 or T_cap - n[b] < T_q:", "if n[b] < 0 or T_cap - n[b] < 1:"),
+    "fp8_exponent_of_first_row": ("vc[b, :, n[b] + i, :], ve[b, :, n[b] + i] = qv[b, :, i], ev[b, :, i]",
+                                  "vc[b, :, n[b] + i, :], ve[b, :, n[b] + i] = qv[b, :, i], ev[b, :, 0]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MULTI_MUTANTS))
+def test_fp8_multi_mutant_is_caught(name, monkeypatch):
+    import inspect
+    import types
+    old, new = FP8_MULTI_MUTANTS[name]
+    src = inspect.getsource(oracle)
+    assert src.count(old) == 1, old
+    m = types.ModuleType("oracle_fp8_multi_mutant")
+    m.__file__ = oracle.__file__
+    exec(compile(src.replace(old, new), "oracle_fp8_multi_mutant", "exec"), m.__dict__)
+    failed = []
+    for pin in (test_fp8_one_new_token_is_the_single_token_fp8_step, test_fp8_several_tokens_are_successive_single_appends):
+        with monkeypatch.context() as mp:
+            mp.setattr(oracle, "append_fp8_multi", m.append_fp8_multi)
+            mp.setattr(oracle, "decode_attention_fp8_multi", m.decode_attention_fp8_multi)
+            try:
+                pin()
+            except (AssertionError, IndexError, ValueError):
+                failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
