@@ -124,8 +124,8 @@ def main():
     torch.cuda.set_device(dev)
     fp8 = args.kv_dtype == "fp8"
     tq = args.new_tokens
-    if tq < 1 or tq > kvd.KVD_MAX_NEW_TOKENS or (tq > 1 and fp8):
-        print(f"--new-tokens must be 1..{kvd.KVD_MAX_NEW_TOKENS} (1 with --kv-dtype fp8)", file=sys.stderr)
+    if tq < 1 or tq > kvd.KVD_MAX_NEW_TOKENS:
+        print(f"--new-tokens must be 1..{kvd.KVD_MAX_NEW_TOKENS}", file=sys.stderr)
         sys.exit(2)
     if fp8 and w.dtype != "bf16":
         print("--kv-dtype fp8 takes a bf16 workload", file=sys.stderr)
@@ -152,7 +152,7 @@ def main():
         keep = {}
         if fp8:
             case = inputs.make_fp8_case(w.B, w.Hq, w.Hkv, w.D, T_cap, attended, seed=w.seed + 1000 * r,
-                                        device=dev)
+                                        device=dev, new_tokens=tq if tq > 1 else None)
             if args.page_size:
                 # codes and exponents in shuffled pages under one block table
                 bt, num_pages = inputs.paged_layout(w.B, T_cap, args.page_size, seed=w.seed + 1000 * r + 1)
@@ -232,10 +232,13 @@ def main():
         L = lens[i % R] = [n + tq for n in lens[i % R]]
         if tq > 1:
             # the cache is read once for all tq queries; q, out and the
-            # appended rows scale with tq
-            kv = traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, L)
-            step_bytes += kv + 2 * w.B * w.Hq * tq * w.D * w.elem_bytes + \
-                traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes) * tq
+            # appended rows scale with tq (q and out stay bf16 over fp8)
+            if fp8:
+                kv, app = traffic.kv_read_bytes_fp8(w.Hkv, w.D, L), traffic.append_bytes_fp8(w.B, w.Hkv, w.D)
+            else:
+                kv = traffic.kv_read_bytes(w.Hkv, w.D, w.elem_bytes, L)
+                app = traffic.append_bytes(w.B, w.Hkv, w.D, w.elem_bytes)
+            step_bytes += kv + 2 * w.B * w.Hq * tq * w.D * w.elem_bytes + app * tq
             partial_bytes += kv + w.B * w.Hq * tq * w.D * w.elem_bytes
         elif fp8:
             step_bytes += traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L) + \
@@ -353,9 +356,12 @@ def cpu_baseline(w, copy, T_cap, fp8=False, tq=1):
         host = [t.cpu().numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
         q = case.q.float().cpu().numpy()
         t0 = time.perf_counter()
-        oracle.decode_attention_fp8(q, *host, L, case.scale, threads=threads)
+        if tq > 1:
+            oracle.decode_attention_fp8_multi(q, *host, L, np.full(w.B, tq), case.scale, threads=threads)
+        else:
+            oracle.decode_attention_fp8(q, *host, L, case.scale, threads=threads)
         sec = time.perf_counter() - t0
-        b = traffic.attend_bytes_fp8(w.B, w.Hq, w.Hkv, w.D, L.tolist())
+        b = traffic.kv_read_bytes_fp8(w.Hkv, w.D, L.tolist()) + 2 * w.B * w.Hq * tq * w.D * 2
     else:
         k = inputs.host_array(case.k_cache)
         v = inputs.host_array(case.v_cache)

@@ -95,32 +95,44 @@ __device__ inline int e4m3_row_exponent(float amax) {
     return max(-127, min(127, e));
 }
 
-// One workgroup per sequence; wave w quantizes the rows of KV heads
-// w, w+4, ...: the row's largest magnitude gives its exponent e (a wave
-// reduction), every value becomes the code of x * 2^-e (exact scaling).
+// One workgroup of APPEND_FP8_WAVES waves per sequence; wave w quantizes
+// new rows w, w+16, ... (row r = g * T_q + i, token i of KV head g): the
+// row's largest magnitude gives its exponent e (a wave reduction), every
+// value becomes the code of x * 2^-e (exact scaling).  Sixteen waves, not
+// four: a sequence holds Hkv * T_q rows of K and of V (320 each for 40 KV
+// heads and 8 new tokens), and with four waves the MHA step's append took
+// about 100 us.
+constexpr int APPEND_FP8_WAVES = 16;
 template <int D>
-__global__ __launch_bounds__(256) void append_fp8_kernel(const uint16_t* __restrict__ k_new,
+__global__ __launch_bounds__(64 * APPEND_FP8_WAVES) void append_fp8_kernel(const uint16_t* __restrict__ k_new,
                                                          const uint16_t* __restrict__ v_new,
                                                          uint8_t* __restrict__ k_cache,
                                                          uint8_t* __restrict__ v_cache,
                                                          int8_t* __restrict__ k_exp,
                                                          int8_t* __restrict__ v_exp,
                                                          KvLayout kvl, int32_t* __restrict__ lengths,
-                                                         int* __restrict__ err, int Hkv, int T_cap) {
+                                                         int* __restrict__ err, int* __restrict__ n_new,
+                                                         int Hkv, int T_cap, int T_q) {
     constexpr int PER = D / 64;  // values per lane
     const int b = blockIdx.x;
     const int n = lengths[b];
-    if (n < 0 || n >= T_cap) {
-        if (threadIdx.x == 0) atomicOr(err, n < 0 ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
+    if (n < 0 || n > T_cap - T_q) {
+        // uniform across the block: nobody writes, lengths stays as is
+        if (threadIdx.x == 0) {
+            atomicOr(err, n < 0 ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
+            if (n_new) n_new[b] = 0;
+        }
         return;
     }
-    // page of the slot (paged pools; a bad entry writes page 0 and is flagged)
-    const int page = kvl.block_table ? kv_page(kvl, b, n >> kvl.page_shift, err) : 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int g = wave; g < Hkv; g += 4) {
-        const size_t src = ((size_t)b * Hkv + g) * D;
-        // the exponent of a row sits at the row's index in the exponent array
-        const size_t row = kvl.block_table ? kv_row_paged(kvl, page, g, Hkv, n) : kv_row_contiguous(b, g, Hkv, T_cap, n);
+    // source row r = g * T_q + i goes to slot n + i of KV head g
+    for (int r = wave; r < Hkv * T_q; r += APPEND_FP8_WAVES) {
+        const int g = r / T_q, t = n + (r - g * T_q);
+        const size_t src = ((size_t)b * Hkv * T_q + r) * D;
+        // the exponent of a row sits at the row's index in the exponent
+        // array; paged: a bad block-table entry writes page 0 and is flagged
+        const size_t row = kvl.block_table ? kv_row_paged(kvl, kv_page(kvl, b, t >> kvl.page_shift, err), g, Hkv, t)
+                                           : kv_row_contiguous(b, g, Hkv, T_cap, t);
 #pragma unroll
         for (int kv = 0; kv < 2; ++kv) {
             const uint16_t* x = (kv ? v_new : k_new) + src;
@@ -142,18 +154,21 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const uint16_t* __restr
     }
     // Every thread has read lengths[b] above; only then is it advanced.
     __syncthreads();
-    if (threadIdx.x == 0) lengths[b] = n + 1;
+    if (threadIdx.x == 0) {
+        lengths[b] = n + T_q;
+        if (n_new) n_new[b] = T_q;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                              int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
-                             int B, int Hkv, int D, int T_cap, hipStream_t stream) {
+                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, hipStream_t stream) {
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(B), dim3(256), 0, stream, static_cast<const uint16_t*>(k_new),
+        hipLaunchKernelGGL(kernel, dim3(B), dim3(64 * APPEND_FP8_WAVES), 0, stream, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), static_cast<uint8_t*>(k_cache),
-                           static_cast<uint8_t*>(v_cache), k_exp, v_exp, kv, lengths, err, Hkv, T_cap);
+                           static_cast<uint8_t*>(v_cache), k_exp, v_exp, kv, lengths, err, n_new, Hkv, T_cap, T_q);
     };
     switch (D) {
         case 64: go(append_fp8_kernel<64>); break;

@@ -310,11 +310,14 @@ inline int wave_fp8_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
-// Quantize the new token's bf16 K/V rows into slot lengths[b] (contiguous
-// or paged, the exponent at the row's index) and advance it.
+// Quantize T_q >= 1 new bf16 K/V rows per (sequence, KV head)
+// (k_new/v_new [B, Hkv, T_q, D]) into slots lengths[b] .. lengths[b] + T_q - 1
+// (contiguous or paged, the exponent at the row's index) and advance
+// lengths; a sequence they do not fit is left unchanged and flagged.  n_new
+// (may be null) receives the rows appended per sequence.
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                              int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
-                             int B, int Hkv, int D, int T_cap, hipStream_t stream);
+                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, hipStream_t stream);
 
 
 // Waves per work unit of the MFMA partial pass for group size M.

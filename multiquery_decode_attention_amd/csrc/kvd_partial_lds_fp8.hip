@@ -76,6 +76,11 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
     const int hw0 = hg * 64 + wave * hpw;
     const int nh = max(0, min(hpw, mg - wave * hpw));
     const bool head_ok = c < nh;
+    // Tokens this lane's query row attends (fewer for the earlier queries of
+    // a several-token step); tiles past the smallest limit are masked per row.
+    const int lim = row_limit(len, hg * 64 + min(wave * hpw + (head_ok ? c : max(nh - 1, 0)), mg - 1), a.T_q,
+                              a.n_new, b);
+    const int mask_from = a.T_q == 1 ? len : len - a.T_q + 1;
 
     // Rows are counted from kb/vb (codes) and ke/ve (exponents, one byte
     // per row): the (b, g) slab of a contiguous cache, or the page pools.
@@ -221,10 +226,10 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
-        if (t0 + MFMA_TILE > t_end) {
+        if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (t0 + slot_token(gq, j) >= t_end) x[j] = -INFINITY;
+                if (t0 + slot_token(gq, j) >= lim) x[j] = -INFINITY;
         }
         float mx = x[0];
 #pragma unroll
@@ -253,10 +258,13 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         // takes them times their token's 2^e
         const uint32_t xv0 = *reinterpret_cast<const uint32_t*>(X + 32 + 4 * gq);
         const uint32_t xv1 = *reinterpret_cast<const uint32_t*>(X + 48 + 4 * gq);
+        // a row with no token yet keeps m_ref = -inf; its scores are -inf
+        // too and must weigh 0, not NaN
+        const float m_sub = m_ref == -INFINITY ? 0.f : m_ref;
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
+            p[j] = __builtin_amdgcn_exp2f(x[j] - m_sub);
             l_run += p[j];
             const uint32_t w = j < 4 ? xv0 : xv1;
             p[j] *= pow2_scale((int)(signed char)(w >> (8 * (j & 3))));
@@ -304,12 +312,13 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         const int r = 4 * gq + i;
         const float li = __shfl(l, r);
         if (r < nh) {
-            const float inv = 1.f / li;
+            const float inv = li > 0.f ? 1.f / li : 0.f;  // a row with no token in this split: 0
             store_partial_row<D>(static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D, acc, i, c, inv);
         }
     }
     if (gq == 0 && head_ok)
-        __builtin_nontemporal_store(m_ref + __builtin_log2f(l), a.lse_part + row0 + (size_t)c * a.S);
+        __builtin_nontemporal_store(l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY,
+                                    a.lse_part + row0 + (size_t)c * a.S);
 }
 
 template <int D>

@@ -81,6 +81,13 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
     const int c = lane & 15, gq = lane >> 4;
     const int n_my = n_tiles > wave ? (n_tiles - wave + 3) / 4 : 0;  // this wave's tiles
     const int mg = min(a.M - hg * ROWS, ROWS);                        // rows of the group
+    // Tokens the lane's query row of each block attends: all `len`, except
+    // in a step with several new tokens, where the earlier ones see fewer;
+    // tiles reaching past the smallest such limit are masked per row.
+    int lim[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lim[rb] = row_limit(len, hg * ROWS + min(rb * 16 + c, mg - 1), a.T_q, a.n_new, b);
+    const int mask_from = a.T_q == 1 ? len : len - a.T_q + 1;
 
     // Rows below are counted from kb/vb (codes) and ke/ve (exponents, one
     // byte per row): the (b, g) slab of a contiguous cache, or the start of
@@ -260,10 +267,10 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[rb][j] = (j < 4 ? sc[rb][0][j] : sc[rb][1][j - 4]) * a.scale_log2e;
-                if (t0 + MFMA_TILE > t_end) {
+                if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        if (t0 + slot_token(gq, j) >= t_end) x[rb][j] = -INFINITY;
+                        if (t0 + slot_token(gq, j) >= lim[rb]) x[rb][j] = -INFINITY;
                 }
                 float mx = x[rb][0];
 #pragma unroll
@@ -359,7 +366,17 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
     wait_vm<0>();
     __syncthreads();
     // State of a wave: accumulators in its own lane layout, then (m, l) per
-    // row block and lane; a wave without tiles offers m = -inf (weight 0).
+    // row block and lane.  A row that saw no token in this wave's tiles (no
+    // tiles at all, or an early query of a several-token step: its first
+    // tile already lies past the row's limit) offers m = -inf, weight 0 --
+    // its reference may still hold a unified maximum far above the others.
+    bool has[RB];  // the row saw a token (in this wave, or in a state it took)
+    {
+        const int t_mine = n_my > 0 ? tile_t0(0) : INT32_MAX;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) has[rb] = t_mine < lim[rb];
+    }
+    auto m_offered = [&](int rb) { return has[rb] ? m_ref[rb] : -INFINITY; };
     auto put = [&](unsigned char* buf) {
         f32x4_t* A = reinterpret_cast<f32x4_t*>(buf);
         float2* ML = reinterpret_cast<float2*>(buf + RB * NE * 64 * 16);
@@ -367,7 +384,7 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int e = 0; e < NE; ++e) A[(rb * NE + e) * 64 + lane] = acc[rb][e];
-            ML[rb * 64 + lane] = make_float2(n_my > 0 ? m_ref[rb] : -INFINITY, l_run[rb]);
+            ML[rb * 64 + lane] = make_float2(m_offered(rb), l_run[rb]);
         }
     };
     auto take = [&](const unsigned char* buf) {
@@ -376,13 +393,14 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const float2 o = ML[rb * 64 + lane];
-            const float m_self = n_my > 0 ? m_ref[rb] : -INFINITY;
+            const float m_self = m_offered(rb);
             const float m_new = fmaxf(m_self, o.x);
             // both -inf: neither holds a token of this row (factors 1, 0)
             const float f_self = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_self - m_new);
             const float f_other = m_new == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o.x - m_new);
             l_run[rb] = l_run[rb] * f_self + o.y * f_other;
             m_ref[rb] = m_new;
+            has[rb] = has[rb] || o.x != -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float fs = __shfl(f_self, 4 * gq + i), fo = __shfl(f_other, 4 * gq + i);
@@ -400,8 +418,8 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
     if (wave != 0) return;
     take(lds);
 
-    // wave 0 now holds the split's state (m_ref is finite: the split's
-    // first tile holds a token); normalise and store
+    // wave 0 now holds the split's state; normalise and store (a row with
+    // no token in the split: partial 0, log-sum-exp -inf)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int r0 = rb * 16;  // first row of the block in the group

@@ -66,13 +66,14 @@ struct Plan {
 
 bool is_fp8(const kvdecode_s* h) { return h->d.dtype == KVD_FP8_E4M3; }
 
-int resolve_variant(const kvdecode_s* h) {
+// T_q: query rows per head of the step.
+int resolve_variant(const kvdecode_s* h, int T_q = 1) {
     if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
-    // fp8: the wave kernel when one workgroup holds the whole query group
-    // (MHA and GQA: each tile is widened once instead of once per wave);
-    // larger groups share tiles between waves
+    // fp8: the wave kernel when one workgroup holds all query rows of a KV
+    // head (MHA and GQA: each tile is widened once instead of once per
+    // wave); more rows share tiles between waves
     if (is_fp8(h))
-        return h->d.head_dim >= 128 && h->M <= 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim)
+        return h->d.head_dim >= 128 && h->M * T_q <= 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim)
                    ? KVD_VARIANT_WAVE
                    : KVD_VARIANT_LDS;
     return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
@@ -151,7 +152,7 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
 // T_q: query rows per head (new tokens per sequence in this step).
 Plan make_plan(const kvdecode_s* h, int T_q = 1) {
     Plan p;
-    p.variant = resolve_variant(h);
+    p.variant = resolve_variant(h, T_q);
     p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
     p.lds_config = kvd::LDS_SHORT;
     const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
@@ -261,8 +262,8 @@ int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new,
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
     hipError_t e =
         is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp, h->kv,
-                                           h->d.lengths, h->err, h->d.batch, h->d.num_kv_heads,
-                                           h->d.head_dim, h->d.capacity, st)
+                                           h->d.lengths, h->err, h->err + 1 + h->d.batch, h->d.batch,
+                                           h->d.num_kv_heads, h->d.head_dim, h->d.capacity, T_q, st)
                   : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths,
                                        h->err, h->err + 1 + h->d.batch, h->d.batch, h->d.num_kv_heads,
                                        h->d.head_dim, h->d.capacity, T_q, h->elem, st);
@@ -289,7 +290,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if (is_fp8(h) ? (p.variant != KVD_VARIANT_LDS && p.variant != KVD_VARIANT_WAVE)
                   : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
         return KVD_EUNSUPPORTED;
-    if (T_q > 1 && (is_fp8(h) || p.variant == KVD_VARIANT_MFMA)) return KVD_EUNSUPPORTED;
+    if (T_q > 1 && p.variant == KVD_VARIANT_MFMA) return KVD_EUNSUPPORTED;
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_workspace(h, p.splits * T_q)) != KVD_OK) return rc;

@@ -197,23 +197,29 @@ def _e4m3_codes(shape, gen, device):
     return ((S << 7) | (E << 3) | M).to(torch.uint8)
 
 
-def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu") -> Fp8Case:
+def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu",
+                  new_tokens: Optional[int] = None) -> Fp8Case:
     """Seeded fp8-cache case: the cache is drawn directly as codes and
     exponents (no quantization here: that is the method's own step, done by
     the append under test and by the oracle); q and the new rows are N(0,1)
-    rounded to bf16."""
+    rounded to bf16.  With ``new_tokens`` T the step appends T rows per
+    sequence (k_new, v_new [B, Hkv, T, D], q [B, Hq, T, D]) and the lengths
+    before it are lengths_attended - T."""
+    T = 1 if new_tokens is None else int(new_tokens)
+    extra = () if new_tokens is None else (T,)
     lengths_attended = torch.as_tensor(lengths_attended, dtype=torch.int32).cpu()
     assert lengths_attended.shape == (B,)
     assert int(lengths_attended.min()) >= 1 and int(lengths_attended.max()) <= T_cap
     gen = torch.Generator(device=device).manual_seed(int(seed))
-    q = _normal((B, Hq, D), gen, device, torch.bfloat16)
+    q = _normal((B, Hq) + extra + (D,), gen, device, torch.bfloat16)
     k_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
     v_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
     k_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
     v_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
-    k_new = _normal((B, Hkv, D), gen, device, torch.bfloat16)
-    v_new = _normal((B, Hkv, D), gen, device, torch.bfloat16)
-    lengths0 = (lengths_attended - 1).to(torch.int32).to(device)
+    k_new = _normal((B, Hkv) + extra + (D,), gen, device, torch.bfloat16)
+    v_new = _normal((B, Hkv) + extra + (D,), gen, device, torch.bfloat16)
+    assert int(lengths_attended.min()) >= T
+    lengths0 = (lengths_attended - T).to(torch.int32).to(device)
     return Fp8Case(q, k_codes, k_exp, v_codes, v_exp, lengths0, k_new, v_new, float(D) ** -0.5)
 
 

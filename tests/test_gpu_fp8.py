@@ -283,3 +283,79 @@ def test_fp8_paged_bad_entry_is_reported(variant):
                                                         case.k_new.float().numpy(), case.v_new.float().numpy())
     ref = oracle.decode_attention_fp8_paged(case.q.float().numpy(), kc2, ke2, vc2, ve2, bt, L2, case.scale)
     assert rel_err_rows(to_f64(out)[1:], ref[1:]) <= TOL_BF16
+
+
+def fp8_multi_check(B, Hq, Hkv, D, T, L_att, T_q, name, *, variant="auto", splits=None, page=0,
+                    expect=kvd.KVD_OK):
+    """Several new tokens per sequence on an fp8 cache (contiguous or paged):
+    the quantizing append of all T_q rows is bit-exact and query i attends
+    over the cache and new tokens 0..i, against the oracle."""
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L_att, seed=200 + T_q + D + page)
+    g = torch.Generator().manual_seed(300 + T_q)
+    kn, vn = (torch.randn(B, Hkv, T_q, D, generator=g).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, Hq, T_q, D, generator=g).to(torch.bfloat16)
+    say(f"fp8 multi {name}: B={B} Hq={Hq} Hkv={Hkv} D={D} T_q={T_q} page={page} {variant} S={splits}")
+    dev = torch.device("cuda")
+    host = [case.k_codes, case.k_exp, case.v_codes, case.v_exp]
+    if page:
+        table, num_pages = inputs.paged_layout(B, T, page, seed=7)
+        host = [inputs.to_pages(x, table, page, num_pages) for x in host]
+    kc, ke, vc, ve = (x.to(dev, copy=True) for x in host)
+    L = case.lengths0.to(dev, torch.int32, copy=True)
+    bt = table.to(dev) if page else None
+    cache = kvd.KVCache(kc, vc, L, Hq, block_table=bt, k_exp=ke, v_exp=ve)
+    try:
+        cache.set_variant(VARIANTS[variant])
+        if splits is not None:
+            cache.set_num_splits(splits)
+        out = cache.step_multi(kn.to(dev), vn.to(dev), q.to(dev), scale=D ** -0.5)
+        status = cache.status()
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    assert status == expect
+    before = [x.numpy() for x in host]
+    if page:
+        gather = [oracle.gather_pages(before[0], table.numpy()), oracle.gather_exponent_pages(before[1], table.numpy()),
+                  oracle.gather_pages(before[2], table.numpy()), oracle.gather_exponent_pages(before[3], table.numpy())]
+    else:
+        gather = before
+    r_kc, r_ke, r_vc, r_ve, r_L, appended = oracle.append_fp8_multi(*gather, case.lengths0.numpy(),
+                                                                     kn.float().numpy(), vn.float().numpy())
+    assert np.array_equal(L.cpu().numpy(), r_L)
+    got = [x.cpu().numpy() for x in (kc, ke, vc, ve)]
+    if page:
+        got = [oracle.gather_pages(got[0], table.numpy()), oracle.gather_exponent_pages(got[1], table.numpy()),
+               oracle.gather_pages(got[2], table.numpy()), oracle.gather_exponent_pages(got[3], table.numpy())]
+    for a, b, what in zip(got, (r_kc, r_ke, r_vc, r_ve), ("K codes", "K exponents", "V codes", "V exponents")):
+        assert np.array_equal(a, b), what
+    ref = oracle.decode_attention_fp8_multi(q.float().numpy(), r_kc, r_ke, r_vc, r_ve, r_L, appended, D ** -0.5)
+    err = rel_err_rows(to_f64(out).reshape(-1, D), ref.reshape(-1, D))
+    say(f"fp8 multi {name}: max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("shape,T_q", [("mha", 4), ("gqa", 4), ("gqa", 8), ("palm_like", 2), ("gqa_d256", 3)])
+def test_fp8_multi_token(shape, T_q, variant):
+    B, Hq, Hkv, D, T, L = {
+        "mha": (2, 16, 16, 128, 512, [400, 95]),
+        "gqa": (4, 64, 8, 128, 1024, [1000, 1, 33, 513]),
+        "palm_like": (3, 48, 1, 256, 2048, [2000, 31, 700]),
+        "gqa_d256": (2, 32, 4, 256, 512, [300, 64]),
+    }[shape]
+    fp8_multi_check(B, Hq, Hkv, D, T, L, T_q, f"{shape} T_q={T_q}", variant=variant)
+
+
+@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("splits", [1, 3, 9])
+def test_fp8_multi_token_empty_splits(variant, splits):
+    """Lengths just below tile edges: early queries' last tokens end in
+    tiles (and waves and splits) that the later queries reach past."""
+    fp8_multi_check(5, 16, 2, 128, 256, [31, 60, 95, 1, 64], 6, f"edges S={splits}", variant=variant,
+                    splits=splits)
+
+
+def test_fp8_multi_token_paged_and_overflow():
+    fp8_multi_check(3, 48, 1, 256, 512, [200, 33, 480], 4, "paged", page=64)
+    fp8_multi_check(3, 16, 2, 128, 128, [126, 124, 10], 4, "overflow", expect=kvd.KVD_ECAPACITY)
