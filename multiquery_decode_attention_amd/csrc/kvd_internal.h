@@ -172,11 +172,12 @@ __device__ __forceinline__ int splits_with_data(int len, int tile, int S) {
     return nt < S ? nt : S;
 }
 
-// Partial-pass grids are one-dimensional and split-major: block
-// L = split * units + unit.  Consecutive blocks are dealt round-robin to the
-// eight XCDs, so consecutive units of the same split land on different XCDs;
-// with ragged lengths the always-active low splits are spread evenly and
-// dispatched first, and the mostly-empty high splits come last.
+// Grids of the VALU and register-direct MFMA kernels are one-dimensional
+// and split-major: block L = split * units + unit.  Consecutive blocks are
+// dealt round-robin to the eight XCDs, so consecutive units of the same
+// split land on different XCDs; with ragged lengths the always-active low
+// splits are spread evenly and dispatched first, and the mostly-empty high
+// splits come last.  (The LDS-staged kernels use lds_coord below.)
 struct BlockCoord {
     int split, unit;
 };
@@ -188,17 +189,18 @@ __device__ __forceinline__ BlockCoord block_coord(int units) {
     return c;
 }
 
-// The LDS kernel's grid deals work units to the eight XCDs in turn (block L
-// runs on XCD L mod 8) and, on each XCD, runs them unit after unit, longest
-// first: the k-th block of XCD x is head group k mod G of split (k / G) mod S
-// of unit slot k / (G * S), i.e. unit = slot * 8 + x, with units numbered in
-// dispatch order (sequence order[p] at position p once the combine has
-// sorted the lengths).  Every split of a unit stays on one XCD, as in the
-// split-major grid (which measured 8% faster at long context than splits
-// spread over the XCDs), its head groups are dispatched one after another
-// (their loads of the same tiles meet in that XCD's L2), and the longest
-// workgroups start first (ragged GQA: 333 us against 366 us).  Blocks of
-// padding slots past the last unit exit at once.
+// The LDS-staged kernels' grids (bf16, and both fp8 kernels) deal work
+// units to the eight XCDs in turn (block L runs on XCD L mod 8) and, on each
+// XCD, run them unit after unit, longest first: the k-th block of XCD x is
+// head group k mod G of split (k / G) mod S of unit slot k / (G * S), i.e.
+// unit = slot * 8 + x, with units numbered in dispatch order (sequence
+// order[p] at position p once the combine has sorted the lengths).  Every
+// split of a unit stays on one XCD, as in the split-major grid (which
+// measured 8% faster at long context than splits spread over the XCDs), its
+// head groups are dispatched one after another (their loads of the same
+// tiles meet in that XCD's L2), and the longest workgroups start first
+// (ragged GQA: 333 us against 366 us).  Blocks of padding slots past the
+// last unit exit at once.
 struct LdsCoord {
     int split, hg, p, g;  // p: dispatch position of the sequence
     bool live;
