@@ -60,7 +60,8 @@ extern "C" {
 
 typedef struct kvdecode_s* kvdecode_t;
 
-/* Element types.  KVD_FP8_E4M3 is a cache type only (kvdecode_create_fp8):
+/* Element types.  KVD_FP8_E4M3 is a cache type only (kvdecode_create_fp8,
+ * kvdecode_create_fp8_paged):
  * q, k_new, v_new and out are then bf16. */
 enum { KVD_F32 = 0, KVD_BF16 = 1, KVD_FP8_E4M3 = 2 };
 
@@ -284,9 +285,10 @@ int32_t kvdecode_append_attend(kvdecode_t h, const void* k_new, const void* v_ne
  * cached tokens and the new tokens 0 .. i.  A sequence without room is not
  * appended (sticky KVD_ECAPACITY) and all its queries attend over its
  * lengths[b] cached tokens.  Same dtype rules as kvdecode_append_attend;
- * bf16 or fp32 contiguous or paged caches (KVD_EUNSUPPORTED for fp8 caches
- * and for KVD_VARIANT_MFMA).  n_tokens = 1 gives kvdecode_append_attend's
- * results.
+ * every cache type and layout (fp32, bf16 or fp8; contiguous or paged), on
+ * every kernel but KVD_VARIANT_MFMA (KVD_EUNSUPPORTED).  An fp8 cache
+ * quantizes each new row as kvdecode_append does.  n_tokens = 1 gives
+ * kvdecode_append_attend's results.
  */
 enum { KVD_MAX_NEW_TOKENS = 16 };
 int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void* k_new,
