@@ -45,6 +45,8 @@ KERNEL_SOURCES = {
                 "kvd_internal.h"],
     "wave_fp8": ["kvd_partial_wave_fp8.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
                  "kvd_internal.h"],
+    "xchg_fp8": ["kvd_partial_xchg_fp8.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
+                 "kvd_internal.h"],
     "mfma": ["kvd_partial_mfma.hip", "kvd_mfma_common.h", "kvd_internal.h"],
     "valu": ["kvd_partial_valu.hip", "kvd_internal.h"],
 }
@@ -87,7 +89,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="force split count (0 = plan)")
-    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma", "lds", "wave"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma", "lds", "wave", "xchg"])
     ap.add_argument("--cache-copies", type=int, default=0, help="0 = enough for 2 GiB")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged cache with this many tokens per page (0 = contiguous cache)")
@@ -146,7 +148,7 @@ def main():
 
     variant = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU,
                "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS,
-               "wave": kvd.KVD_VARIANT_WAVE}[args.variant]
+               "wave": kvd.KVD_VARIANT_WAVE, "xchg": kvd.KVD_VARIANT_XCHG}[args.variant]
     copies = []
     for r in range(R):
         keep = {}

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
     "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
-    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KVD_VARIANT_WAVE", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
+    "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KVD_VARIANT_WAVE", "KVD_VARIANT_XCHG", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
     "kvdecode_create_fp8", "kvdecode_create_fp8_paged", "kvdecode_fp8_paged_desc_t",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
     "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
@@ -36,7 +36,7 @@ __all__ = [
 KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
 KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE = -4, -5, -6, -7, -8
 KVD_F32, KVD_BF16, KVD_FP8_E4M3 = 0, 1, 2
-KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS, KVD_VARIANT_WAVE = 0, 1, 2, 3, 4
+KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS, KVD_VARIANT_WAVE, KVD_VARIANT_XCHG = 0, 1, 2, 3, 4, 5
 KVD_TIME_PARTIAL, KVD_TIME_COMBINE, KVD_TIME_APPEND, KVD_TIME_ALL = 1, 2, 4, 7
 
 # KVD_LIBRARY may name another build of the same library (e.g. one compiled
@@ -319,7 +319,7 @@ def kvdecode_get_plan(h: int) -> dict:
     v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(library().kvdecode_get_plan(h, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)),
            "kvdecode_get_plan")
-    return {"variant": {1: "valu", 2: "mfma", 3: "lds", 4: "wave"}.get(v.value, str(v.value)),
+    return {"variant": {1: "valu", 2: "mfma", 3: "lds", 4: "wave", 5: "xchg"}.get(v.value, str(v.value)),
             "num_splits": s.value, "split_tokens": c.value}
 
 

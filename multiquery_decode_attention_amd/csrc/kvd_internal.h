@@ -312,6 +312,32 @@ inline int wave_fp8_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
+// fp8 cache, kernel for large query groups in which the four waves split
+// every 64-token tile by tokens for the scores and by value columns for the
+// output, exchanging the weights through LDS (kvd_partial_xchg_fp8.hip).
+// A workgroup holds up to XCHG_MAX_ROW_BLOCKS(D) blocks of 16 query rows
+// (queries and accumulators in registers: three at d = 256, four at
+// d = 128); larger groups take several workgroups of equal row blocks.
+constexpr int XCHG_TILE = 64;
+constexpr int xchg_max_row_blocks(int D) { return D == 256 ? 3 : 4; }
+struct XchgShape {
+    int row_blocks, groups;
+};
+inline XchgShape xchg_shape(int D, int rows) {
+    const int blocks = (rows + 15) / 16;
+    const int mx = xchg_max_row_blocks(D);
+    const int groups = (blocks + mx - 1) / mx;
+    return XchgShape{(blocks + groups - 1) / groups, groups};
+}
+// Ring slots (one 64-token tile's K and V codes and exponents each) and
+// workgroups per CU: the kernel keeps to 256 registers per lane (two waves
+// per SIMD), so at most two workgroups fit; LDS may allow fewer.
+constexpr int xchg_slots(int D) { return D == 256 ? 2 : 2; }
+constexpr int xchg_lds_bytes(int D) {
+    return xchg_slots(D) * (2 * XCHG_TILE * D + 1024) + 2 * 16 * xchg_max_row_blocks(D) * (2 * XCHG_TILE + 16);
+}
+constexpr int xchg_groups_per_cu(int D) { return 160 * 1024 / xchg_lds_bytes(D) >= 2 ? 2 : 1; }
+hipError_t launch_partial_xchg_fp8(const PartialArgs& a, hipStream_t stream);
 // Quantize T_q >= 1 new bf16 K/V rows per (sequence, KV head)
 // (k_new/v_new [B, Hkv, T_q, D]) into slots lengths[b] .. lengths[b] + T_q - 1
 // (contiguous or paged, the exponent at the row's index) and advance

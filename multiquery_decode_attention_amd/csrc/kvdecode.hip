@@ -69,13 +69,15 @@ bool is_fp8(const kvdecode_s* h) { return h->d.dtype == KVD_FP8_E4M3; }
 // T_q: query rows per head of the step.
 int resolve_variant(const kvdecode_s* h, int T_q = 1) {
     if (h->variant_req != KVD_VARIANT_AUTO) return h->variant_req;
-    // fp8: the wave kernel when one workgroup holds all query rows of a KV
-    // head (MHA and GQA: each tile is widened once instead of once per
-    // wave); more rows share tiles between waves
-    if (is_fp8(h))
-        return h->d.head_dim >= 128 && h->M * T_q <= 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim)
-                   ? KVD_VARIANT_WAVE
-                   : KVD_VARIANT_LDS;
+    // fp8 at d >= 128: the wave kernel when one workgroup holds all query
+    // rows of a KV head (MHA and small GQA groups: no barrier in its loop),
+    // else the exchange kernel (each code widened once however many rows
+    // share it); d = 64: the shared-tile kernel
+    if (is_fp8(h)) {
+        if (h->d.head_dim < 128) return KVD_VARIANT_LDS;
+        return h->M * T_q <= 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim) ? KVD_VARIANT_WAVE
+                                                                              : KVD_VARIANT_XCHG;
+    }
     return h->d.dtype == KVD_BF16 ? KVD_VARIANT_LDS : KVD_VARIANT_VALU;
 }
 
@@ -108,6 +110,9 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
         const int rows_per_group = 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim);
         sh.units = bkv * ((rows + rows_per_group - 1) / rows_per_group);
         sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(h->d.head_dim);
+    } else if (variant == KVD_VARIANT_XCHG) {
+        sh.units = bkv * kvd::xchg_shape(h->d.head_dim, rows).groups;
+        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(h->d.head_dim);
     } else if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((rows + 63) / 64);
         sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
@@ -153,7 +158,9 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
 Plan make_plan(const kvdecode_s* h, int T_q = 1) {
     Plan p;
     p.variant = resolve_variant(h, T_q);
-    p.tile = p.variant == KVD_VARIANT_VALU ? kvd::VALU_TILE : kvd::MFMA_TILE;
+    p.tile = p.variant == KVD_VARIANT_VALU   ? kvd::VALU_TILE
+             : p.variant == KVD_VARIANT_XCHG ? kvd::XCHG_TILE
+                                             : kvd::MFMA_TILE;
     p.lds_config = kvd::LDS_SHORT;
     const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
     auto clamp_splits = [&](long long s) { return s < 1 ? 1 : (s > n_tiles ? n_tiles : s); };
@@ -287,7 +294,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
     const Plan p = make_plan(h, T_q);
-    if (is_fp8(h) ? (p.variant != KVD_VARIANT_LDS && p.variant != KVD_VARIANT_WAVE)
+    if (is_fp8(h) ? (p.variant != KVD_VARIANT_LDS && p.variant != KVD_VARIANT_WAVE && p.variant != KVD_VARIANT_XCHG)
                   : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
         return KVD_EUNSUPPORTED;
     if (T_q > 1 && p.variant == KVD_VARIANT_MFMA) return KVD_EUNSUPPORTED;
@@ -356,6 +363,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
     hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, st)
+                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg_fp8(a, st)
                    : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, st)
                    : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
@@ -582,15 +590,15 @@ int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
 
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
     if (!is_live(h)) return KVD_EINVAL;
-    if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
+    if (variant < KVD_VARIANT_AUTO || variant > KVD_VARIANT_XCHG) return KVD_EUNSUPPORTED;
     if (is_fp8(h)) {
         const bool ok = variant == KVD_VARIANT_AUTO || variant == KVD_VARIANT_LDS ||
-                        (variant == KVD_VARIANT_WAVE && h->d.head_dim >= 128);
+                        ((variant == KVD_VARIANT_WAVE || variant == KVD_VARIANT_XCHG) && h->d.head_dim >= 128);
         if (!ok) return KVD_EUNSUPPORTED;
         h->variant_req = variant;
         return KVD_OK;
     }
-    if (variant == KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_WAVE || variant == KVD_VARIANT_XCHG) return KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;

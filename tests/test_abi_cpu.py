@@ -256,15 +256,26 @@ def test_fp8_handle(lib):
     assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
     assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_WAVE) == kvd.KVD_OK
     assert kvd.kvdecode_get_plan(h.value)["variant"] == "wave"
+    # the exchange kernel walks 64-token tiles: its splits hold multiples of 64
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_XCHG) == kvd.KVD_OK
+    p = kvd.kvdecode_get_plan(h.value)
+    assert p["variant"] == "xchg" and p["split_tokens"] % 64 == 0
     assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
-    # d = 64: the wave kernel needs 16-byte code chunks of the value rows
+    # d = 64: the wave and exchange kernels need 16-byte code chunks of the value rows
     assert lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc(head_dim=64)), ctypes.byref(h)) == kvd.KVD_OK
     assert kvd.kvdecode_get_plan(h.value)["variant"] == "lds"
     assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_WAVE) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_set_variant(h.value, kvd.KVD_VARIANT_XCHG) == kvd.KVD_EUNSUPPORTED
     assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
-    # bf16 handles have no wave kernel
+    # groups above 16 query rows at d = 256 take the exchange kernel
+    assert lib.kvdecode_create_fp8(ctypes.byref(make_fp8_desc(head_dim=256, num_q_heads=48, num_kv_heads=1)),
+                                   ctypes.byref(h)) == kvd.KVD_OK
+    assert kvd.kvdecode_get_plan(h.value)["variant"] == "xchg"
+    assert lib.kvdecode_destroy(h.value) == kvd.KVD_OK
+    # bf16 handles have neither kernel
     rc, hb = create(lib, make_desc())
     assert rc == kvd.KVD_OK and lib.kvdecode_set_variant(hb, kvd.KVD_VARIANT_WAVE) == kvd.KVD_EUNSUPPORTED
+    assert lib.kvdecode_set_variant(hb, kvd.KVD_VARIANT_XCHG) == kvd.KVD_EUNSUPPORTED
     assert lib.kvdecode_destroy(hb) == kvd.KVD_OK
     # the fp8 cache type is only reachable through kvdecode_create_fp8
     rc, h2 = create(lib, make_desc(dtype=kvd.KVD_FP8_E4M3))

@@ -21,8 +21,11 @@ pytestmark = pytest.mark.gpu
 
 # wave: each wave streams its own tiles for all query heads of its group
 # (d >= 128; several row groups share tiles through L2); lds: the four waves
-# share every tile
-VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "wave": kvd.KVD_VARIANT_WAVE, "lds": kvd.KVD_VARIANT_LDS}
+# share every tile; xchg: the waves split each 64-token tile by tokens for
+# the scores and by columns for the values, exchanging weights in LDS
+# (d >= 128)
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "wave": kvd.KVD_VARIANT_WAVE, "lds": kvd.KVD_VARIANT_LDS,
+            "xchg": kvd.KVD_VARIANT_XCHG}
 
 
 def fp8_step(case, Hq, *, fused=True, splits=None, lengths=None, unified_max=None, variant="auto"):
@@ -88,18 +91,18 @@ SHAPES = {  # name: (B, Hq, Hkv, D, T_cap, lengths)
 }
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("name", list(SHAPES))
 def test_fp8_shapes(name, fused, variant):
     B, Hq, Hkv, D, T, L = SHAPES[name]
-    if variant == "wave" and D < 128:
-        pytest.skip("the wave kernel needs d >= 128")
+    if variant in ("wave", "xchg") and D < 128:
+        pytest.skip("the wave and exchange kernels need d >= 128")
     case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=90 + len(name))
     check_fp8(case, Hq, f"fp8/{name}/{variant}", fused=fused, variant=variant)
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("Hq", [16, 48])
 @pytest.mark.parametrize("splits", [1, 2, 5])
 def test_fp8_forced_splits(splits, Hq, variant):
@@ -108,6 +111,22 @@ def test_fp8_forced_splits(splits, Hq, variant):
     lengths = [1, 31, 32, 33, 64, 65, 127, 128, 200, 256]
     case = inputs.make_fp8_case(len(lengths), Hq, 2, 128, 256, lengths, seed=95 + splits)
     check_fp8(case, Hq, f"fp8 S={splits} Hq={Hq} {variant}", splits=splits, variant=variant)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(48, 1, 256), (32, 1, 256), (16, 2, 256), (96, 1, 256), (64, 1, 128),
+                                     (80, 1, 128), (40, 2, 128)])
+@pytest.mark.parametrize("splits", [None, 1, 3])
+def test_fp8_xchg_row_groups_and_edges(Hq, Hkv, D, splits):
+    """The exchange kernel over 1-4 row blocks per workgroup and several row
+    groups (96 rows at d = 256: two groups of three blocks; 80 at d = 128:
+    two groups of three), with lengths on and next to the edges of its
+    16-token blocks and 64-token tiles, so that whole blocks of a tile lie
+    past a sequence's end."""
+    lengths = [1, 15, 16, 17, 48, 63, 64, 65, 100, 129, 250]
+    case = inputs.make_fp8_case(len(lengths), Hq, Hkv, D, 256, lengths, seed=150 + Hq + D)
+    out, plan = check_fp8(case, Hq, f"fp8 xchg Hq={Hq} Hkv={Hkv} D={D} S={splits}", splits=splits,
+                          variant="xchg")
+    assert plan["variant"] == "xchg"
 
 
 def test_fp8_append_extremes():
@@ -128,12 +147,14 @@ def test_fp8_append_extremes():
 
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,variant", [("mha", 2, 8, 8, 128, "wave"), ("gqa", 2, 64, 8, 128, "wave"),
                                                       ("mqa48_d128", 2, 48, 1, 128, "wave"),
-                                                      ("mqa48_d256", 2, 48, 1, 256, "lds"),
+                                                      ("mqa64_d128", 2, 64, 1, 128, "xchg"),
+                                                      ("mqa48_d256", 2, 48, 1, 256, "xchg"),
                                                       ("mqa16_d256", 2, 16, 1, 256, "wave"),
                                                       ("d64", 2, 8, 1, 64, "lds")])
 def test_fp8_auto_picks(name, B, Hq, Hkv, D, variant):
-    """The automatic choice: the wave kernel when one workgroup holds the
-    whole query group at d >= 128, the shared-tile kernel otherwise."""
+    """The automatic choice at d >= 128: the wave kernel when one workgroup
+    holds the whole query group, else the exchange kernel; the shared-tile
+    kernel at d = 64."""
     case = inputs.make_fp8_case(B, Hq, Hkv, D, 256, [200, 100], seed=77)
     out, plan = check_fp8(case, Hq, f"fp8 auto {name}")
     assert plan["variant"] == variant
@@ -150,7 +171,7 @@ def test_fp8_capacity_overflow():
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("phi", [0.0, -40.0, 1e4])
 def test_fp8_unified_max(phi, variant):
     B, Hq, Hkv, D, T, L = SHAPES["palm_like"]
@@ -158,7 +179,7 @@ def test_fp8_unified_max(phi, variant):
     check_fp8(case, Hq, f"fp8 unified max {phi} {variant}", unified_max=phi, variant=variant)
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 def test_fp8_consecutive_steps_ragged_batch(variant):
     """Several steps on one handle over a ragged batch: from the second step
     on the wave kernel dispatches sequences in the length order the previous
@@ -231,7 +252,7 @@ def fp8_paged_step(case, Hq, page_size, *, variant="wave", seed=5, fused=True, t
     return out, after, before, table.numpy(), L.cpu().numpy(), status, plan
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("name,page", [("ragged_gqa_like", 64), ("mha_like", 256), ("palm_like", 128),
                                        ("gqa48_d128", 32), ("small_d64", 32)])
 def test_fp8_paged(name, page, variant):
@@ -239,8 +260,8 @@ def test_fp8_paged(name, page, variant):
     block table) is bit-exact on every pool, spare pages included, and the
     attention matches the oracle over the gathered cache."""
     B, Hq, Hkv, D, T, L = SHAPES[name]
-    if variant == "wave" and D < 128:
-        pytest.skip("the wave kernel needs d >= 128")
+    if variant in ("wave", "xchg") and D < 128:
+        pytest.skip("the wave and exchange kernels need d >= 128")
     case = inputs.make_fp8_case(B, Hq, Hkv, D, T, L, seed=130 + len(name))
     say(f"fp8 paged {name} page={page} {variant}")
     out, after, before, bt, L_gpu, status, plan = fp8_paged_step(case, Hq, page, variant=variant)
@@ -267,7 +288,7 @@ def test_fp8_paged_equals_contiguous_bitwise():
     assert torch.equal(out_c.cpu().view(torch.int16), out_p.cpu().view(torch.int16))
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 def test_fp8_paged_bad_entry_is_reported(variant):
     """A block-table entry in use outside the pool reads page 0 (memory
     safe) and is reported; the other sequences are unaffected."""
@@ -335,7 +356,7 @@ def fp8_multi_check(B, Hq, Hkv, D, T, L_att, T_q, name, *, variant="auto", split
     assert err <= TOL_BF16, err
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("shape,T_q", [("mha", 4), ("gqa", 4), ("gqa", 8), ("palm_like", 2), ("gqa_d256", 3)])
 def test_fp8_multi_token(shape, T_q, variant):
     B, Hq, Hkv, D, T, L = {
@@ -347,7 +368,7 @@ def test_fp8_multi_token(shape, T_q, variant):
     fp8_multi_check(B, Hq, Hkv, D, T, L, T_q, f"{shape} T_q={T_q}", variant=variant)
 
 
-@pytest.mark.parametrize("variant", ["wave", "lds"])
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("splits", [1, 3, 9])
 def test_fp8_multi_token_empty_splits(variant, splits):
     """Lengths just below tile edges: early queries' last tokens end in
