@@ -331,8 +331,10 @@ inline XchgShape xchg_shape(int D, int rows) {
 }
 // Ring slots (one 64-token tile's K and V codes and exponents each) and
 // workgroups per CU: the kernel keeps to 256 registers per lane (two waves
-// per SIMD), so at most two workgroups fit; LDS may allow fewer.
-constexpr int xchg_slots(int D) { return D == 256 ? 2 : 2; }
+// per SIMD), so at most two workgroups fit; LDS may allow fewer.  Two slots
+// keep two workgroups per CU at d = 256; four slots with one workgroup per
+// CU measured slower (long context 80 against 67 us).
+constexpr int xchg_slots(int) { return 2; }
 constexpr int xchg_lds_bytes(int D) {
     return xchg_slots(D) * (2 * XCHG_TILE * D + 1024) + 2 * 16 * xchg_max_row_blocks(D) * (2 * XCHG_TILE + 16);
 }

@@ -56,6 +56,19 @@ using namespace fp8;
 // s_waitcnt lgkmcnt(0), then s_barrier: LDS writes of every wave visible.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Maximum of x over lanes i, i^16, i^32, i^48 with gfx950's lane swaps (no
+// LDS round trip): given the same value twice, the 16-lane swap returns the
+// values of rows (0, 1) and (2, 3) in its two results, and the 32-lane swap
+// those of the two halves.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D, int R, int NS, bool GROUPED, bool PAGED>
 __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
     constexpr int TT = XCHG_TILE;          // tokens per tile
@@ -65,7 +78,6 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     constexpr int KS = D / 32;             // k-steps of the score product
     constexpr int DQ = D / 4;              // value columns per wave
     constexpr int NC = DQ / 16;            // output column blocks per wave = codes per lane and token
-    constexpr int VW = NC / 2;             // dwords of widened values per lane and token
     constexpr int ROWS = 16 * R;           // query rows per workgroup
     constexpr int NKV = 16 * D / 1024;     // 1 KB loads of a wave's 16 K (or V) rows
     constexpr int REGION = TT * D;         // bytes of K (or V) codes per slot
@@ -196,10 +208,17 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         v_row = r0;
         v_last = last;
         const char* kt = kb + r0 * D;
+        if (last == 15) {  // (uniform) a whole block: a scalar base and fixed lane offsets
 #pragma unroll
-        for (int n = 0; n < NKV; ++n)
-            __builtin_amdgcn_global_load_lds((const void*)(kt + kgo[n] + (min(lrow[n], last) - lrow[n]) * D),
-                                             (lds_void_t*)(kd + n * 1024), 16, 0, KV_POLICY);
+            for (int n = 0; n < NKV; ++n)
+                __builtin_amdgcn_global_load_lds((const void*)(kt + kgo[n]), (lds_void_t*)(kd + n * 1024), 16, 0,
+                                                 KV_POLICY);
+        } else {
+#pragma unroll
+            for (int n = 0; n < NKV; ++n)
+                __builtin_amdgcn_global_load_lds((const void*)(kt + kgo[n] + (min(lrow[n], last) - lrow[n]) * D),
+                                                 (lds_void_t*)(kd + n * 1024), 16, 0, KV_POLICY);
+        }
         // lane l, q = l & 7: K exponents of rows 4q .. 4q+3 for q < 4, else V
         // exponents of rows 4(q-4) ..; lanes 8-63 repeat them.  Bytes 0-15
         // are K, 16-31 V; those of rows past the sequence's end are never
@@ -217,10 +236,17 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
             return;
         }
         const char* vt = vb + v_row * D;
+        if (v_last == 15) {
 #pragma unroll
-        for (int n = 0; n < NKV; ++n)
-            __builtin_amdgcn_global_load_lds((const void*)(vt + vgo[n] + (min(lrow[n], v_last) - lrow[n]) * D),
-                                             (lds_void_t*)(vd + n * 1024), 16, 0, KV_POLICY);
+            for (int n = 0; n < NKV; ++n)
+                __builtin_amdgcn_global_load_lds((const void*)(vt + vgo[n]), (lds_void_t*)(vd + n * 1024), 16, 0,
+                                                 KV_POLICY);
+        } else {
+#pragma unroll
+            for (int n = 0; n < NKV; ++n)
+                __builtin_amdgcn_global_load_lds((const void*)(vt + vgo[n] + (min(lrow[n], v_last) - lrow[n]) * D),
+                                                 (lds_void_t*)(vd + n * 1024), 16, 0, KV_POLICY);
+        }
     };
 
     // LDS read offsets.  Score operand: K row 16*wave + c, codes 32ks + 8gq
@@ -276,26 +302,28 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) sc[rb] = mfma16x16x32(kop, qop[rb][ks], sc[rb]);
         }
-        // lane (c, gq) holds row 16rb + c, tokens tw .. tw+3
+        // lane (c, gq) holds row 16rb + c, tokens tw .. tw+3; x are the
+        // unscaled products q.k (the scale is positive, so the row maximum
+        // of x times the scale is the maximum of the scaled logits)
         const int t0 = t_first + it * tstride;
         const int tw = t0 + 16 * wave + 4 * gq;
+        const float sl = a.scale_log2e;
         float x[R][4], mx[R];
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[rb][i] = sc[rb][i] * a.scale_log2e;
+            for (int i = 0; i < 4; ++i) x[rb][i] = sc[rb][i];
             if (t0 + TT > mask_from) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (tw + i >= lim[rb]) x[rb][i] = -INFINITY;
             }
-            float m = fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]));
-            m = fmaxf(m, __shfl_xor(m, 16));
-            mx[rb] = fmaxf(m, __shfl_xor(m, 32));
+            mx[rb] = max_over_row_groups(fmaxf(fmaxf(x[rb][0], x[rb][1]), fmaxf(x[rb][2], x[rb][3]))) * sl;
         }
         // Weights under the current references into this tile's buffer:
-        // 2^(x - m) summed as they are, times the token's 2^e for the value
-        // product.  A row with no token yet keeps m_ref = -inf and weighs 0.
+        // 2^(x * scale - m) summed as they are, times the token's 2^e for the
+        // value product.  A row with no token yet keeps m_ref = -inf and
+        // weighs 0.
         const uint32_t xv = *reinterpret_cast<const uint32_t*>(X + 16 + 4 * gq);
         float lt[R];
         // weight row r holds its 16-byte chunk h at position h ^ ((r >> 1) & 7):
@@ -310,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
                 float sum = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(x[rb][i] - m_sub);
+                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][i], sl, -m_sub));
                     sum += p[i];
                     p[i] *= pow2_scale((int)(signed char)(xv >> (8 * i)));
                 }
@@ -370,19 +398,29 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         for (int rb = 0; rb < R; ++rb) l_run[rb] += lt[rb];
 
         // values: the 64 tokens' weights of every row times this wave's
-        // columns of the V rows, each code widened once for all row blocks
+        // columns of the V rows, each code widened once for all row blocks.
+        // A lane holds NC codes (its columns) of each of tokens 8gq + j; byte
+        // permutes pair tokens 2m and 2m+1 column by column before widening,
+        // so each widened dword is dword m of one column block's operand.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint32_t v[8][VW];
+            uint32_t w[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const unsigned char* vp = slot + voff + (32 * h + j) * D;
+                w[j] = NC == 4 ? *reinterpret_cast<const uint32_t*>(vp)
+                               : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
+            }
+            u32x4_t vop[NC];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t c01 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05010400u);
+                vop[0][m] = widen2<false>(c01, 1.0f);
+                vop[1][m] = widen2<true>(c01, 1.0f);
                 if constexpr (NC == 4) {
-                    const uint32_t w = *reinterpret_cast<const uint32_t*>(vp);
-                    v[j][0] = widen2<false>(w, 1.0f);
-                    v[j][VW - 1] = widen2<true>(w, 1.0f);
-                } else {
-                    v[j][0] = widen2<false>((uint32_t)*reinterpret_cast<const uint16_t*>(vp), 1.0f);
+                    const uint32_t c23 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07030602u);
+                    vop[2][m] = widen2<false>(c23, 1.0f);
+                    vop[3][m] = widen2<true>(c23, 1.0f);
                 }
             }
             u32x4_t pop[R];
@@ -391,9 +429,8 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
                 pop[rb] = *reinterpret_cast<const u32x4_t*>(Pb + (16 * rb + c) * PST + (((4 * h + gq) ^ pkey) << 4));
 #pragma unroll
             for (int e = 0; e < NC; ++e) {
-                const u32x4_t vop = v_operand(v, e);
 #pragma unroll
-                for (int rb = 0; rb < R; ++rb) acc[rb][e] = mfma16x16x32(pop[rb], vop, acc[rb][e]);
+                for (int rb = 0; rb < R; ++rb) acc[rb][e] = mfma16x16x32(pop[rb], vop[e], acc[rb][e]);
             }
         }
     }
