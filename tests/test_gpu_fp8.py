@@ -254,7 +254,7 @@ def fp8_paged_step(case, Hq, page_size, *, variant="wave", seed=5, fused=True, t
 
 @pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("name,page", [("ragged_gqa_like", 64), ("mha_like", 256), ("palm_like", 128),
-                                       ("gqa48_d128", 32), ("small_d64", 32)])
+                                       ("palm_like", 32), ("gqa48_d128", 32), ("small_d64", 32)])
 def test_fp8_paged(name, page, variant):
     """fp8 codes and exponents in shuffled pages: the append (through the
     block table) is bit-exact on every pool, spare pages included, and the
