@@ -180,8 +180,9 @@ typedef struct {
  * (ties to the even code).  Attention reads code * 2^e: exact in bf16 for
  * every e that keeps the values within bf16's normal range.  Callers that
  * write the cache themselves (prefill) must follow the same format.  The
- * partial pass runs on the fp8 WAVE or LDS kernel (kvdecode_set_variant);
- * kvdecode_create_fp8_paged takes the same format in page pools.
+ * partial pass runs on the fp8 WAVE, XCHG or LDS kernel
+ * (kvdecode_set_variant); kvdecode_create_fp8_paged takes the same format
+ * in page pools.
  */
 typedef struct {
     kvdecode_desc_t cache; /* dtype KVD_FP8_E4M3; caches hold the codes              */
@@ -271,8 +272,10 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
  * same lengths update, same sticky errors -- in fewer launches: with the
  * LDS and VALU kernels the append is folded into the partial pass (the new
  * token's row is read from k_new/v_new directly and written to its cache
- * slot alongside), and the combine advances lengths; the MFMA kernel runs
- * the append kernel first.
+ * slot alongside), and with the fp8 WAVE and XCHG kernels the workgroups
+ * owning the new token's tile quantize it into its slot before reading
+ * that tile; the combine advances lengths.  The MFMA kernel and the fp8
+ * LDS kernel run the append kernel first.
  * Same page, section "Implementation: JetStream": generate emits one token
  * per batch item and appends its single-token KV cache.
  */

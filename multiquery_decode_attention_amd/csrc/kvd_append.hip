@@ -13,7 +13,7 @@
 // One workgroup per sequence; 16-byte vector copies.  The copy is bit-exact:
 // k_new/v_new already have the cache dtype.  With a paged cache the slot's
 // row is found through the block table.
-#include "kvd_internal.h"
+#include "kvd_fp8_common.h"
 
 namespace kvd {
 namespace {
@@ -59,42 +59,6 @@ __global__ __launch_bounds__(256) void append_kernel(const uint4* __restrict__ k
 
 // --- fp8 cache: quantizing append ------------------------------------------
 
-// Nearest OCP E4M3 code of y (finite, |y| <= 448), ties to the even code;
-// the sign bit is y's.  Codes 0..8 below 2^-6 are the subnormals (and 2^-6
-// itself), spaced 2^-9; above, 3 mantissa bits are kept by rounding the
-// fp32 mantissa half to even.
-__device__ inline uint32_t e4m3_encode(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
-    uint32_t code;
-    if (a < 0.015625f) {
-        code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling; round half to even
-    } else {
-        const uint32_t ab = __float_as_uint(a);
-        int E = (int)(ab >> 23) - 127;  // -6 .. 8
-        uint32_t q = (ab >> 20) & 7u;
-        const uint32_t rem = ab & 0xFFFFFu;
-        if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
-        if (q == 8u) {
-            q = 0;
-            ++E;
-        }
-        code = ((uint32_t)(E + 7) << 3) | q;
-    }
-    return sign | code;
-}
-
-// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax 0.
-// With amax = m * 2^k, m in [1, 2): e = k - 8, plus 1 when m > 1.75.
-__device__ inline int e4m3_row_exponent(float amax) {
-    if (!(amax > 0.f)) return 0;
-    const uint32_t b = __float_as_uint(amax);
-    const int E = (int)(b >> 23);
-    if (E == 0) return -127;  // subnormal amax: far below the clamp
-    const int e = E - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    return max(-127, min(127, e));
-}
-
 // One workgroup of APPEND_FP8_WAVES waves per sequence; wave w quantizes
 // new rows w, w+16, ... (row r = g * T_q + i, token i of KV head g): the
 // row's largest magnitude gives its exponent e (a wave reduction), every
@@ -113,7 +77,6 @@ __global__ __launch_bounds__(64 * APPEND_FP8_WAVES) void append_fp8_kernel(const
                                                          KvLayout kvl, int32_t* __restrict__ lengths,
                                                          int* __restrict__ err, int* __restrict__ n_new,
                                                          int Hkv, int T_cap, int T_q) {
-    constexpr int PER = D / 64;  // values per lane
     const int b = blockIdx.x;
     const int n = lengths[b];
     if (n < 0 || n > T_cap - T_q) {
@@ -134,23 +97,9 @@ __global__ __launch_bounds__(64 * APPEND_FP8_WAVES) void append_fp8_kernel(const
         const size_t row = kvl.block_table ? kv_row_paged(kvl, kv_page(kvl, b, t >> kvl.page_shift, err), g, Hkv, t)
                                            : kv_row_contiguous(b, g, Hkv, T_cap, t);
 #pragma unroll
-        for (int kv = 0; kv < 2; ++kv) {
-            const uint16_t* x = (kv ? v_new : k_new) + src;
-            float y[PER];
-            float amax = 0.f;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                y[i] = __uint_as_float((uint32_t)x[lane * PER + i] << 16);
-                amax = fmaxf(amax, fabsf(y[i]));
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-            const int e = e4m3_row_exponent(amax);
-            uint8_t* dst = (kv ? v_cache : k_cache) + row * D + lane * PER;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) dst[i] = (uint8_t)e4m3_encode(ldexpf(y[i], -e));
-            if (lane == 0) (kv ? v_exp : k_exp)[row] = (int8_t)e;
-        }
+        for (int kv = 0; kv < 2; ++kv)
+            fp8::quantize_row<D>((kv ? v_new : k_new) + src, (kv ? v_cache : k_cache) + row * D,
+                                 (kv ? v_exp : k_exp) + row, lane);
     }
     // Every thread has read lengths[b] above; only then is it advanced.
     __syncthreads();

@@ -1,6 +1,7 @@
-// kvd_fp8_common.h -- device helpers of the fp8-cache partial kernels:
-// widening OCP FP8 E4M3 codes to bf16 matrix-core operands with gfx950's
-// scaled conversion.
+// kvd_fp8_common.h -- device helpers of the fp8-cache kernels: widening
+// OCP FP8 E4M3 codes to bf16 matrix-core operands with gfx950's scaled
+// conversion, and the quantization of new rows (the append kernel, and the
+// partial kernels' fused append).
 #pragma once
 
 #include "kvd_lds_common.h"
@@ -32,6 +33,64 @@ __device__ __forceinline__ u32x4_t widen8(u32x2_t x, float scale) {
     o[2] = widen2<false>(x[1], scale);
     o[3] = widen2<true>(x[1], scale);
     return o;
+}
+
+// Nearest OCP E4M3 code of y (finite, |y| <= 448), ties to the even code;
+// the sign bit is y's.  Codes 0..8 below 2^-6 are the subnormals (and 2^-6
+// itself), spaced 2^-9; above, 3 mantissa bits are kept by rounding the
+// fp32 mantissa half to even.
+__device__ inline uint32_t e4m3_encode(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    uint32_t code;
+    if (a < 0.015625f) {
+        code = (uint32_t)__builtin_rintf(a * 512.0f);  // exact scaling; round half to even
+    } else {
+        const uint32_t ab = __float_as_uint(a);
+        int E = (int)(ab >> 23) - 127;  // -6 .. 8
+        uint32_t q = (ab >> 20) & 7u;
+        const uint32_t rem = ab & 0xFFFFFu;
+        if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+        if (q == 8u) {
+            q = 0;
+            ++E;
+        }
+        code = ((uint32_t)(E + 7) << 3) | q;
+    }
+    return sign | code;
+}
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax 0.
+// With amax = m * 2^k, m in [1, 2): e = k - 8, plus 1 when m > 1.75.
+__device__ inline int e4m3_row_exponent(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const uint32_t b = __float_as_uint(amax);
+    const int E = (int)(b >> 23);
+    if (E == 0) return -127;  // subnormal amax: far below the clamp
+    const int e = E - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return max(-127, min(127, e));
+}
+
+// Quantizing append of one row, by the 64 lanes of a wave: the row's largest
+// magnitude gives its exponent e (a wave reduction), every value becomes the
+// code of x * 2^-e (exact scaling); lane l handles values l*D/64 ..
+// (l+1)*D/64 - 1 of the bf16 row src, the codes go to dst and e to *xdst.
+template <int D>
+__device__ inline void quantize_row(const uint16_t* src, uint8_t* dst, int8_t* xdst, int lane) {
+    constexpr int PER = D / 64;
+    float y[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        y[i] = __uint_as_float((uint32_t)src[lane * PER + i] << 16);
+        amax = fmaxf(amax, fabsf(y[i]));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const int e = e4m3_row_exponent(amax);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) dst[lane * PER + i] = (uint8_t)e4m3_encode(ldexpf(y[i], -e));
+    if (lane == 0) *xdst = (int8_t)e;
 }
 
 }  // namespace fp8

@@ -100,8 +100,9 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     if (!lc.live) return;  // padding, before any barrier
     const SeqAt sa = seq_at(lc.p, a.B, a.order, a.lengths);
     const int s = lc.split, hg = lc.hg, g = lc.g, b = sa.b;
-    const int len = sequence_length_of(sa.len0, a.err, a.len_att, b, a.T_cap, false,
-                                       s == 0 && g == 0 && hg == 0 && threadIdx.x == 0).len;
+    const SeqLen sl = sequence_length_of(sa.len0, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
+                                         s == 0 && g == 0 && hg == 0 && threadIdx.x == 0);
+    const int len = sl.len;
     const int n_seq_tiles = (len + TT - 1) / TT;
     if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
     const int n_tiles = (n_seq_tiles - s + a.S - 1) / a.S;  // tiles of this split
@@ -112,6 +113,28 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     const int wave = wave_index();
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, gq = lane >> 4;
+
+    // Fused append (one new token; k_new/v_new set): the split owning the
+    // token's tile quantizes its K and V rows into the cache slot before any
+    // load of that tile -- waves 0 and 1 write them, and the barrier (a
+    // workgroup-scope release and acquire) makes the stores visible to every
+    // wave's loads.  Every head group of that split writes the same bytes; no
+    // other workgroup reads the slot in this launch.
+    if (sl.appended && s == (sl.slot / TT) % a.S) {
+        if (wave < 2) {
+            size_t row;
+            if constexpr (PAGED)
+                row = kv_row_paged(a.kv, kv_page(a.kv, b, sl.slot >> a.kv.page_shift, a.err), g, a.Hkv, sl.slot);
+            else
+                row = kv_row_contiguous(b, g, a.Hkv, a.T_cap, sl.slot);
+            const uint16_t* src = static_cast<const uint16_t*>(wave ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + g) * D;
+            uint8_t* cache = static_cast<uint8_t*>(const_cast<void*>(wave ? a.v_cache : a.k_cache));
+            int8_t* exps = const_cast<int8_t*>(wave ? a.v_exp : a.k_exp);
+            quantize_row<D>(src, cache + row * D, exps + row, lane);
+        }
+        __syncthreads();
+    }
+
     const int mg = min(a.M - hg * ROWS, ROWS);  // rows of the group
     // Tokens the lane's query row of each block attends: all `len`, except
     // in a step with several new tokens, where the earlier ones see fewer;

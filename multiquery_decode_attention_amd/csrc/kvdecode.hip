@@ -303,9 +303,13 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     if ((rc = ensure_workspace(h, p.splits * T_q)) != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
     const bool with_append = k_new != nullptr;
-    // the fp8 append quantizes in its own kernel, before the partial pass,
-    // and so does an append of several tokens
-    const bool fused = with_append && p.variant != KVD_VARIANT_MFMA && !is_fp8(h) && T_q == 1;
+    // One new token is appended inside the partial pass (bf16 and fp32:
+    // every kernel but MFMA; fp8: the wave and exchange kernels, which
+    // quantize it there); otherwise, and for several new tokens, the append
+    // kernel runs first.
+    const bool fused = with_append && T_q == 1 &&
+                       (is_fp8(h) ? p.variant == KVD_VARIANT_WAVE || p.variant == KVD_VARIANT_XCHG
+                                  : p.variant != KVD_VARIANT_MFMA);
     if (with_append && !fused) {
         if ((rc = launch_append_timed(h, k_new, v_new, st, T_q)) != KVD_OK) return rc;
     }
