@@ -25,6 +25,9 @@
 // then 1 into 0), merged by the same exact rescaling as the log-sum-exp
 // combine, and wave 0 writes the split's partial.
 //
+// In a decode step the kernel also appends the new token: the workgroups
+// owning its tile quantize its rows into the cache slot first (below).
+//
 // Sources: quantized KV caches save memory bandwidth ("All About Transformer
 // Inference", section on tricks for generation throughput); bf16 arithmetic
 // on quantized storage ("Efficiently Scaling Transformer Inference", section

@@ -26,8 +26,9 @@
 // after) are they recomputed and rewritten, and the waves meet at a second
 // barrier before the value product.
 //
-// LDS holds two slots of K codes, V codes and exponents, two buffers of
-// weights and two of row maxima (tile it uses slot and buffers it & 1).
+// LDS holds NS slots (two; xchg_slots) of K codes, V codes and exponents,
+// two buffers of weights and two of row maxima (tile it uses slot it % NS
+// and buffers it & 1).
 // Each wave fills its own 16 rows of a slot with direct global->LDS loads:
 // K rows with their 16-byte chunks XOR-swizzled by row (the score operand
 // reads 16 rows at once), V rows swizzled by 8-token group (the value
@@ -37,6 +38,9 @@
 // and are refilled after the barrier.  Weight rows are swizzled by row pair
 // for the same reason.  At d = 256 with 48 rows this is 81408 bytes, two
 // workgroups per CU.
+//
+// In a decode step the kernel also appends the new token: the workgroups
+// owning its tile quantize its rows into the cache slot first (below).
 //
 // Sources: quantized KV caches save memory bandwidth ("All About Transformer
 // Inference", section on tricks for generation throughput); bf16 arithmetic
