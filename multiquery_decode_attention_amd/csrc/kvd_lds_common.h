@@ -45,6 +45,19 @@ __device__ __forceinline__ int wave_index() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// Maximum of x over lanes i, i^16, i^32, i^48 with gfx950's lane swaps (no
+// LDS round trip): given the same value twice, the 16-lane swap returns the
+// values of rows (0, 1) and (2, 3) in its two results, and the 32-lane swap
+// those of the two halves.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // True when the predicate holds in any active lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(xs[j] - m_sub);
+            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], a.scale_log2e, -m_sub));
             l_run += p[j];
         }
         u32x4_t pop;
@@ -356,8 +356,10 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                 sc[0] = mfma16x16x32(k0, qop[ks], sc[0]);
                 sc[1] = mfma16x16x32(k1, qop[ks], sc[1]);
             }
+            // x: the unscaled products q.k (the scale is positive, so the
+            // row maximum of x times the scale is that of the scaled logits)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
+            for (int j = 0; j < 8; ++j) x[j] = j < 4 ? sc[0][j] : sc[1][j - 4];
             if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -366,8 +368,7 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
             float mx = x[0];
 #pragma unroll
             for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_over_row_groups(mx) * a.scale_log2e;
             // raise the reference past the headroom; on the first tile also drop a
             // unified maximum that lies far above every score
             const bool low = it == 0 && mx < m_ref - TAU;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         }
         float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? sc[0][j] : sc[1][j - 4]) * a.scale_log2e;
+        for (int j = 0; j < 8; ++j) x[j] = j < 4 ? sc[0][j] : sc[1][j - 4];  // unscaled q.k
         if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -234,8 +234,9 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         float mx = x[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // (the scale is positive: the row maximum of q.k times the scale is
+        // that of the scaled logits)
+        mx = max_over_row_groups(mx) * a.scale_log2e;
         // raise the reference past the headroom; on the first tile also drop a
         // unified maximum that lies far above every score
         const bool low = it == 0 && mx < m_ref - TAU;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(x[j] - m_sub);
+            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2e, -m_sub));
             l_run += p[j];
             const uint32_t w = j < 4 ? xv0 : xv1;
             p[j] *= pow2_scale((int)(signed char)(w >> (8 * (j & 3))));

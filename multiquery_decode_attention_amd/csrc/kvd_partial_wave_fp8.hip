@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[rb][j] = (j < 4 ? sc[rb][0][j] : sc[rb][1][j - 4]) * a.scale_log2e;
+                for (int j = 0; j < 8; ++j) x[rb][j] = j < 4 ? sc[rb][0][j] : sc[rb][1][j - 4];  // unscaled q.k
                 if (t0 + MFMA_TILE > mask_from) {
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
@@ -300,8 +300,9 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
                 float mx = x[rb][0];
 #pragma unroll
                 for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[rb][j]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // (the scale is positive: the row maximum of q.k times the
+                // scale is that of the scaled logits)
+                mx = max_over_row_groups(mx) * a.scale_log2e;
                 mxs[rb] = mx;
                 // past the headroom; on the wave's first tile also a unified
                 // maximum far above every score
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
                 float p[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(x[rb][j] - m_sub);
+                    p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][j], a.scale_log2e, -m_sub));
                     l_run[rb] += p[j];
                     p[j] *= pow2_scale((int)(signed char)((j < 4 ? xv0 : xv1) >> (8 * (j & 3))));
                 }

@@ -60,19 +60,6 @@ using namespace fp8;
 // s_waitcnt lgkmcnt(0), then s_barrier: LDS writes of every wave visible.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Maximum of x over lanes i, i^16, i^32, i^48 with gfx950's lane swaps (no
-// LDS round trip): given the same value twice, the 16-lane swap returns the
-// values of rows (0, 1) and (2, 3) in its two results, and the 32-lane swap
-// those of the two halves.
-__device__ __forceinline__ float max_over_row_groups(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t w = __float_as_uint(x);
-    const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
 template <int D, int R, int NS, bool GROUPED, bool PAGED>
 __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
     constexpr int TT = XCHG_TILE;          // tokens per tile
