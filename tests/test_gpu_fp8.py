@@ -121,7 +121,9 @@ def test_fp8_xchg_row_groups_and_edges(Hq, Hkv, D, splits):
     groups (96 rows at d = 256: two groups of three blocks; 80 at d = 128:
     two groups of three), with lengths on and next to the edges of its
     16-token blocks and 64-token tiles, so that whole blocks of a tile lie
-    past a sequence's end."""
+    past a sequence's end (lengths attended, the new token included: the
+    fused append's token lands in slots 0, 16 and 64, opening a sequence, a
+    block and a tile)."""
     lengths = [1, 15, 16, 17, 48, 63, 64, 65, 100, 129, 250]
     case = inputs.make_fp8_case(len(lengths), Hq, Hkv, D, 256, lengths, seed=150 + Hq + D)
     out, plan = check_fp8(case, Hq, f"fp8 xchg Hq={Hq} Hkv={Hkv} D={D} S={splits}", splits=splits,
