@@ -173,6 +173,24 @@ def test_fp8_capacity_overflow():
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("variant,Hq,D", [("wave", 16, 128), ("xchg", 48, 256), ("xchg", 64, 128)])
+def test_fp8_fused_step_with_out_of_range_length(variant, Hq, D):
+    """A length past capacity in a step whose append is fused into the wave
+    or exchange kernel: no append for that sequence, attention clamped to
+    capacity, KVD_ELENGTH; the other sequence steps normally."""
+    case = inputs.make_fp8_case(2, Hq, 1, D, 96, [96, 41], seed=160)
+    L_bad = torch.tensor([1000, 40], dtype=torch.int32)
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, Hq, lengths=L_bad, variant=variant)
+    assert plan["variant"] == variant
+    assert status == kvd.KVD_ELENGTH
+    assert L.cpu().tolist() == [1000, 41]
+    # sequence 0 is full in the oracle's run, so it is not appended there either
+    ref, kc2, ke2, vc2, ve2, L2 = oracle_fp8_step(case, lengths=torch.tensor([96, 40], dtype=torch.int32))
+    assert np.array_equal(kc.cpu().numpy(), kc2) and np.array_equal(ke.cpu().numpy(), ke2)
+    assert np.array_equal(vc.cpu().numpy(), vc2) and np.array_equal(ve.cpu().numpy(), ve2)
+    assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
 @pytest.mark.parametrize("phi", [0.0, -40.0, 1e4])
 def test_fp8_unified_max(phi, variant):
