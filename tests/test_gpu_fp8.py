@@ -80,6 +80,42 @@ def check_fp8(case, Hq, name, **kw):
     return out, plan
 
 
+# Workloads at full size with an fp8 cache: sequences whose attention the
+# oracle checks (None: all; else a seeded sample of that many).
+FP8_FULL = {"palm_mqa_bf16": None, "llama13b_mha_bf16": 8, "ragged_gqa_bf16": 16, "longctx_mqa_bf16": None}
+
+
+@pytest.mark.parametrize("name", list(FP8_FULL))
+def test_fp8_workload_full_size(name):
+    """Each bf16 workload's shape at full size with an fp8 cache, through the
+    one-call step the benchmark times with --kv-dtype fp8 (automatic kernel
+    and split plan, fused append): codes, exponents and lengths bit-exact on
+    the whole cache, attention against the oracle on every sequence or on a
+    seeded sample of them."""
+    w = inputs.WORKLOADS[name]
+    say(f"fp8 full {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} T_cap={w.T_cap}")
+    # drawn on the device (the cache is up to 1 GiB of codes per tensor)
+    case = inputs.make_fp8_case(w.B, w.Hq, w.Hkv, w.D, w.T_cap, inputs.attended_lengths(w), seed=w.seed,
+                                device="cuda")
+    host = [t.cpu().numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, w.Hq)
+    say(f"fp8 full {name}: gpu done, plan={plan}, status={status}")
+    assert status == kvd.KVD_OK
+    f32 = lambda t: t.float().cpu().numpy()
+    L0 = case.lengths0.cpu().numpy().astype(np.int32)
+    kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8(*host, L0, f32(case.k_new), f32(case.v_new))
+    assert np.array_equal(L.cpu().numpy(), L2)
+    for got, want, what in ((kc, kc2, "K codes"), (ke, ke2, "K exponents"), (vc, vc2, "V codes"),
+                            (ve, ve2, "V exponents")):
+        assert np.array_equal(got.cpu().numpy(), want), what
+    n = FP8_FULL[name]
+    sel = np.arange(w.B) if n is None else np.sort(np.random.default_rng(w.seed).choice(w.B, n, replace=False))
+    ref = oracle.decode_attention_fp8(f32(case.q)[sel], kc2[sel], ke2[sel], vc2[sel], ve2[sel], L2[sel], case.scale)
+    err = rel_err_rows(to_f64(out)[sel], ref)
+    say(f"fp8 full {name}: {len(sel)} sequences checked, max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+
+
 SHAPES = {  # name: (B, Hq, Hkv, D, T_cap, lengths)
     "palm_like": (3, 48, 1, 256, 2048, [2048, 1000, 33]),
     "mha_like": (2, 40, 40, 128, 4096, [4096, 1500]),
