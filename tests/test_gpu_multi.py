@@ -76,6 +76,31 @@ def check_multi(case, Hq, name, expect_status=kvd.KVD_OK, **kw):
     return out
 
 
+@pytest.mark.parametrize("name,T_q,sample", [("palm_mqa_bf16", 4, None), ("longctx_mqa_bf16", 4, None),
+                                           ("llama13b_mha_bf16", 8, 8), ("ragged_gqa_bf16", 4, 16)])
+def test_multi_token_full_size(name, T_q, sample):
+    """The workloads at full size with T_q new tokens per sequence (the
+    step `bench.py --new-tokens T_q` times, automatic plan): the append bit
+    for bit on the whole cache, attention against the oracle on every
+    sequence or on a seeded sample of them."""
+    w = inputs.WORKLOADS[name]
+    L0 = inputs.attended_lengths(w) - T_q
+    say(f"multi full {name}: B={w.B} Hq={w.Hq} T_q={T_q} T_cap={w.T_cap}")
+    case = inputs.make_multi_case(w.B, w.Hq, w.Hkv, w.D, w.T_cap, L0, T_q, w.dtype, seed=w.seed, device="cuda")
+    out, kc, vc, L, status = multi_step(case, w.Hq)
+    assert status == kvd.KVD_OK
+    k2, v2, L2, a = oracle.append_multi(inputs.host_array(case.k_cache), inputs.host_array(case.v_cache),
+                                        L0.numpy(), inputs.host_array(case.k_new), inputs.host_array(case.v_new))
+    assert np.array_equal(L, L2)
+    assert np.array_equal(kc, k2) and np.array_equal(vc, v2), "caches differ after the append"
+    sel = np.arange(w.B) if sample is None else np.sort(np.random.default_rng(w.seed).choice(w.B, sample, replace=False))
+    ref = oracle.decode_attention_multi(inputs.host_array(case.q)[sel], k2[sel], v2[sel], L2[sel], a[sel], case.scale,
+                                        oracle.BF16)
+    err = rel_err_rows(to_f64(out)[sel], ref)
+    say(f"multi full {name}: {len(sel)} sequences checked, max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+
+
 @pytest.mark.parametrize("T_q", [2, 4, 8, 16])
 @pytest.mark.parametrize("shape", ["palm_like", "gqa", "mha"])
 def test_multi_token_shapes(shape, T_q):
