@@ -116,6 +116,68 @@ def test_fp8_workload_full_size(name):
     assert err <= TOL_BF16, err
 
 
+@pytest.mark.parametrize("name,T_q,page,sample", [("longctx_mqa_bf16", 4, 0, None), ("llama13b_mha_bf16", 8, 0, 8),
+                                                  ("ragged_gqa_bf16", 1, 256, 16), ("longctx_mqa_bf16", 1, 256, None)])
+def test_fp8_workload_full_size_multi_and_paged(name, T_q, page, sample):
+    """The fp8 steps `bench.py --kv-dtype fp8` times with --new-tokens or
+    --page-size, at full size: several new tokens (the append kernel, then
+    the exchange or wave kernel over all query rows) and one new token on
+    shuffled 256-token pages (fused append through the block table).
+    Codes, exponents and lengths bit-exact on the whole cache; attention
+    against the oracle on every sequence or a seeded sample."""
+    w = inputs.WORKLOADS[name]
+    say(f"fp8 full {name}: T_q={T_q} page={page}")
+    case = inputs.make_fp8_case(w.B, w.Hq, w.Hkv, w.D, w.T_cap, inputs.attended_lengths(w), seed=w.seed + 5,
+                                device="cuda", new_tokens=T_q if T_q > 1 else None)
+    host = [t.cpu().numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
+    dev = torch.device("cuda")
+    L = case.lengths0.to(dev, torch.int32, copy=True)
+    if page:
+        table, num_pages = inputs.paged_layout(w.B, w.T_cap, page, seed=w.seed)
+        pools = [inputs.to_pages(x, table.to(x.device), page, num_pages).to(dev) for x in
+                 (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
+        bt = table.to(dev)
+    else:
+        pools = [x.to(dev, copy=True) for x in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
+        bt = None
+    kc, ke, vc, ve = pools
+    cache = kvd.KVCache(kc, vc, L, w.Hq, block_table=bt, k_exp=ke, v_exp=ve)
+    try:
+        plan = cache.plan()
+        kn, vn, q = (t.contiguous() for t in (case.k_new, case.v_new, case.q))
+        out = cache.step_multi(kn, vn, q, scale=case.scale) if T_q > 1 else cache.step(kn, vn, q, scale=case.scale)
+        status = cache.status()
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    say(f"fp8 full {name}: gpu done, plan={plan}, status={status}")
+    assert status == kvd.KVD_OK
+    got = [x.cpu().numpy() for x in (kc, ke, vc, ve)]
+    if page:
+        tb = table.numpy()
+        got = [oracle.gather_pages(got[0], tb), oracle.gather_exponent_pages(got[1], tb),
+               oracle.gather_pages(got[2], tb), oracle.gather_exponent_pages(got[3], tb)]
+    f32 = lambda t: t.float().cpu().numpy()
+    L0 = case.lengths0.cpu().numpy().astype(np.int32)
+    if T_q > 1:
+        kc2, ke2, vc2, ve2, L2, appended = oracle.append_fp8_multi(*host, L0, f32(case.k_new), f32(case.v_new))
+    else:
+        kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8(*host, L0, f32(case.k_new), f32(case.v_new))
+    assert np.array_equal(L.cpu().numpy(), L2)
+    for g, want, what in zip(got, (kc2, ke2, vc2, ve2), ("K codes", "K exponents", "V codes", "V exponents")):
+        assert np.array_equal(g, want), what
+    sel = np.arange(w.B) if sample is None else np.sort(np.random.default_rng(w.seed).choice(w.B, sample, replace=False))
+    qs = f32(case.q)[sel]
+    if T_q > 1:
+        ref = oracle.decode_attention_fp8_multi(qs, kc2[sel], ke2[sel], vc2[sel], ve2[sel], L2[sel], appended[sel],
+                                                case.scale)
+    else:
+        ref = oracle.decode_attention_fp8(qs, kc2[sel], ke2[sel], vc2[sel], ve2[sel], L2[sel], case.scale)
+    err = rel_err_rows(to_f64(out)[sel], ref)
+    say(f"fp8 full {name}: {len(sel)} sequences checked, max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+
+
 SHAPES = {  # name: (B, Hq, Hkv, D, T_cap, lengths)
     "palm_like": (3, 48, 1, 256, 2048, [2048, 1000, 33]),
     "mha_like": (2, 40, 40, 128, 4096, [4096, 1500]),
