@@ -16,7 +16,8 @@ constexpr int ERRBIT_PAGE = 4;      // a block-table entry in use was outside [0
 // (sequence b, KV head g) is row (b * Hkv + g) * T_cap + t of k_cache/v_cache.
 // Paged: the caches are a pool of pages [num_pages, Hkv, page, d] and token t
 // is row (block_table[b * max_pages + t / page] * Hkv + g) * page + t % page,
-// page = 2^page_shift >= 32 tokens, so a 32-token tile never straddles pages.
+// page = 2^page_shift >= 32 tokens, so a 32-token tile (and each 16-token
+// block of the fp8 exchange kernel's 64-token tiles) never straddles pages.
 struct KvLayout {
     const int32_t* block_table;
     int page_shift;
@@ -189,7 +190,7 @@ __device__ __forceinline__ BlockCoord block_coord(int units) {
     return c;
 }
 
-// The LDS-staged kernels' grids (bf16, and both fp8 kernels) deal work
+// The LDS-staged kernels' grids (bf16, and the three fp8 kernels) deal work
 // units to the eight XCDs in turn (block L runs on XCD L mod 8) and, on each
 // XCD, run them unit after unit, longest first: the k-th block of XCD x is
 // head group k mod G of split (k / G) mod S of unit slot k / (G * S), i.e.
