@@ -280,6 +280,22 @@ def main():
         cpu = cpu_baseline(w, copies[0], T_cap, fp8, tq)
 
     kvariant = plan["variant"] + ("_fp8" if fp8 else "")
+    # The partial pass is HBM-bound unless its arithmetic intensity passes
+    # the bf16 matrix-core ridge (peak FLOP/s over peak bytes/s, about 312
+    # FLOP/B): with many query rows per KV head (48 heads times several new
+    # tokens) it is a contraction and is measured against the matrix peak.
+    intensity = flops / partial_bytes
+    ridge = traffic.MI355X_BF16_DENSE_TFLOPS * 1e12 / (traffic.MI355X_HBM_PEAK_GBPS * 1e9)
+    tflops = flops / K / (partial_ms * 1e-3) / 1e12
+    traffic_rec = measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype, tq), kvariant)
+    if w.dtype == "bf16" and intensity > ridge:
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": traffic.MI355X_BF16_DENSE_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / traffic.MI355X_BF16_DENSE_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": traffic.MI355X_HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4)}
+    roofline.update({"traffic": traffic_rec, "kernel": f"partial_{kvariant}_kernel",
+                     "intensity_flop_per_byte": round(intensity, 1)})
     result = {
         "metric": "decode-attention KV-cache HBM GB/s (% of peak) and tokens/sec at 1 GPU",
         "value": round(value, 2),
@@ -297,17 +313,13 @@ def main():
         "pct_of_peak": round(value / traffic.MI355X_HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(w.B * tq * K / elapsed, 1),
         "kernel_us": {"partial": round(partial_ms * 1e3, 2)},
-        "partial_tflops": round(flops / K / (partial_ms * 1e-3) / 1e12, 2),
+        "partial_tflops": round(tflops, 2),
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "head_dim": w.D,
                    "T": w.T, "cache_dtype": "fp8_e4m3" if fp8 else w.dtype, "num_splits": plan["num_splits"],
                    "split_tokens": plan["split_tokens"], "variant": plan["variant"],
                    "cache_copies": R, "seed": w.seed, "page_size": args.page_size or None,
                    "new_tokens": tq},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": traffic.MI355X_HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / traffic.MI355X_HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(traffic_key(w.name, args.page_size, args.kv_dtype, tq), kvariant),
-                     "kernel": f"partial_{kvariant}_kernel"},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "device": device_info(),
     }
