@@ -45,8 +45,10 @@ KERNEL_SOURCES = {
                 "kvd_internal.h"],
     "wave_fp8": ["kvd_partial_wave_fp8.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
                  "kvd_internal.h"],
-    "xchg_fp8": ["kvd_partial_xchg_fp8.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
+    "xchg_fp8": ["kvd_partial_xchg.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
                  "kvd_internal.h"],
+    "xchg_bf16": ["kvd_partial_xchg.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
+                  "kvd_internal.h"],
     "mfma": ["kvd_partial_mfma.hip", "kvd_mfma_common.h", "kvd_internal.h"],
     "valu": ["kvd_partial_valu.hip", "kvd_internal.h"],
 }
@@ -279,7 +281,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, copies[0], T_cap, fp8, tq)
 
-    kvariant = plan["variant"] + ("_fp8" if fp8 else "")
+    # kernel name suffix: the fp8 kernels, and the exchange kernel's bf16 instance
+    kvariant = plan["variant"] + ("_fp8" if fp8 else ("_bf16" if plan["variant"] == "xchg" else ""))
     # The partial pass is HBM-bound unless its arithmetic intensity passes
     # the bf16 matrix-core ridge (peak FLOP/s over peak bytes/s, about 312
     # FLOP/B): with many query rows per KV head (48 heads times several new

@@ -41,7 +41,7 @@ FILE_FLAGS = {
     "kvd_partial_lds.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kvd_partial_lds_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "kvd_partial_wave_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "kvd_partial_xchg_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kvd_partial_xchg.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,7 +1,7 @@
-// kvd_partial_xchg_fp8.hip -- split-KV partial pass over an fp8 KV cache for
-// large query groups (many query heads per KV head, as in multiquery
-// attention), in which the four waves of a workgroup split every tile and
-// exchange the softmax weights through LDS.
+// kvd_partial_xchg.hip -- split-KV partial pass over an fp8 (or bf16) KV
+// cache for large query groups (many query heads per KV head, as in
+// multiquery attention), in which the four waves of a workgroup split every
+// tile and exchange the softmax weights through LDS.
 //
 // Work unit: (split s, sequence b, KV head g[, group hg of up to 16*R query
 // rows]) -> one workgroup of four waves, over 64-token tiles.  In the other
@@ -39,8 +39,15 @@
 // for the same reason.  At d = 256 with 48 rows this is 81408 bytes, two
 // workgroups per CU.
 //
+// The same body serves a bf16 cache (FP8 false): rows are twice as long,
+// there are no exponents and no widening, the weights are not scaled.  At
+// d = 256 a slot then holds 64 KB, one workgroup per CU; the LDS kernel,
+// which keeps every K/V tile in LDS for all four waves' row blocks, is the
+// faster choice there and the exchange kernel runs only when asked for.
+//
 // In a decode step the kernel also appends the new token: the workgroups
-// owning its tile quantize its rows into the cache slot first (below).
+// owning its tile quantize (fp8) or copy (bf16) its rows into the cache
+// slot first (below).
 //
 // Sources: quantized KV caches save memory bandwidth ("All About Transformer
 // Inference", section on tricks for generation throughput); bf16 arithmetic
@@ -60,25 +67,29 @@ using namespace fp8;
 // s_waitcnt lgkmcnt(0), then s_barrier: LDS writes of every wave visible.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D, int R, int NS, bool GROUPED, bool PAGED>
-__global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
+// The kernel body for an fp8 cache (FP8) or a bf16 cache.
+template <bool FP8, int D, int R, int NS, bool GROUPED, bool PAGED>
+__device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_groups) {
     constexpr int TT = XCHG_TILE;          // tokens per tile
-    constexpr int CH = D / 16;             // 16-byte chunks per row of codes
+    constexpr int EB = FP8 ? 1 : 2;        // bytes per cached value
+    constexpr int ROWB = D * EB;           // bytes per cache row
+    constexpr int CH = ROWB / 16;          // 16-byte chunks per row
     constexpr int SWZ = CH - 1;            // K chunk swizzle mask
     constexpr int VKEY = CH / 4;           // V chunk swizzle step per 8-token group
     constexpr int KS = D / 32;             // k-steps of the score product
     constexpr int DQ = D / 4;              // value columns per wave
     constexpr int NC = DQ / 16;            // output column blocks per wave = codes per lane and token
     constexpr int ROWS = 16 * R;           // query rows per workgroup
-    constexpr int NKV = 16 * D / 1024;     // 1 KB loads of a wave's 16 K (or V) rows
-    constexpr int REGION = TT * D;         // bytes of K (or V) codes per slot
-    constexpr int XBYTES = 4 * 256;        // exponents per slot: 256 bytes per wave
+    constexpr int NKV = 16 * ROWB / 1024;  // 1 KB loads of a wave's 16 K (or V) rows
+    constexpr int REGION = TT * ROWB;      // bytes of K (or V) rows per slot
+    constexpr int XBYTES = FP8 ? 4 * 256 : 0;  // exponents per slot: 256 bytes per wave
     constexpr int SLOT = 2 * REGION + XBYTES;
     constexpr int PST = 2 * TT;            // bytes per row of weights
     constexpr int PBUF = ROWS * PST;
     constexpr int MBUF = ROWS * 4 * 4;     // per row, the maxima of the four waves
     constexpr int P_AT = NS * SLOT, M_AT = P_AT + 2 * PBUF;
-    constexpr int PERT = 2 * NKV + 1;      // loads of a wave per tile
+    constexpr int KX = NKV + (FP8 ? 1 : 0);  // loads of a wave's K rows (and exponents) per tile
+    constexpr int PERT = NKV + KX;            // loads of a wave per tile
     static_assert(NC == 2 || NC == 4, "d = 128 or 256");
     static_assert(NS >= 2 && (NS - 1) * PERT < 64, "vmcnt range");
     __shared__ __attribute__((aligned(16))) unsigned char lds[M_AT + 2 * MBUF];
@@ -120,8 +131,14 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
                 row = kv_row_contiguous(b, g, a.Hkv, a.T_cap, sl.slot);
             const uint16_t* src = static_cast<const uint16_t*>(wave ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + g) * D;
             uint8_t* cache = static_cast<uint8_t*>(const_cast<void*>(wave ? a.v_cache : a.k_cache));
-            int8_t* exps = const_cast<int8_t*>(wave ? a.v_exp : a.k_exp);
-            quantize_row<D>(src, cache + row * D, exps + row, lane);
+            if constexpr (FP8) {
+                int8_t* exps = const_cast<int8_t*>(wave ? a.v_exp : a.k_exp);
+                quantize_row<D>(src, cache + row * D, exps + row, lane);
+            } else {  // a bit copy: lane l copies values l*D/64 .. (l+1)*D/64 - 1
+                uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + row * D;
+#pragma unroll
+                for (int i = 0; i < D / 64; ++i) dst[lane * (D / 64) + i] = src[lane * (D / 64) + i];
+            }
         }
         __syncthreads();
     }
@@ -138,8 +155,8 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     // Rows are counted from kb/vb (codes) and ke/ve (exponents, one byte per
     // row): the (b, g) slab of a contiguous cache, or the page pools.
     const size_t slab = PAGED ? 0 : kv_row_contiguous(b, g, a.Hkv, a.T_cap, 0);
-    const char* kb = static_cast<const char*>(a.k_cache) + slab * D;
-    const char* vb = static_cast<const char*>(a.v_cache) + slab * D;
+    const char* kb = static_cast<const char*>(a.k_cache) + slab * ROWB;
+    const char* vb = static_cast<const char*>(a.v_cache) + slab * ROWB;
     const char* ke = reinterpret_cast<const char*>(a.k_exp) + slab;
     const char* ve = reinterpret_cast<const char*>(a.v_exp) + slab;
     // This wave's 16-token block of tile k starts at block_t(k); a block
@@ -194,8 +211,8 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         const int t = j / CH, p = j % CH;
         const int vkey = (((16 * wave + t) >> 3) & 3) * VKEY;
         lrow[n] = t;
-        kgo[n] = (uint32_t)(t * D + 16 * (p ^ (t & SWZ)));
-        vgo[n] = (uint32_t)(t * D + 16 * (p ^ vkey));
+        kgo[n] = (uint32_t)(t * ROWB + 16 * (p ^ (t & SWZ)));
+        vgo[n] = (uint32_t)(t * ROWB + 16 * (p ^ vkey));
     }
     // Non-temporal K/V loads (each byte is read once), except where several
     // row groups read the same tiles through L2.
@@ -207,13 +224,13 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     // of one cached chunk (never read), keeps the waits' arithmetic fixed.
     auto issue_kx = [&](int k) {
         unsigned char* slot = lds + (k % NS) * SLOT;
-        unsigned char* kd = slot + 16 * wave * D;
+        unsigned char* kd = slot + 16 * wave * ROWB;
         unsigned char* xd = slot + 2 * REGION + 256 * wave;
         if (k >= n_tiles) {
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
                 __builtin_amdgcn_global_load_lds((const void*)kb, (lds_void_t*)(kd + n * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)xd, 4, 0, 0);
+            if constexpr (FP8) __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)xd, 4, 0, 0);
             return;
         }
         const int tb = block_t(k);
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         const int last = min(15, len - 1 - tb);
         v_row = r0;
         v_last = last;
-        const char* kt = kb + r0 * D;
+        const char* kt = kb + r0 * ROWB;
         if (last == 15) {  // (uniform) a whole block: a scalar base and fixed lane offsets
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
@@ -230,26 +247,28 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         } else {
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
-                __builtin_amdgcn_global_load_lds((const void*)(kt + kgo[n] + (min(lrow[n], last) - lrow[n]) * D),
+                __builtin_amdgcn_global_load_lds((const void*)(kt + kgo[n] + (min(lrow[n], last) - lrow[n]) * ROWB),
                                                  (lds_void_t*)(kd + n * 1024), 16, 0, KV_POLICY);
         }
         // lane l, q = l & 7: K exponents of rows 4q .. 4q+3 for q < 4, else V
         // exponents of rows 4(q-4) ..; lanes 8-63 repeat them.  Bytes 0-15
         // are K, 16-31 V; those of rows past the sequence's end are never
         // used (the 16 rows lie inside the cache row or page).
-        const int q = lane & 7;
-        __builtin_amdgcn_global_load_lds((const void*)((q < 4 ? ke : ve) + r0 + 4 * (q & 3)), (lds_void_t*)xd, 4,
-                                         0, 0);
+        if constexpr (FP8) {
+            const int q = lane & 7;
+            __builtin_amdgcn_global_load_lds((const void*)((q < 4 ? ke : ve) + r0 + 4 * (q & 3)), (lds_void_t*)xd, 4,
+                                             0, 0);
+        }
     };
     auto issue_v = [&](int k) {
-        unsigned char* vd = lds + (k % NS) * SLOT + REGION + 16 * wave * D;
+        unsigned char* vd = lds + (k % NS) * SLOT + REGION + 16 * wave * ROWB;
         if (k >= n_tiles) {
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
                 __builtin_amdgcn_global_load_lds((const void*)kb, (lds_void_t*)(vd + n * 1024), 16, 0, 0);
             return;
         }
-        const char* vt = vb + v_row * D;
+        const char* vt = vb + v_row * ROWB;
         if (v_last == 15) {
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
@@ -258,22 +277,29 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         } else {
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
-                __builtin_amdgcn_global_load_lds((const void*)(vt + vgo[n] + (min(lrow[n], v_last) - lrow[n]) * D),
+                __builtin_amdgcn_global_load_lds((const void*)(vt + vgo[n] + (min(lrow[n], v_last) - lrow[n]) * ROWB),
                                                  (lds_void_t*)(vd + n * 1024), 16, 0, KV_POLICY);
         }
     };
 
-    // LDS read offsets.  Score operand: K row 16*wave + c, codes 32ks + 8gq
-    // .. +7 (half of a swizzled chunk).  Value operand: V rows 8gq + j (+32
-    // for the second half of the tile), codes wave*DQ + NC*c .. +NC-1.
+    // LDS read offsets.  Score operand: K row 16*wave + c, values 32ks + 8gq
+    // .. +7 (half of a swizzled chunk of codes, or a whole chunk of bf16).
+    // Value operand: V rows 8gq + j (+32 for the second half of the tile),
+    // columns vcol .. vcol+NC-1.
     uint32_t koff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        const int p = 2 * ks + (gq >> 1);
-        koff[ks] = (uint32_t)(16 * wave * D + (c * CH + (p ^ (c & SWZ))) * 16 + 8 * (gq & 1));
+        if constexpr (FP8) {
+            const int p = 2 * ks + (gq >> 1);
+            koff[ks] = (uint32_t)(16 * wave * ROWB + (c * CH + (p ^ (c & SWZ))) * 16 + 8 * (gq & 1));
+        } else {
+            const int p = 4 * ks + gq;
+            koff[ks] = (uint32_t)(16 * wave * ROWB + (c * CH + (p ^ (c & SWZ))) * 16);
+        }
     }
-    const int vbyte = wave * DQ + NC * c;
-    const uint32_t voff = (uint32_t)(REGION + 8 * gq * D + (((vbyte >> 4) ^ (gq * VKEY)) << 4) + (vbyte & 15));
+    const int vcol = wave * DQ + NC * c;
+    const int vbyte = vcol * EB;
+    const uint32_t voff = (uint32_t)(REGION + 8 * gq * ROWB + (((vbyte >> 4) ^ (gq * VKEY)) << 4) + (vbyte & 15));
 
     f32x4_t acc[R][NC];
     float m_ref[R], l_run[R];
@@ -304,15 +330,20 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         wait_vm<(NS - 1) * PERT>();
 
         // scores of the wave's 16 tokens for every row block: each K row
-        // widened once, with its own 2^e (a row past the sequence's end
-        // holds the last row's codes: take that row's 2^e too)
-        const float sk = pow2_scale(X[min(c, len - 1 - block_t(it))]);
+        // read once (fp8: widened once, with its own 2^e; a row past the
+        // sequence's end holds the last row's codes and takes its 2^e too)
+        float sk = 1.f;
+        if constexpr (FP8) sk = pow2_scale(X[min(c, len - 1 - block_t(it))]);
         f32x4_t sc[R];
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) sc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const u32x4_t kop = widen8(*reinterpret_cast<const u32x2_t*>(slot + koff[ks]), sk);
+            u32x4_t kop;
+            if constexpr (FP8)
+                kop = widen8(*reinterpret_cast<const u32x2_t*>(slot + koff[ks]), sk);
+            else
+                kop = *reinterpret_cast<const u32x4_t*>(slot + koff[ks]);
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) sc[rb] = mfma16x16x32(kop, qop[rb][ks], sc[rb]);
         }
@@ -338,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         // 2^(x * scale - m) summed as they are, times the token's 2^e for the
         // value product.  A row with no token yet keeps m_ref = -inf and
         // weighs 0.
-        const uint32_t xv = *reinterpret_cast<const uint32_t*>(X + 16 + 4 * gq);
+        const uint32_t xv = FP8 ? *reinterpret_cast<const uint32_t*>(X + 16 + 4 * gq) : 0u;
         float lt[R];
         // weight row r holds its 16-byte chunk h at position h ^ ((r >> 1) & 7):
         // lane (c, gq) writes tokens 16*wave + 4gq .. +3 (half a chunk)
@@ -354,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
                 for (int i = 0; i < 4; ++i) {
                     p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][i], sl, -m_sub));
                     sum += p[i];
-                    p[i] *= pow2_scale((int)(signed char)(xv >> (8 * i)));
+                    if constexpr (FP8) p[i] *= pow2_scale((int)(signed char)(xv >> (8 * i)));
                 }
                 lt[rb] = sum;
                 const u32x2_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
@@ -370,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         // still be in flight); after the barrier every wave's V rows,
         // weights and maxima of tile it are visible, and every wave is past
         // its value product of tile it-1, whose V slot is refilled
-        wait_vm_barrier<(NS - 2) * PERT + NKV + 1>();
+        wait_vm_barrier<(NS - 2) * PERT + KX>();
         issue_v(it + NS - 1);
 
         // tile maxima per row, the same in every wave
@@ -412,30 +443,44 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
         for (int rb = 0; rb < R; ++rb) l_run[rb] += lt[rb];
 
         // values: the 64 tokens' weights of every row times this wave's
-        // columns of the V rows, each code widened once for all row blocks.
-        // A lane holds NC codes (its columns) of each of tokens 8gq + j; byte
-        // permutes pair tokens 2m and 2m+1 column by column before widening,
-        // so each widened dword is dword m of one column block's operand.
+        // columns of the V rows, each value read (and widened) once for all
+        // row blocks.  A lane holds NC values (its columns) of each of tokens
+        // 8gq + j.  fp8: byte permutes pair tokens 2m and 2m+1 column by
+        // column before widening, so each widened dword is dword m of one
+        // column block's operand; bf16: halfword permutes pair them.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint32_t w[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const unsigned char* vp = slot + voff + (32 * h + j) * D;
-                w[j] = NC == 4 ? *reinterpret_cast<const uint32_t*>(vp)
-                               : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
-            }
             u32x4_t vop[NC];
+            if constexpr (FP8) {
+                uint32_t w[8];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t c01 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05010400u);
-                vop[0][m] = widen2<false>(c01, 1.0f);
-                vop[1][m] = widen2<true>(c01, 1.0f);
-                if constexpr (NC == 4) {
-                    const uint32_t c23 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07030602u);
-                    vop[2][m] = widen2<false>(c23, 1.0f);
-                    vop[3][m] = widen2<true>(c23, 1.0f);
+                for (int j = 0; j < 8; ++j) {
+                    const unsigned char* vp = slot + voff + (32 * h + j) * ROWB;
+                    w[j] = NC == 4 ? *reinterpret_cast<const uint32_t*>(vp)
+                                   : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
                 }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t c01 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05010400u);
+                    vop[0][m] = widen2<false>(c01, 1.0f);
+                    vop[1][m] = widen2<true>(c01, 1.0f);
+                    if constexpr (NC == 4) {
+                        const uint32_t c23 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07030602u);
+                        vop[2][m] = widen2<false>(c23, 1.0f);
+                        vop[3][m] = widen2<true>(c23, 1.0f);
+                    }
+                }
+            } else {
+                constexpr int VW = NC / 2;  // dwords of bf16 pairs per token
+                uint32_t v[8][VW];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const unsigned char* vp = slot + voff + (32 * h + j) * ROWB;
+#pragma unroll
+                    for (int i = 0; i < VW; ++i) v[j][i] = reinterpret_cast<const uint32_t*>(vp)[i];
+                }
+#pragma unroll
+                for (int e = 0; e < NC; ++e) vop[e] = v_operand(v, e);
             }
             u32x4_t pop[R];
 #pragma unroll
@@ -474,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
             const float li = __shfl(l, 4 * gq + i);
             if (r < mg) {
                 const float inv = li > 0.f ? 1.f / li : 0.f;
-                uint16_t* o = static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D + vbyte;
+                uint16_t* o = static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D + vcol;
                 if constexpr (NC == 4) {
                     const u32x2_t w = {pack_bf16x2(acc[rb][0][i] * inv, acc[rb][1][i] * inv),
                                        pack_bf16x2(acc[rb][2][i] * inv, acc[rb][3][i] * inv)};
@@ -491,46 +536,68 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
     }
 }
 
-template <int D, int R>
+// One kernel per cache type, so traces and counters name it.
+template <int D, int R, int NS, bool GROUPED, bool PAGED>
+__global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
+    partial_xchg<true, D, R, NS, GROUPED, PAGED>(a, head_groups);
+}
+template <int D, int R, int NS, bool GROUPED, bool PAGED>
+__global__ __launch_bounds__(256, 2) void partial_xchg_bf16_kernel(PartialArgs a, int head_groups) {
+    partial_xchg<false, D, R, NS, GROUPED, PAGED>(a, head_groups);
+}
+
+template <bool FP8, int D, int R, int NS, bool GROUPED, bool PAGED>
+void launch_one(const PartialArgs& a, int groups, hipStream_t stream) {
+    const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
+    if constexpr (FP8)
+        hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
+    else
+        hipLaunchKernelGGL((partial_xchg_bf16_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
+}
+
+template <bool FP8, int D, int R>
 hipError_t launch_r(const PartialArgs& a, int groups, hipStream_t stream) {
     constexpr int NS = xchg_slots(D);
-    const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
     const bool paged = a.kv.block_table != nullptr;
     if (groups == 1) {
         if (paged)
-            hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, false, true>), grid, block, 0, stream, a, 1);
+            launch_one<FP8, D, R, NS, false, true>(a, 1, stream);
         else
-            hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, false, false>), grid, block, 0, stream, a, 1);
+            launch_one<FP8, D, R, NS, false, false>(a, 1, stream);
     } else {
         if (paged)
-            hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, true, true>), grid, block, 0, stream, a, groups);
+            launch_one<FP8, D, R, NS, true, true>(a, groups, stream);
         else
-            hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, true, false>), grid, block, 0, stream, a,
-                               groups);
+            launch_one<FP8, D, R, NS, true, false>(a, groups, stream);
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_partial_xchg_fp8(const PartialArgs& a, hipStream_t stream) {
+template <bool FP8>
+hipError_t launch_t(const PartialArgs& a, hipStream_t stream) {
     const XchgShape x = xchg_shape(a.D, a.M);
     if (a.D == 256) {
         switch (x.row_blocks) {
-            case 1: return launch_r<256, 1>(a, x.groups, stream);
-            case 2: return launch_r<256, 2>(a, x.groups, stream);
-            default: return launch_r<256, 3>(a, x.groups, stream);
+            case 1: return launch_r<FP8, 256, 1>(a, x.groups, stream);
+            case 2: return launch_r<FP8, 256, 2>(a, x.groups, stream);
+            default: return launch_r<FP8, 256, 3>(a, x.groups, stream);
         }
     }
     if (a.D == 128) {
         switch (x.row_blocks) {
-            case 1: return launch_r<128, 1>(a, x.groups, stream);
-            case 2: return launch_r<128, 2>(a, x.groups, stream);
-            case 3: return launch_r<128, 3>(a, x.groups, stream);
-            default: return launch_r<128, 4>(a, x.groups, stream);
+            case 1: return launch_r<FP8, 128, 1>(a, x.groups, stream);
+            case 2: return launch_r<FP8, 128, 2>(a, x.groups, stream);
+            case 3: return launch_r<FP8, 128, 3>(a, x.groups, stream);
+            default: return launch_r<FP8, 128, 4>(a, x.groups, stream);
         }
     }
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_partial_xchg(const PartialArgs& a, bool fp8, hipStream_t stream) {
+    return fp8 ? launch_t<true>(a, stream) : launch_t<false>(a, stream);
 }
 
 }  // namespace kvd

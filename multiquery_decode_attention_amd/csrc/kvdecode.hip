@@ -112,7 +112,7 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
         sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(h->d.head_dim);
     } else if (variant == KVD_VARIANT_XCHG) {
         sh.units = bkv * kvd::xchg_shape(h->d.head_dim, rows).groups;
-        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(h->d.head_dim);
+        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(h->d.head_dim, is_fp8(h), rows);
     } else if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((rows + 63) / 64);
         sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
@@ -367,7 +367,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
     hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, st)
-                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg_fp8(a, st)
+                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg(a, is_fp8(h), st)
                    : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, st)
                    : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
@@ -602,7 +602,8 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
         h->variant_req = variant;
         return KVD_OK;
     }
-    if (variant == KVD_VARIANT_WAVE || variant == KVD_VARIANT_XCHG) return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_XCHG && (h->d.dtype != KVD_BF16 || h->d.head_dim < 128)) return KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;

@@ -19,7 +19,8 @@ from gpu_helpers import gpu_step, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS}
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS,
+            "xchg": kvd.KVD_VARIANT_XCHG}
 
 
 def multi_step(case, Hq, *, variant="auto", splits=None, page_size=0, reserve=0):
