@@ -346,3 +346,41 @@ def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D):
         cache.close()
     assert np.array_equal(L.cpu().numpy(), L_ref)
     assert np.array_equal(inputs.host_array(kc), k_ref) and np.array_equal(inputs.host_array(vc), v_ref)
+
+
+@pytest.mark.parametrize("variant", ["lds", "valu"])
+def test_batch_past_the_sort_limit(variant):
+    """2100 sequences (more than the combine's length sort takes, so every
+    step dispatches in batch order) with ragged short lengths, over two
+    consecutive steps on one handle; 2000 sequences (sorted dispatch from the
+    second step on) alongside."""
+    for B in (2100, 2000):
+        g = torch.Generator().manual_seed(B)
+        lengths = torch.randint(0, 62, (B,), generator=g).to(torch.int32)
+        case = inputs.make_case(B, 8, 1, 64, 64, lengths + 1, "bf16", seed=B)
+        dev = torch.device("cuda")
+        kc, vc = case.k_cache.to(dev, copy=True), case.v_cache.to(dev, copy=True)
+        L = lengths.to(dev, copy=True)
+        cache = kvd.KVCache(kc, vc, L, 8)
+        cache.set_variant(VARIANTS[variant])
+        k_ref, v_ref, L_ref = inputs.host_array(case.k_cache), inputs.host_array(case.v_cache), lengths.numpy().copy()
+        try:
+            for step in range(2):
+                gs = torch.Generator().manual_seed(7 * step + B)
+                kn = torch.randn(B, 1, 64, generator=gs).to(torch.bfloat16)
+                vn = torch.randn(B, 1, 64, generator=gs).to(torch.bfloat16)
+                q = torch.randn(B, 8, 64, generator=gs).to(torch.bfloat16)
+                say(f"batch {B} {variant}: step {step}")
+                out = cache.step(kn.to(dev), vn.to(dev), q.to(dev), scale=0.125)
+                k_ref, v_ref, L_ref, _ = oracle.append(k_ref, v_ref, L_ref, inputs.host_array(kn),
+                                                       inputs.host_array(vn))
+                ref = oracle.decode_attention(inputs.host_array(q), k_ref, v_ref, L_ref, 0.125, oracle.BF16)
+                torch.cuda.synchronize()
+                assert cache.status() == kvd.KVD_OK
+                assert np.array_equal(L.cpu().numpy(), L_ref)
+                assert np.array_equal(inputs.host_array(kc), k_ref)
+                err = rel_err_rows(to_f64(out), ref)
+                say(f"batch {B} {variant}: step {step} max row-relative error {err:.3e}")
+                assert err <= TOL_BF16, err
+        finally:
+            cache.close()
