@@ -384,3 +384,41 @@ def test_batch_past_the_sort_limit(variant):
                 assert err <= TOL_BF16, err
         finally:
             cache.close()
+
+
+def test_cache_past_4_gib():
+    """An MHA cache of 5.4 GB per tensor (64 sequences, 40 KV heads, 8192
+    tokens, d = 128): byte offsets of the later sequences pass 2^32.  One
+    decode step at full length on the automatic plan; the first, a middle
+    and the last sequence are checked against the oracle on their own
+    slices (append bit for bit, attention to the bf16 tolerance)."""
+    B, H, T, D = 64, 40, 8192, 128
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(4321)
+    kc = torch.randn(B, H, T, D, generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn(B, H, T, D, generator=g, device=dev).to(torch.bfloat16)
+    assert kc.numel() * 2 > 2 ** 32
+    lengths = torch.randint(T - 64, T, (B,), generator=g, device=dev).to(torch.int32)
+    kn, vn = (torch.randn(B, H, D, generator=g, device=dev).to(torch.bfloat16) for _ in range(2))
+    q = torch.randn(B, H, D, generator=g, device=dev).to(torch.bfloat16)
+    picks = [0, B // 2, B - 1]
+    before = {b: (inputs.host_array(kc[b:b + 1]), inputs.host_array(vc[b:b + 1])) for b in picks}
+    L0 = lengths.cpu().numpy()
+    cache = kvd.KVCache(kc, vc, lengths, H)
+    try:
+        say(f"cache past 4 GiB: B={B} H={H} T={T} D={D} plan={cache.plan()}")
+        out = cache.step(kn, vn, q, scale=D ** -0.5)
+        torch.cuda.synchronize()
+        assert cache.status() == kvd.KVD_OK
+    finally:
+        cache.close()
+    assert np.array_equal(lengths.cpu().numpy(), L0 + 1)
+    for b in picks:
+        k1, v1, L1, _ = oracle.append(*before[b], L0[b:b + 1], inputs.host_array(kn[b:b + 1]),
+                                      inputs.host_array(vn[b:b + 1]))
+        assert np.array_equal(inputs.host_array(kc[b:b + 1]), k1) and np.array_equal(inputs.host_array(vc[b:b + 1]), v1)
+        ref = oracle.decode_attention(inputs.host_array(q[b:b + 1]), k1, v1, L1, D ** -0.5, oracle.BF16)
+        err = rel_err_rows(to_f64(out[b:b + 1]), ref)
+        say(f"cache past 4 GiB: sequence {b} max row-relative error {err:.3e}")
+        assert err <= TOL_BF16, err
+    del kc, vc
