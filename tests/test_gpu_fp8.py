@@ -498,3 +498,34 @@ def test_fp8_multi_token_empty_splits(variant, splits):
 def test_fp8_multi_token_paged_and_overflow():
     fp8_multi_check(3, 48, 1, 256, 512, [200, 33, 480], 4, "paged", page=64)
     fp8_multi_check(3, 16, 2, 128, 128, [126, 124, 10], 4, "overflow", expect=kvd.KVD_ECAPACITY)
+
+
+def test_fp8_cache_past_4_gib():
+    """An fp8 MHA cache of 5.4 GB of codes per tensor (128 sequences, 40 KV
+    heads, 8192 tokens, d = 128): code offsets of the later sequences pass
+    2^32.  One fused step on the automatic plan; the first, a middle and the
+    last sequence are checked against the oracle on their own slices."""
+    B, H, T, D = 128, 40, 8192, 128
+    L_att = torch.full((B,), T, dtype=torch.int32)
+    L_att[1::2] = T - 100
+    case = inputs.make_fp8_case(B, H, H, D, T, L_att, seed=4322, device="cuda")
+    assert case.k_codes.numel() > 2 ** 32
+    picks = [0, B // 2, B - 1]
+    sl = lambda t, b: t[b:b + 1].cpu().numpy()
+    before = {b: [sl(t, b) for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)] for b in picks}
+    say(f"fp8 cache past 4 GiB: B={B} H={H} T={T} D={D}")
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, H)
+    say(f"fp8 cache past 4 GiB: gpu done, plan={plan}, status={status}")
+    assert status == kvd.KVD_OK
+    L0 = case.lengths0.cpu().numpy().astype(np.int32)
+    assert np.array_equal(L.cpu().numpy(), L0 + 1)
+    f32 = lambda t, b: t[b:b + 1].float().cpu().numpy()
+    for b in picks:
+        kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8(*before[b], L0[b:b + 1], f32(case.k_new, b), f32(case.v_new, b))
+        for got, want, what in ((kc, kc2, "K codes"), (ke, ke2, "K exponents"), (vc, vc2, "V codes"),
+                                (ve, ve2, "V exponents")):
+            assert np.array_equal(sl(got, b), want), (what, b)
+        ref = oracle.decode_attention_fp8(f32(case.q, b), kc2, ke2, vc2, ve2, L2, case.scale)
+        err = rel_err_rows(to_f64(out[b:b + 1]), ref)
+        say(f"fp8 cache past 4 GiB: sequence {b} max row-relative error {err:.3e}")
+        assert err <= TOL_BF16, err
