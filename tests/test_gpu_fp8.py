@@ -529,3 +529,5 @@ def test_fp8_cache_past_4_gib():
         err = rel_err_rows(to_f64(out[b:b + 1]), ref)
         say(f"fp8 cache past 4 GiB: sequence {b} max row-relative error {err:.3e}")
         assert err <= TOL_BF16, err
+    del case, out, kc, ke, vc, ve
+    torch.cuda.empty_cache()  # return the 22 GB to the device for the tests after this one

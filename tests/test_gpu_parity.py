@@ -421,4 +421,5 @@ def test_cache_past_4_gib():
         err = rel_err_rows(to_f64(out[b:b + 1]), ref)
         say(f"cache past 4 GiB: sequence {b} max row-relative error {err:.3e}")
         assert err <= TOL_BF16, err
-    del kc, vc
+    del kc, vc, out, cache
+    torch.cuda.empty_cache()  # return the 11 GB to the device for the tests after this one
