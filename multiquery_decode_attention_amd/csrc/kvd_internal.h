@@ -341,9 +341,10 @@ constexpr int xchg_lds_bytes(int D, bool fp8, int row_blocks) {
     return xchg_slots(D) * (2 * XCHG_TILE * D * (fp8 ? 1 : 2) + (fp8 ? 1024 : 0)) +
            2 * 16 * row_blocks * (2 * XCHG_TILE + 16);
 }
-// Workgroups per CU: at most two (the kernel keeps to 256 registers per
-// lane), fewer where the LDS of two exceeds the CU's 160 KB (bf16 rows of
-// 512 bytes at d = 256: one).
+// Workgroups per CU: at most two (the fp8 instances keep to 256 registers
+// per lane), fewer where the LDS of two exceeds the CU's 160 KB (bf16 rows
+// of 512 bytes at d = 256: one, whose three-block instance also takes more
+// than 256 registers, so one wave per SIMD).
 inline int xchg_groups_per_cu(int D, bool fp8, int rows) {
     const int g = LDS_BYTES_PER_CU / xchg_lds_bytes(D, fp8, xchg_shape(D, rows).row_blocks);
     return g < 1 ? 1 : (g > 2 ? 2 : g);
