@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "longctx_mqa_bf16"
 MIN_ROTATION_BYTES = 2 << 30  # cycle >= 2 GiB of caches per round of steps
+CPU_BASELINE_SECONDS = 10.0  # oracle time spent on the CPU baseline
 
 
 def log(*a):
@@ -359,8 +360,9 @@ def calibrate_copy(mib: int, reps: int):
 
 
 def cpu_baseline(w, copy, T_cap, fp8=False, tq=1):
-    """The fp64 oracle (test infrastructure) on one full step of the same
-    workload: the first copy's cache as it now stands, attended once."""
+    """The fp64 oracle (test infrastructure) on whole steps of the same
+    workload: the first copy's cache as it now stands, attended again and
+    again until about CPU_BASELINE_SECONDS have run (at least once)."""
     import numpy as np
     import oracle
     from multiquery_decode_attention_amd import inputs, traffic
@@ -372,29 +374,34 @@ def cpu_baseline(w, copy, T_cap, fp8=False, tq=1):
     if fp8:
         host = [t.cpu().numpy() for t in (case.k_codes, case.k_exp, case.v_codes, case.v_exp)]
         q = case.q.float().cpu().numpy()
-        t0 = time.perf_counter()
-        if tq > 1:
-            oracle.decode_attention_fp8_multi(q, *host, L, np.full(w.B, tq), case.scale, threads=threads)
-        else:
-            oracle.decode_attention_fp8(q, *host, L, case.scale, threads=threads)
-        sec = time.perf_counter() - t0
+        def run():
+            if tq > 1:
+                oracle.decode_attention_fp8_multi(q, *host, L, np.full(w.B, tq), case.scale, threads=threads)
+            else:
+                oracle.decode_attention_fp8(q, *host, L, case.scale, threads=threads)
         b = traffic.kv_read_bytes_fp8(w.Hkv, w.D, L.tolist()) + 2 * w.B * w.Hq * tq * w.D * 2
     else:
         k = inputs.host_array(case.k_cache)
         v = inputs.host_array(case.v_cache)
         q = inputs.host_array(case.q)
         dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
-        t0 = time.perf_counter()
-        if tq > 1:
-            oracle.decode_attention_multi(q, k, v, L, np.full(w.B, tq), case.scale, dt, threads=threads)
-        else:
-            oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
-        sec = time.perf_counter() - t0
+        def run():
+            if tq > 1:
+                oracle.decode_attention_multi(q, k, v, L, np.full(w.B, tq), case.scale, dt, threads=threads)
+            else:
+                oracle.decode_attention(q, k, v, L, case.scale, dt, threads=threads)
         b = traffic.attend_bytes(w.B, w.Hq * tq, w.Hkv, w.D, w.elem_bytes, L.tolist())
-    log(f"cpu baseline: {sec:.2f} s for one step")
+    # whole attend steps, repeated until about CPU_BASELINE_SECONDS have run
+    runs, t0 = 0, time.perf_counter()
+    while runs == 0 or time.perf_counter() - t0 < CPU_BASELINE_SECONDS:
+        run()
+        runs += 1
+    total = time.perf_counter() - t0
+    sec = total / runs
+    log(f"cpu baseline: {runs} steps in {total:.1f} s, {sec:.2f} s per step")
     return {"value": round(b / sec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full attend step of {w.name} (B={w.B}, all {w.Hq} heads, "
-                      f"{int(L.sum())} cached tokens), fp64, {sec:.2f} s",
+            "sample": f"{runs} full attend steps of {w.name} (B={w.B}, all {w.Hq} heads, "
+                      f"{int(L.sum())} cached tokens each), fp64, {total:.1f} s in all, {sec:.2f} s per step",
             "tokens_per_s": round(w.B * tq / sec, 2)}
 
 

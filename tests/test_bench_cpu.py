@@ -51,3 +51,20 @@ def test_traffic_keys():
     assert bench.traffic_key("longctx_mqa_bf16") == "longctx_mqa_bf16"
     assert bench.traffic_key("ragged_gqa_bf16", 256) == "ragged_gqa_bf16_paged256"
     assert bench.traffic_key("palm_mqa_bf16", 0, "fp8", 4) == "palm_mqa_bf16_fp8_tq4"
+
+
+def test_cpu_baseline_repeats_whole_steps(monkeypatch):
+    """The oracle baseline on the tiny workload's shape, on host tensors:
+    whole steps repeated until the time budget has run, rates consistent
+    with the step count."""
+    import torch
+    from multiquery_decode_attention_amd import inputs
+    w = inputs.WORKLOADS["tiny_mqa_f32"]
+    case = inputs.make_workload_case(w, device="cpu")
+    copy = {"case": case, "len": (case.lengths0 + 1).tolist()}
+    monkeypatch.setattr(bench, "CPU_BASELINE_SECONDS", 0.3)
+    r = bench.cpu_baseline(w, copy, w.T_cap)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] >= 1 and r["value"] > 0
+    runs = int(r["sample"].split()[0])
+    assert runs >= 1 and "full attend steps of tiny_mqa_f32" in r["sample"]
+    assert r["tokens_per_s"] > 0 and isinstance(case.q, torch.Tensor)
