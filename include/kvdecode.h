@@ -73,7 +73,7 @@ typedef enum {
     KVD_ECAPACITY = -4,    /* (from kvdecode_status) an append found a sequence already at capacity */
     KVD_EHIP = -5,         /* a HIP runtime call or kernel launch failed */
     KVD_ENOMEM = -6,       /* host or device allocation failed */
-    KVD_ELENGTH = -7,      /* (from kvdecode_status) attend found lengths[b] outside [0, capacity] */
+    KVD_ELENGTH = -7,      /* (from kvdecode_status) an append or attend found lengths[b] outside [0, capacity] */
     KVD_EPAGE = -8         /* (from kvdecode_status) a block-table entry in use was outside [0, num_pages) */
 } kvd_status_t;
 
@@ -176,11 +176,15 @@ typedef struct {
  *
  * `cache` describes the codes: dtype KVD_FP8_E4M3, k_cache / v_cache
  * [B, Hkv, T_cap, d] uint8, capacity a multiple of 32.  q, k_new, v_new and
- * out are bf16.  An append quantizes each new K (and V) row: e is the
- * smallest integer with max|x| <= 448 * 2^e (clamped to [-127, 127]; 0 for
+ * out are bf16.  Stored exponents lie in [-117, 119], the range in which
+ * every code * 2^e is zero or a finite normal bf16 number, so attention
+ * reads the dequantized cache exactly; an exponent outside it is read as
+ * the nearest bound.  An append quantizes each new K (and V) row: e is the
+ * smallest integer with max|x| <= 448 * 2^e (clamped to [-117, 119]; 0 for
  * an all-zero row) and each value becomes the code nearest to x * 2^-e
- * (ties to the even code).  Attention reads code * 2^e: exact in bf16 for
- * every e that keeps the values within bf16's normal range.  Callers that
+ * (ties to the even code; +-448 when e was clamped at 119, so values
+ * beyond 448 * 2^119 saturate, and 0 below 2^-127 when it was clamped at
+ * -117).  Products and sums are fp32, as for a bf16 cache.  Callers that
  * write the cache themselves (prefill) must follow the same format.  The
  * partial pass runs on the fp8 WAVE, XCHG or LDS kernel
  * (kvdecode_set_variant); kvdecode_create_fp8_paged takes the same format

@@ -12,10 +12,19 @@ namespace fp8 {
 using mfma::u32x2_t;
 using mfma::u32x4_t;
 
-// 2^e as an fp32 whose exponent field is e + 127 (e in [-127, 127]); the
-// scaled conversions read only that field.
+// Range of the stored row exponents.  Every code * 2^e in it is zero or a
+// finite normal bf16 number -- the smallest subnormal code, 2^-9, times
+// 2^-117 is 2^-126, bf16's smallest normal value, and the largest, 448, times
+// 2^119 is 1.75 * 2^127 -- so widened operands and scaled weights hold the
+// dequantized cache exactly.  The append clamps to it; an exponent stored
+// outside it is read as the nearest bound.
+constexpr int EXP_MIN = -117;
+constexpr int EXP_MAX = 119;
+
+// 2^e as an fp32 whose exponent field is e + 127, for e clamped to
+// [EXP_MIN, EXP_MAX]; the scaled conversions read only that field.
 __device__ __forceinline__ float pow2_scale(int e) {
-    e = max(-127, min(127, e));
+    e = max(EXP_MIN, min(EXP_MAX, e));
     return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
 }
 
@@ -60,21 +69,23 @@ __device__ inline uint32_t e4m3_encode(float y) {
     return sign | code;
 }
 
-// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax 0.
-// With amax = m * 2^k, m in [1, 2): e = k - 8, plus 1 when m > 1.75.
+// Smallest e with amax <= 448 * 2^e, clamped to [EXP_MIN, EXP_MAX]; 0 for
+// amax 0.  With amax = m * 2^k, m in [1, 2): e = k - 8, plus 1 when m > 1.75.
 __device__ inline int e4m3_row_exponent(float amax) {
     if (!(amax > 0.f)) return 0;
     const uint32_t b = __float_as_uint(amax);
     const int E = (int)(b >> 23);
-    if (E == 0) return -127;  // subnormal amax: far below the clamp
+    if (E == 0) return EXP_MIN;  // subnormal amax: far below the clamp
     const int e = E - 127 - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    return max(-127, min(127, e));
+    return max(EXP_MIN, min(EXP_MAX, e));
 }
 
 // Quantizing append of one row, by the 64 lanes of a wave: the row's largest
 // magnitude gives its exponent e (a wave reduction), every value becomes the
-// code of x * 2^-e (exact scaling); lane l handles values l*D/64 ..
-// (l+1)*D/64 - 1 of the bf16 row src, the codes go to dst and e to *xdst.
+// code of x * 2^-e (exact scaling; saturated at +-448 when e was clamped at
+// EXP_MAX, and rounded to 0 below half the smallest code when it was
+// clamped at EXP_MIN); lane l handles values l*D/64 .. (l+1)*D/64 - 1 of
+// the bf16 row src, the codes go to dst and e to *xdst.
 template <int D>
 __device__ inline void quantize_row(const uint16_t* src, uint8_t* dst, int8_t* xdst, int lane) {
     constexpr int PER = D / 64;
@@ -89,7 +100,8 @@ __device__ inline void quantize_row(const uint16_t* src, uint8_t* dst, int8_t* x
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     const int e = e4m3_row_exponent(amax);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) dst[lane * PER + i] = (uint8_t)e4m3_encode(ldexpf(y[i], -e));
+    for (int i = 0; i < PER; ++i)
+        dst[lane * PER + i] = (uint8_t)e4m3_encode(fminf(fmaxf(ldexpf(y[i], -e), -448.f), 448.f));
     if (lane == 0) *xdst = (int8_t)e;
 }
 

@@ -187,24 +187,45 @@ class Fp8Case:
 
 
 def _e4m3_codes(shape, gen, device):
-    """Random finite E4M3 codes: uniform sign and mantissa, exponent field
-    8..15 (magnitudes 2 .. 448, where a row scaled to its largest value
-    puts most codes); the NaN pattern S.1111.111 is mapped to S.1111.110."""
+    """Random finite E4M3 codes: uniform sign, exponent field 0..15 and
+    mantissa, so every finite code -- the subnormals of field 0 and zero
+    included -- is drawn; the NaN pattern S.1111.111 is mapped to
+    S.1111.110."""
     S = torch.randint(0, 2, shape, generator=gen, device=device, dtype=torch.int32)
-    E = torch.randint(8, 16, shape, generator=gen, device=device, dtype=torch.int32)
+    E = torch.randint(0, 16, shape, generator=gen, device=device, dtype=torch.int32)
     M = torch.randint(0, 8, shape, generator=gen, device=device, dtype=torch.int32)
     M = torch.where((E == 15) & (M == 7), torch.full_like(M, 6), M)
     return ((S << 7) | (E << 3) | M).to(torch.uint8)
 
 
+# Stored row exponents of the fp8 cache format: [-117, 119].
+FP8_EXP_MIN, FP8_EXP_MAX = -117, 119
+
+
+def _row_exponents(shape, gen, device, lo, hi, wide_lo, wide_hi):
+    """Per-row exponents: 7 of 8 rows uniform on [lo, hi], the rest uniform
+    on [wide_lo, wide_hi]."""
+    base = torch.randint(lo, hi + 1, shape, generator=gen, device=device, dtype=torch.int32)
+    wide = torch.randint(wide_lo, wide_hi + 1, shape, generator=gen, device=device, dtype=torch.int32)
+    pick = torch.randint(0, 8, shape, generator=gen, device=device, dtype=torch.int32) == 0
+    return torch.where(pick, wide, base).to(torch.int8)
+
+
 def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu",
-                  new_tokens: Optional[int] = None) -> Fp8Case:
+                  new_tokens: Optional[int] = None, k_exp_value: Optional[int] = None,
+                  v_exp_value: Optional[int] = None) -> Fp8Case:
     """Seeded fp8-cache case: the cache is drawn directly as codes and
     exponents (no quantization here: that is the method's own step, done by
     the append under test and by the oracle); q and the new rows are N(0,1)
-    rounded to bf16.  With ``new_tokens`` T the step appends T rows per
-    sequence (k_new, v_new [B, Hkv, T, D], q [B, Hq, T, D]) and the lengths
-    before it are lengths_attended - T."""
+    rounded to bf16.  Codes cover every finite E4M3 code.  Row exponents:
+    keys mostly in [-12, -4] with one row in eight at the bottom of the
+    stored range, [-117, -100] (keys that score about 0); values mostly in
+    [-12, -4] with one row in eight anywhere in [-117, 32] (32 keeps the
+    fp32 sums of weighted values far from overflow at any length).
+    ``k_exp_value`` / ``v_exp_value`` instead give every row that exponent.
+    With ``new_tokens`` T the step appends T rows per sequence (k_new, v_new
+    [B, Hkv, T, D], q [B, Hq, T, D]) and the lengths before it are
+    lengths_attended - T."""
     T = 1 if new_tokens is None else int(new_tokens)
     extra = () if new_tokens is None else (T,)
     lengths_attended = torch.as_tensor(lengths_attended, dtype=torch.int32).cpu()
@@ -214,8 +235,12 @@ def make_fp8_case(B, Hq, Hkv, D, T_cap, lengths_attended, seed, device="cpu",
     q = _normal((B, Hq) + extra + (D,), gen, device, torch.bfloat16)
     k_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
     v_codes = _e4m3_codes((B, Hkv, T_cap, D), gen, device)
-    k_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
-    v_exp = torch.randint(-9, -4, (B, Hkv, T_cap), generator=gen, device=device, dtype=torch.int32).to(torch.int8)
+    k_exp = _row_exponents((B, Hkv, T_cap), gen, device, -12, -4, FP8_EXP_MIN, -100)
+    v_exp = _row_exponents((B, Hkv, T_cap), gen, device, -12, -4, FP8_EXP_MIN, 32)
+    if k_exp_value is not None:
+        k_exp = torch.full_like(k_exp, int(k_exp_value))
+    if v_exp_value is not None:
+        v_exp = torch.full_like(v_exp, int(v_exp_value))
     k_new = _normal((B, Hkv) + extra + (D,), gen, device, torch.bfloat16)
     v_new = _normal((B, Hkv) + extra + (D,), gen, device, torch.bfloat16)
     assert int(lengths_attended.min()) >= T

@@ -101,7 +101,14 @@ def load(path: str | None = None):
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Threads for the oracle: the CPUs this process may run on, or fewer
+    when OMP_NUM_THREADS sets the host's share."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    except ValueError:
+        share = 0
+    return max(1, min(n, share) if share > 0 else n)
 
 
 def _as_bits(a: np.ndarray, dtype: int) -> np.ndarray:
@@ -226,8 +233,13 @@ def decode_attention_paged(q, k_pages, v_pages, block_table, lengths, scale, dty
 # --- fp8 (OCP E4M3) cache ----------------------------------------------------
 
 E4M3_MAX = 448.0
-E4M3_EXP_MIN = -127  # range of the stored power-of-two exponents (int8)
-E4M3_EXP_MAX = 127
+# Range of the stored power-of-two exponents.  The pages fix no scale format;
+# this library's reading keeps every code * 2^e zero or a finite normal
+# bfloat16 number: the smallest subnormal code 2^-9 times 2^-117 is 2^-126
+# (the smallest normal bf16), and 448 * 2^119 = 1.75 * 2^127 is below the
+# largest bf16.  An append clamps each row's exponent into it.
+E4M3_EXP_MIN = -117
+E4M3_EXP_MAX = 119
 
 
 def e4m3_value(code: int) -> float:
@@ -272,8 +284,9 @@ def quantize_rows(x):
     """Quantize each row (last axis) of x to (codes uint8, exponent int8).
 
     e is the smallest integer with max|x| <= 448 * 2^e, clamped to
-    [-127, 127] (0 for an all-zero row); codes are x / 2^e rounded to
-    E4M3.  x must be finite.
+    [E4M3_EXP_MIN, E4M3_EXP_MAX] (0 for an all-zero row); codes are x / 2^e
+    rounded to E4M3, saturated at +-448 when e was clamped at the top.  x
+    must be finite.
     """
     x = np.asarray(x, dtype=np.float64)
     amax = np.max(np.abs(x), axis=-1)

@@ -245,6 +245,76 @@ def test_fp8_append_extremes():
     check_fp8(case, Hq, "fp8 append extremes")
 
 
+@pytest.mark.parametrize("variant", ["wave", "lds", "xchg"])
+@pytest.mark.parametrize("k_e,v_e", [(-117, -117), (-6, -117), (-117, 64), (-4, 64)])
+def test_fp8_exponent_range_edges(variant, k_e, v_e):
+    """Every cached row at one exponent, at or near the ends of the stored
+    range [-117, 119], over every finite code (subnormals included): keys at
+    -117 score about 0 (uniform weights), values at -117 are the smallest
+    normal bf16 numbers the format holds (weights times 2^-117), values at 64
+    are large but keep the fp32 sums finite.  The kernels read code * 2^e
+    exactly at either end."""
+    B, Hq, Hkv, D, T = 2, 48, 1, 256, 256
+    if variant == "lds" or variant == "wave":
+        Hq = 16
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, [200, 77], seed=300 + k_e + v_e, k_exp_value=k_e,
+                                v_exp_value=v_e)
+    # the appended rows on the same scale (N(0,1) rows quantize to about 2^-7)
+    case.k_new = (case.k_new.float() * 2.0 ** (k_e + 7)).to(torch.bfloat16)
+    case.v_new = (case.v_new.float() * 2.0 ** (v_e + 7)).to(torch.bfloat16)
+    check_fp8(case, Hq, f"fp8 exponent edge k_e={k_e} v_e={v_e} {variant}", variant=variant)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_fp8_append_exponent_clamp(fused):
+    """New rows whose exponent falls outside the stored range: a row of
+    values around 1e-36 takes exponent -117 (values below 2^-127 become 0), a
+    row near bf16's largest value takes 119 and saturates at +-448; codes,
+    exponents and lengths bit-exact against the oracle's append (through the
+    separate append kernel, or the wave kernel's fused append)."""
+    B, Hq, Hkv, D, T = 2, 8, 2, 128, 64
+    case = inputs.make_fp8_case(B, Hq, Hkv, D, T, [10, 20], seed=310)
+    kn = case.k_new.float()
+    kn[0, 0] *= 1e-36
+    kn[0, 1] = torch.linspace(-1.0, 1.0, D) * 3.3e38
+    # largest 2^-109 gives exponent -117 exactly: 2^-126 becomes the smallest
+    # code, 2^-128 rounds to 0, -2^-127 is a tie and goes to the even code -0
+    kn[1, 0] = torch.tensor([2.0 ** -109, -(2.0 ** -127), 2.0 ** -128, 2.0 ** -126] * (D // 4))
+    case.k_new = kn.to(torch.bfloat16)
+    vn = case.v_new.float()
+    vn[1, 1] *= 3e-38
+    case.v_new = vn.to(torch.bfloat16)
+    dev = torch.device("cuda")
+    kc, vc = case.k_codes.to(dev, copy=True), case.v_codes.to(dev, copy=True)
+    ke, ve = case.k_exp.to(dev, copy=True), case.v_exp.to(dev, copy=True)
+    L = case.lengths0.to(dev, copy=True)
+    cache = kvd.KVCache(kc, vc, L, Hq, k_exp=ke, v_exp=ve)
+    try:
+        cache.set_variant(kvd.KVD_VARIANT_WAVE)
+        kn_d, vn_d = case.k_new.to(dev).contiguous(), case.v_new.to(dev).contiguous()
+        if fused:
+            # keys near bf16's largest value make some logits infinite: only
+            # the cache is compared here
+            cache.step(kn_d, vn_d, case.q.to(dev).contiguous(), scale=case.scale)
+        else:
+            cache.append(kn_d, vn_d)
+        status = cache.status()
+        torch.cuda.synchronize()
+    finally:
+        cache.close()
+    assert status == kvd.KVD_OK
+    f32 = lambda t: t.float().cpu().numpy()
+    kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8(case.k_codes.numpy(), case.k_exp.numpy(), case.v_codes.numpy(),
+                                                  case.v_exp.numpy(), case.lengths0.numpy().astype(np.int32),
+                                                  f32(case.k_new), f32(case.v_new))
+    assert ke2[0, 0, 9] == -117 and ke2[0, 1, 9] == 119, (ke2[0, 0, 9], ke2[0, 1, 9])
+    assert ke2[1, 0, 19] == -117 and kc2[1, 0, 19, :4].tolist() == [0x78, 0x80, 0x00, 0x01]
+    assert np.array_equal(L.cpu().numpy(), L2)
+    for got, want, what in ((kc, kc2, "K codes"), (ke, ke2, "K exponents"), (vc, vc2, "V codes"),
+                            (ve, ve2, "V exponents")):
+        assert np.array_equal(got.cpu().numpy(), want), what
+
+
 @pytest.mark.parametrize("name,B,Hq,Hkv,D,variant", [("mha", 2, 8, 8, 128, "wave"), ("gqa", 2, 64, 8, 128, "wave"),
                                                       ("mqa48_d128", 2, 48, 1, 128, "wave"),
                                                       ("mqa64_d128", 2, 64, 1, 128, "xchg"),

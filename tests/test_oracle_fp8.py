@@ -94,6 +94,39 @@ def test_quantize_exponent_is_minimal_and_error_bounded():
     assert np.all(err <= bound)
 
 
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+BF16_MIN_NORMAL = 2.0 ** -126
+
+
+def test_exponent_range_keeps_values_bf16_normal():
+    """The stored exponent range is the reading that every code * 2^e is
+    zero or a finite normal bf16 number, and it is the widest such range:
+    one step further down the smallest code leaves bf16's normal range, one
+    step up the largest code exceeds bf16's largest value."""
+    vals = np.abs(oracle.E4M3_TABLE[np.isfinite(oracle.E4M3_TABLE)])
+    nz = vals[vals > 0]
+    for e in (oracle.E4M3_EXP_MIN, oracle.E4M3_EXP_MAX):
+        scaled = nz * 2.0 ** e
+        assert np.all(scaled >= BF16_MIN_NORMAL) and np.all(scaled <= BF16_MAX), e
+    assert nz.min() * 2.0 ** (oracle.E4M3_EXP_MIN - 1) < BF16_MIN_NORMAL
+    assert nz.max() * 2.0 ** (oracle.E4M3_EXP_MAX + 1) > BF16_MAX
+
+
+def test_quantize_clamps_to_exponent_range():
+    """Rows whose exponent falls outside the stored range: a tiny row takes
+    the lowest exponent and rounds what lies below half the smallest code
+    to zero (a tie goes to the even code 0); a huge row takes the highest
+    and saturates at 448."""
+    tiny = [2.0 ** -120, 2.0 ** -126, 2.0 ** -128, -(2.0 ** -127)]
+    huge = [1.9 * 2.0 ** 127, -1.9 * 2.0 ** 127, 2.0 ** 119, 0.0]
+    codes, e = oracle.quantize_rows(np.array([tiny, huge]))
+    assert e.tolist() == [-117, 119]
+    # 2^-120 * 2^117 = 2^-3 (0x20); 2^-9 is the smallest subnormal (0x01);
+    # 2^-11 rounds to 0; -2^-10 is halfway between 0 and 2^-9: even code, signed
+    assert codes[0].tolist() == [0x20, 0x01, 0x00, 0x80]
+    assert codes[1].tolist() == [0x7E, 0xFE, 0x38, 0x00]
+
+
 def test_append_fp8_hand_worked():
     B, Hkv, T, D = 2, 1, 3, 4
     kc = np.zeros((B, Hkv, T, D), np.uint8)
@@ -134,6 +167,8 @@ FP8_MUTANTS = {
                          "y = np.clip(x * np.exp2(e.astype(np.float64))[..., None], -448, 448)"),
     "sign_dropped": ("return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)",
                      "return code.astype(np.uint8)"),
+    "int8_exponent_range": ("E4M3_EXP_MIN = -117", "E4M3_EXP_MIN = -127"),
+    "no_saturation": ("y = np.clip(y, -E4M3_MAX, E4M3_MAX)", "y = np.clip(y, -512.0, 512.0)"),
 }
 
 
@@ -151,12 +186,13 @@ def test_fp8_mutant_is_caught(name, monkeypatch):
     m = _mutant(*FP8_MUTANTS[name])
     pins = [test_decode_known_values, test_decode_table_shape, test_rounding_is_nearest_ties_to_even,
             test_quantize_hand_worked, test_quantize_exponent_is_minimal_and_error_bounded,
+            test_exponent_range_keeps_values_bf16_normal, test_quantize_clamps_to_exponent_range,
             test_append_fp8_hand_worked]
     failed = []
     for pin in pins:
         with monkeypatch.context() as mp:
             for fn in ("e4m3_value", "E4M3_TABLE", "_POS_VALUES", "_POS_CODES", "_round_to_e4m3",
-                       "quantize_rows", "dequantize", "append_fp8"):
+                       "quantize_rows", "dequantize", "append_fp8", "E4M3_EXP_MIN", "E4M3_EXP_MAX"):
                 mp.setattr(oracle, fn, getattr(m, fn))
             try:
                 pin()
