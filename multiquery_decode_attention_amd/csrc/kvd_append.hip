@@ -28,9 +28,11 @@ __global__ __launch_bounds__(256) void append_kernel(const uint4* __restrict__ k
     const int b = blockIdx.x;
     const int n = lengths[b];
     if (n < 0 || n > T_cap - T_q) {
-        // Uniform across the block: nobody writes, lengths stays as is.
+        // Uniform across the block: nobody writes, lengths stays as is.  A
+        // length outside [0, T_cap] is a bad length; one without room for
+        // the new rows, a full cache.
         if (threadIdx.x == 0) {
-            atomicOr(err, n < 0 ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
+            atomicOr(err, n < 0 || n > T_cap ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
             if (n_new) n_new[b] = 0;
         }
         return;
@@ -80,9 +82,10 @@ __global__ __launch_bounds__(64 * APPEND_FP8_WAVES) void append_fp8_kernel(const
     const int b = blockIdx.x;
     const int n = lengths[b];
     if (n < 0 || n > T_cap - T_q) {
-        // uniform across the block: nobody writes, lengths stays as is
+        // uniform across the block: nobody writes, lengths stays as is (a
+        // bad length, or a full cache, as in append_kernel)
         if (threadIdx.x == 0) {
-            atomicOr(err, n < 0 ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
+            atomicOr(err, n < 0 || n > T_cap ? ERRBIT_LENGTH : ERRBIT_CAPACITY);
             if (n_new) n_new[b] = 0;
         }
         return;

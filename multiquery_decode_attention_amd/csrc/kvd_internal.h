@@ -8,7 +8,7 @@
 namespace kvd {
 
 // Sticky device error bits, OR-ed into the handle's flag word.
-constexpr int ERRBIT_CAPACITY = 1;  // append found lengths[b] == T_cap
+constexpr int ERRBIT_CAPACITY = 1;  // an append found no room in a cache (its length in [0, T_cap])
 constexpr int ERRBIT_LENGTH = 2;    // a kernel saw lengths[b] outside [0, T_cap]
 constexpr int ERRBIT_PAGE = 4;      // a block-table entry in use was outside [0, num_pages)
 

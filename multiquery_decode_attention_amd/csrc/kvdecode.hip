@@ -23,6 +23,12 @@ struct kvdecode_s {
     int elem = 4;
     int variant_req = KVD_VARIANT_AUTO;
     int forced_splits = 0;
+    // Plans of steps with 1..KVD_MAX_NEW_TOKENS new tokens, made on first use
+    // (cleared when the variant or the forced split count changes).
+    struct CachedPlan {
+        bool valid;
+        int variant, tile, splits, chunk, lds_config;
+    } plans[KVD_MAX_NEW_TOKENS + 1] = {};
     bool unified = false;     // unified softmax maximum (LDS kernels)
     float unified_max = 0.f;  // in units of scale * q.k
 
@@ -130,23 +136,26 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
     return sh;
 }
 
-// Cost-model choice of the split count for one kernel shape.
-long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles, int T_q) {
+// Cost-model choice of the split count (at most s_max) for one kernel
+// shape.  Only the smallest S of each busiest-split size ceil(n_tiles / S)
+// is a candidate (a larger S with the same busiest split costs more rounds),
+// and those are enumerated directly: O(sqrt(n_tiles)) of them.
+long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles, int T_q,
+                      long long s_max) {
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * T_q * (h->d.head_dim + 1) * 4 * 2;
     double best = 0;
     std::vector<std::pair<long long, double>> cand;
-    long long prev_per = -1;
-    for (long long s = 1; s <= n_tiles; ++s) {
+    for (long long s = 1; s <= n_tiles && s <= s_max;) {
         const long long per = (n_tiles + s - 1) / s;  // tiles of the busiest split
-        if (per == prev_per) continue;
-        prev_per = per;
         const long long rounds = (sh.units * s + sh.slots - 1) / sh.slots;
         const double cost = (double)rounds * (per * tile * tok_bytes + fill) * sh.slots +
                             (double)sh.units * s * part_bytes;
         cand.emplace_back(s, cost);
         if (best == 0 || cost < best) best = cost;
+        if (per == 1) break;
+        s = (n_tiles + per - 2) / (per - 1);  // smallest S whose busiest split is smaller
     }
     long long pick = 1;
     for (auto& c : cand)
@@ -154,8 +163,60 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
     return pick;
 }
 
+// Grid of the partial-pass launch of a plan: workgroups per split and
+// threads per workgroup, as the variant's launcher sizes them.  A launch's
+// grid counts work-items in 32 bits per dimension, so blocks * threads must
+// stay below 2^32.
+struct GridShape {
+    long long blocks_per_split;
+    int threads;
+};
+GridShape partial_grid(const kvdecode_s* h, int variant, int T_q) {
+    const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
+    const long long padded = (bkv + 7) / 8 * 8;  // lds_grid_blocks: units padded to whole XCD rounds
+    const int rows = h->M * T_q;
+    const int D = h->d.head_dim;
+    GridShape g{0, 256};
+    if (variant == KVD_VARIANT_WAVE) {
+        const int rb = kvd::wave_fp8_row_blocks(D, rows);
+        g.blocks_per_split = padded * ((rows + 16 * rb - 1) / (16 * rb));
+    } else if (variant == KVD_VARIANT_XCHG) {
+        g.blocks_per_split = padded * kvd::xchg_shape(D, rows).groups;
+    } else if (variant == KVD_VARIANT_LDS) {
+        g.blocks_per_split = padded * ((rows + 63) / 64);
+    } else if (variant == KVD_VARIANT_MFMA) {
+        const int hb = kvd::mfma_head_blocks(h->M);
+        const int nw = hb < 4 ? hb : 4;
+        g.blocks_per_split = bkv * ((hb + nw - 1) / nw);
+        g.threads = 64 * nw;
+    } else {
+        g.blocks_per_split = (long long)h->d.batch * h->d.num_q_heads * T_q;
+        g.threads = 64;
+    }
+    return g;
+}
+constexpr long long GRID_ITEMS_MAX = 0xFFFFFFFFll;
+// Most splits whose partial-pass grid fits (0: not even one).
+long long max_splits_for_grid(const kvdecode_s* h, int variant, int T_q) {
+    const GridShape g = partial_grid(h, variant, T_q);
+    return GRID_ITEMS_MAX / ((long long)g.threads * g.blocks_per_split);
+}
+
 // T_q: query rows per head (new tokens per sequence in this step).
-Plan make_plan(const kvdecode_s* h, int T_q = 1) {
+Plan compute_plan(const kvdecode_s* h, int T_q);
+Plan make_plan(kvdecode_s* h, int T_q = 1) {
+    auto& c = h->plans[T_q];
+    if (!c.valid) {
+        const Plan p = compute_plan(h, T_q);
+        c = kvdecode_s::CachedPlan{true, p.variant, p.tile, p.splits, p.chunk, p.lds_config};
+    }
+    return Plan{c.variant, c.tile, c.splits, c.chunk, c.lds_config};
+}
+void clear_plans(kvdecode_s* h) {
+    for (auto& c : h->plans) c.valid = false;
+}
+
+Plan compute_plan(const kvdecode_s* h, int T_q) {
     Plan p;
     p.variant = resolve_variant(h, T_q);
     p.tile = p.variant == KVD_VARIANT_VALU   ? kvd::VALU_TILE
@@ -163,7 +224,13 @@ Plan make_plan(const kvdecode_s* h, int T_q = 1) {
                                              : kvd::MFMA_TILE;
     p.lds_config = kvd::LDS_SHORT;
     const long long n_tiles = (h->d.capacity + p.tile - 1) / p.tile;  // tiles of a full cache
-    auto clamp_splits = [&](long long s) { return s < 1 ? 1 : (s > n_tiles ? n_tiles : s); };
+    // at most one split per tile, and no more than the launch grid holds
+    const long long grid_cap = max_splits_for_grid(h, p.variant, T_q);
+    const long long s_max = n_tiles < grid_cap ? n_tiles : grid_cap;
+    auto clamp_splits = [&](long long s) {
+        s = s > s_max ? s_max : s;
+        return s < 1 ? 1 : s;  // (a grid that holds no split is refused before any launch)
+    };
     // tiles are dealt round-robin: a split holds at most ceil(n_tiles / S)
     auto finish = [&](long long s) {
         s = clamp_splits(s);
@@ -174,7 +241,7 @@ Plan make_plan(const kvdecode_s* h, int T_q = 1) {
         const long long s = clamp_splits(h->forced_splits > 0
                                              ? h->forced_splits
                                              : plan_splits(h, shape_for(h, p.variant, kvd::LDS_LONG, T_q),
-                                                           p.tile, n_tiles, T_q));
+                                                           p.tile, n_tiles, T_q, s_max));
         if ((n_tiles + s - 1) / s >= kvd::LDS_LONG_MIN_TILES) {
             p.lds_config = kvd::LDS_LONG;
             finish(s);
@@ -185,7 +252,7 @@ Plan make_plan(const kvdecode_s* h, int T_q = 1) {
         finish(h->forced_splits);
         return p;
     }
-    finish(plan_splits(h, shape_for(h, p.variant, kvd::LDS_SHORT, T_q), p.tile, n_tiles, T_q));
+    finish(plan_splits(h, shape_for(h, p.variant, kvd::LDS_SHORT, T_q), p.tile, n_tiles, T_q, s_max));
     return p;
 }
 
@@ -263,17 +330,36 @@ int32_t ensure_events(kvdecode_s* h) {
     return KVD_OK;
 }
 
-int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new, hipStream_t st,
-                            int T_q = 1) {
-    const bool timed = (h->timing_what & KVD_TIME_APPEND) && h->timing_cap > 0 && h->n_append < h->timing_cap;
+// Device memory a step uses besides the caller's tensors: the sticky error
+// word, per sequence the attended length (and the rows a several-token
+// append added), the dispatch order the combine leaves for the next step
+// (null: batch order, no sort), and the split partials.
+struct Workspace {
+    int* err;
+    int* len_att;   // [B]
+    int* n_new;     // [B]
+    int* order;     // [B] + flag, or null
+    void* o_part;
+    float* lse_part;
+};
+
+Workspace handle_workspace(const kvdecode_s* h) {
+    return Workspace{h->err, h->err + 1, h->err + 1 + h->d.batch, h->err + 1 + 2 * h->d.batch, h->o_part,
+                     h->lse_part};
+}
+
+int32_t launch_append_timed(kvdecode_s* h, const Workspace& ws, const void* k_new, const void* v_new,
+                            hipStream_t st, int T_q = 1, bool may_time = true) {
+    const bool timed = may_time && (h->timing_what & KVD_TIME_APPEND) && h->timing_cap > 0 &&
+                       h->n_append < h->timing_cap;
     if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
     hipError_t e =
         is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp, h->kv,
-                                           h->d.lengths, h->err, h->err + 1 + h->d.batch, h->d.batch,
-                                           h->d.num_kv_heads, h->d.head_dim, h->d.capacity, T_q, st)
-                  : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths,
-                                       h->err, h->err + 1 + h->d.batch, h->d.batch, h->d.num_kv_heads,
-                                       h->d.head_dim, h->d.capacity, T_q, h->elem, st);
+                                           h->d.lengths, ws.err, ws.n_new, h->d.batch, h->d.num_kv_heads,
+                                           h->d.head_dim, h->d.capacity, T_q, st)
+                  : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths, ws.err,
+                                       ws.n_new, h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
+                                       T_q, h->elem, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed) {
         if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
@@ -282,14 +368,8 @@ int32_t launch_append_timed(kvdecode_s* h, const void* k_new, const void* v_new,
     return KVD_OK;
 }
 
-// One attend, optionally preceded by an append.  The LDS kernel folds the
-// append into its partial pass (the combine then advances lengths); the
-// other kernels launch the append kernel first.  Argument checks happen
-// before any device work.
-// T_q > 1: a step with T_q new tokens per sequence (append then causal
-// attend of their T_q queries); q and out then hold Hq * T_q rows.
-int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void* q, void* out,
-                 float scale, hipStream_t st, int T_q = 1) {
+// Host checks of a step (before any device work) and its plan.
+int32_t check_step(kvdecode_s* h, const void* q, void* out, float scale, int T_q, Plan* plan) {
     if (!q || !out) return KVD_EINVAL;
     if (!aligned16(q) || !aligned16(out)) return KVD_EALIGN;
     if (!(scale > 0.f) || !isfinite(scale)) return KVD_EINVAL;
@@ -298,20 +378,35 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
                   : (p.variant != KVD_VARIANT_VALU && h->d.dtype != KVD_BF16))
         return KVD_EUNSUPPORTED;
     if (T_q > 1 && p.variant == KVD_VARIANT_MFMA) return KVD_EUNSUPPORTED;
-    int32_t rc = ensure_device(h);
-    if (rc != KVD_OK) return rc;
-    if ((rc = ensure_workspace(h, p.splits * T_q)) != KVD_OK) return rc;
-    if ((rc = ensure_events(h)) != KVD_OK) return rc;
+    // Launch sizes: the partial pass (at its planned splits) and the
+    // combine (one extra workgroup, and rows of B * Hq * T_q query rows, at
+    // least one row per 256-thread workgroup) must fit 32-bit grids; the
+    // kernels' int row arithmetic then fits too.
+    const GridShape g = partial_grid(h, p.variant, T_q);
+    const long long rows = (long long)h->d.batch * h->d.num_q_heads * T_q;
+    if ((long long)g.threads * g.blocks_per_split * p.splits > GRID_ITEMS_MAX || (rows + 1) * 256 > GRID_ITEMS_MAX)
+        return KVD_EINVAL;
+    *plan = p;
+    return KVD_OK;
+}
+
+// One step's launches on a given workspace: optionally the append kernel,
+// the partial pass, the combine.  The LDS and VALU kernels fold a one-token
+// append into the partial pass (the combine then advances lengths), as do
+// the fp8 wave and exchange kernels; the other kernels, and several new
+// tokens, launch the append kernel first.  T_q > 1: a step with T_q new
+// tokens per sequence (append then causal attend of their T_q queries); q
+// and out then hold Hq * T_q rows.  may_time: record the timing events
+// kvdecode_timing_enable asked for.
+int32_t launch_step(kvdecode_s* h, const Plan& p, const Workspace& ws, const void* k_new, const void* v_new,
+                    const void* q, void* out, float scale, hipStream_t st, int T_q, bool may_time) {
     const bool with_append = k_new != nullptr;
-    // One new token is appended inside the partial pass (bf16 and fp32:
-    // every kernel but MFMA; fp8: the wave and exchange kernels, which
-    // quantize it there); otherwise, and for several new tokens, the append
-    // kernel runs first.
     const bool fused = with_append && T_q == 1 &&
                        (is_fp8(h) ? p.variant == KVD_VARIANT_WAVE || p.variant == KVD_VARIANT_XCHG
                                   : p.variant != KVD_VARIANT_MFMA);
+    int32_t rc;
     if (with_append && !fused) {
-        if ((rc = launch_append_timed(h, k_new, v_new, st, T_q)) != KVD_OK) return rc;
+        if ((rc = launch_append_timed(h, ws, k_new, v_new, st, T_q, may_time)) != KVD_OK) return rc;
     }
 
     kvd::PartialArgs a;
@@ -319,10 +414,10 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.k_cache = h->d.k_cache;
     a.v_cache = h->d.v_cache;
     a.lengths = h->d.lengths;
-    a.o_part = h->o_part;
-    a.lse_part = h->lse_part;
-    a.err = h->err;
-    a.len_att = h->err + 1;
+    a.o_part = ws.o_part;
+    a.lse_part = ws.lse_part;
+    a.err = ws.err;
+    a.len_att = ws.len_att;
     a.k_new = fused ? k_new : nullptr;
     a.v_new = fused ? v_new : nullptr;
     a.B = h->d.batch;
@@ -330,8 +425,8 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.Hkv = h->d.num_kv_heads;
     a.M = h->M * T_q;
     a.T_q = T_q;
-    a.n_new = T_q > 1 ? h->err + 1 + h->d.batch : nullptr;
-    a.order = h->err + 1 + 2 * h->d.batch;
+    a.n_new = T_q > 1 ? ws.n_new : nullptr;
+    a.order = ws.order;
     a.D = h->d.head_dim;
     a.T_cap = h->d.capacity;
     a.S = p.splits;
@@ -344,10 +439,10 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     a.tau = h->unified ? 64.f : 8.f;
 
     kvd::CombineArgs c;
-    c.o_part = h->o_part;
-    c.lse_part = h->lse_part;
-    c.len_att = h->err + 1;
-    c.order = h->err + 1 + 2 * h->d.batch;
+    c.o_part = ws.o_part;
+    c.lse_part = ws.lse_part;
+    c.len_att = ws.len_att;
+    c.order = ws.order;
     c.lengths = h->d.lengths;
     c.fused_append = fused ? 1 : 0;
     c.out = out;
@@ -362,7 +457,7 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     // ev[0] before the partial pass, ev[1] between the two launches, ev[2]
     // after the combine.
     const int what = h->timing_what;
-    const bool timed = (what & (KVD_TIME_PARTIAL | KVD_TIME_COMBINE)) && h->timing_cap > 0 &&
+    const bool timed = may_time && (what & (KVD_TIME_PARTIAL | KVD_TIME_COMBINE)) && h->timing_cap > 0 &&
                        h->n_attend < h->timing_cap;
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
@@ -381,6 +476,20 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
         ++h->n_attend;
     }
     return KVD_OK;
+}
+
+// One attend, optionally preceded by an append, on the handle's workspace
+// (allocated here on first use).  Argument checks happen before any device
+// work.
+int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void* q, void* out,
+                 float scale, hipStream_t st, int T_q = 1) {
+    Plan p;
+    int32_t rc = check_step(h, q, out, scale, T_q, &p);
+    if (rc != KVD_OK) return rc;
+    if ((rc = ensure_device(h)) != KVD_OK) return rc;
+    if ((rc = ensure_workspace(h, p.splits * T_q)) != KVD_OK) return rc;
+    if ((rc = ensure_events(h)) != KVD_OK) return rc;
+    return launch_step(h, p, handle_workspace(h), k_new, v_new, q, out, scale, st, T_q, true);
 }
 
 }  // namespace
@@ -516,7 +625,7 @@ int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void
     int32_t rc = ensure_device(h);
     if (rc != KVD_OK) return rc;
     if ((rc = ensure_events(h)) != KVD_OK) return rc;
-    return launch_append_timed(h, k_new, v_new, static_cast<hipStream_t>(stream));
+    return launch_append_timed(h, handle_workspace(h), k_new, v_new, static_cast<hipStream_t>(stream));
 }
 
 int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream) {
@@ -589,6 +698,7 @@ int32_t kvdecode_set_unified_max(kvdecode_t h, int32_t enable, float phi) {
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n) {
     if (!is_live(h) || n < 0) return KVD_EINVAL;
     h->forced_splits = n;
+    clear_plans(h);
     return KVD_OK;
 }
 
@@ -600,6 +710,7 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
                         ((variant == KVD_VARIANT_WAVE || variant == KVD_VARIANT_XCHG) && h->d.head_dim >= 128);
         if (!ok) return KVD_EUNSUPPORTED;
         h->variant_req = variant;
+        clear_plans(h);
         return KVD_OK;
     }
     if (variant == KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
@@ -608,6 +719,7 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;
     h->variant_req = variant;
+    clear_plans(h);
     return KVD_OK;
 }
 

@@ -129,6 +129,33 @@ def test_handle_calls_validate_before_any_device_work(lib):
     assert lib.kvdecode_destroy(None) == kvd.KVD_EINVAL
 
 
+def test_launch_arithmetic_is_validated(lib):
+    """Shapes whose launches would not fit 32-bit grids (each grid
+    dimension counts work-items in 32 bits; the kernels' row arithmetic is
+    int) are refused by the step with KVD_EINVAL before any HIP call: the
+    combine takes B * Hq * T_q query rows on 256-thread workgroups; the
+    planner caps the split count so that the partial pass's grid fits."""
+    # 65535 * 512 query rows: 2^25 of them, past 2^32 work-items
+    rc, h = create(lib, make_desc(batch=65535, num_q_heads=512, num_kv_heads=1, capacity=64))
+    assert rc == kvd.KVD_OK
+    assert lib.kvdecode_attend(h, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert lib.kvdecode_append_attend(h, FAKE, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    lib.kvdecode_destroy(h)
+    # 65535 * 256 rows fit with one new token, not with two
+    rc, h = create(lib, make_desc(batch=65535, num_q_heads=256, num_kv_heads=1, capacity=64))
+    assert rc == kvd.KVD_OK
+    assert lib.kvdecode_append_attend_multi(h, 2, FAKE, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    lib.kvdecode_destroy(h)
+    # MHA over 65535 x 64 (sequence, head) units: a forced split count is
+    # capped at the 4 splits whose grid of 256-thread workgroups fits
+    rc, h = create(lib, make_desc(batch=65535, num_q_heads=64, num_kv_heads=64, capacity=65536))
+    assert rc == kvd.KVD_OK
+    kvd.kvdecode_set_num_splits(h, 10**6)
+    units = -(-65535 * 64 // 8) * 8
+    assert kvd.kvdecode_get_plan(h)["num_splits"] == (2**32 - 1) // (256 * units) == 4
+    lib.kvdecode_destroy(h)
+
+
 def test_mfma_variant_needs_bf16(lib):
     rc, h = create(lib, make_desc(dtype=kvd.KVD_F32))
     assert rc == kvd.KVD_OK

@@ -166,6 +166,23 @@ def test_fused_step_with_out_of_range_length(variant):
     assert rel_err_rows(to_f64(out), ref) <= TOL_BF16
 
 
+@pytest.mark.parametrize("dtype,variant", [("bf16", "lds"), ("bf16", "mfma"), ("f32", "valu")])
+def test_separate_append_with_out_of_range_length(dtype, variant):
+    """The separate append (kvdecode_append, and the append kernel the MFMA
+    step runs first) on a length past capacity reports it as a bad length,
+    KVD_ELENGTH, as the fused step does -- not as a full cache -- and leaves
+    that sequence unchanged; the other sequence is appended."""
+    B, Hq, Hkv, D, T_cap = 2, 16, 1, 128, 96
+    case = inputs.make_case(B, Hq, Hkv, D, T_cap, [96, 41], dtype, seed=13)
+    L_bad = torch.tensor([1000, 40], dtype=torch.int32)
+    out, kc, vc, L, status, _ = gpu_step(case, Hq, lengths=L_bad, fused=False, variant=VARIANTS[variant])
+    assert status == kvd.KVD_ELENGTH
+    assert L.cpu().tolist() == [1000, 41]
+    ref, k2, v2, _ = oracle_step(case, lengths=torch.tensor([96, 40], dtype=torch.int32))
+    assert np.array_equal(inputs.host_array(kc), k2) and np.array_equal(inputs.host_array(vc), v2)
+    assert rel_err_rows(to_f64(out), ref) <= tol_for(case)
+
+
 def test_length_out_of_range_is_clamped_and_reported():
     B, Hq, Hkv, D, T_cap = 2, 16, 1, 128, 96
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, [96, 40], "bf16", seed=10)
