@@ -74,7 +74,8 @@ typedef enum {
     KVD_EHIP = -5,         /* a HIP runtime call or kernel launch failed */
     KVD_ENOMEM = -6,       /* host or device allocation failed */
     KVD_ELENGTH = -7,      /* (from kvdecode_status) an append or attend found lengths[b] outside [0, capacity] */
-    KVD_EPAGE = -8         /* (from kvdecode_status) a block-table entry in use was outside [0, num_pages) */
+    KVD_EPAGE = -8,        /* (from kvdecode_status) a block-table entry in use was outside [0, num_pages) */
+    KVD_ESCRATCH = -9      /* kvdecode_append_attend_noalloc: the step needs more workspace than its static buffer */
 } kvd_status_t;
 
 /* Kernel variants for the partial pass (kvdecode_set_variant).
@@ -311,10 +312,39 @@ int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void*
                                      void* stream);
 
 /*
+ * kvdecode_append_attend without any allocation, for callers that cannot
+ * allocate device memory while they run: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results, cache update and sticky errors as kvdecode_append_attend, and it
+ * calls no hipMalloc, hipFree or other allocating routine: the step's
+ * workspace (split partials, their log-sum-exps, attended lengths, the
+ * error word) is a static device array of KVD_NOALLOC_SCRATCH_MIB MiB that
+ * every GPU the library runs on holds until the process ends.  A step that
+ * needs more (about B * Hq * splits * head_dim * 2 bytes of partials,
+ * 4 bytes per element for fp32) returns KVD_ESCRATCH and launches nothing.
+ * The handle's own workspace is not used, so a handle created by
+ * kvdecode_create can take these steps without ever allocating.
+ * Every call on one GPU shares that GPU's array: calls that overlap on a GPU
+ * (on unordered streams, from any handle) race and must be serialised by
+ * the caller.  The array keeps the last call's contents; the sticky error
+ * word in it collects the errors of every such step on that GPU until a
+ * kvdecode_status call on a handle that ran one reads and clears it.  Steps
+ * dispatch the batch in its own order (the handle's length-sorted dispatch
+ * order needs workspace kept between steps).  Timing events are not
+ * recorded.  Argument checks and return codes otherwise as for
+ * kvdecode_append_attend.
+ */
+enum { KVD_NOALLOC_SCRATCH_MIB = 32 };
+int32_t kvdecode_append_attend_noalloc(kvdecode_t h, const void* k_new, const void* v_new, const void* q,
+                                       void* out, float scale, void* stream);
+
+/*
  * Synchronise `stream`, then report and clear the sticky device error:
  * KVD_OK, KVD_ECAPACITY, KVD_ELENGTH or KVD_EPAGE (in that order of
- * precedence when several occurred).  Returns KVD_OK without a device call if the handle has never
- * touched a device.
+ * precedence when several occurred).  For a handle that ran allocation-free
+ * steps it also reads and clears the error word of the current device's
+ * static buffer (shared by every such step on that GPU).  Returns KVD_OK
+ * without a device call if the handle has never touched a device.
  */
 int32_t kvdecode_status(kvdecode_t h, void* stream);
 

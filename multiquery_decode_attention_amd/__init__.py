@@ -21,11 +21,11 @@ import torch
 
 __all__ = [
     "KVD_OK", "KVD_EINVAL", "KVD_EUNSUPPORTED", "KVD_EALIGN", "KVD_ECAPACITY", "KVD_EHIP",
-    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
+    "KVD_ENOMEM", "KVD_ELENGTH", "KVD_EPAGE", "KVD_ESCRATCH", "KVD_NOALLOC_SCRATCH_MIB", "KVD_F32", "KVD_FP8_E4M3", "KVD_BF16", "KVD_VARIANT_AUTO", "KVD_VARIANT_VALU",
     "KVD_VARIANT_MFMA", "KVD_VARIANT_LDS", "KVD_VARIANT_WAVE", "KVD_VARIANT_XCHG", "KvdError", "KvdLibraryMissing", "kvdecode_desc_t", "kvdecode_paged_desc_t", "kvdecode_fp8_desc_t", "kvdecode_create", "kvdecode_create_paged",
     "kvdecode_create_fp8", "kvdecode_create_fp8_paged", "kvdecode_fp8_paged_desc_t",
     "kvdecode_append", "kvdecode_attend", "kvdecode_append_attend", "kvdecode_append_attend_multi",
-    "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
+    "kvdecode_append_attend_noalloc", "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
     "KVD_TIME_APPEND", "KVD_TIME_ALL",
     "kvdecode_reserve", "kvdecode_set_num_splits",
     "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan", "kvdecode_timing_enable",
@@ -34,7 +34,8 @@ __all__ = [
 ]
 
 KVD_OK, KVD_EINVAL, KVD_EUNSUPPORTED, KVD_EALIGN = 0, -1, -2, -3
-KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE = -4, -5, -6, -7, -8
+KVD_ECAPACITY, KVD_EHIP, KVD_ENOMEM, KVD_ELENGTH, KVD_EPAGE, KVD_ESCRATCH = -4, -5, -6, -7, -8, -9
+KVD_NOALLOC_SCRATCH_MIB = 32
 KVD_F32, KVD_BF16, KVD_FP8_E4M3 = 0, 1, 2
 KVD_VARIANT_AUTO, KVD_VARIANT_VALU, KVD_VARIANT_MFMA, KVD_VARIANT_LDS, KVD_VARIANT_WAVE, KVD_VARIANT_XCHG = 0, 1, 2, 3, 4, 5
 KVD_TIME_PARTIAL, KVD_TIME_COMBINE, KVD_TIME_APPEND, KVD_TIME_ALL = 1, 2, 4, 7
@@ -47,7 +48,8 @@ LIB_PATH = os.environ.get("KVD_LIBRARY") or os.path.join(os.path.dirname(os.path
 EXPORTS = (
     "kvdecode_create", "kvdecode_create_paged", "kvdecode_create_fp8", "kvdecode_create_fp8_paged",
     "kvdecode_append", "kvdecode_attend",
-    "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_status", "kvdecode_reserve",
+    "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_append_attend_noalloc",
+    "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan",
     "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
 )
@@ -114,6 +116,7 @@ def library():
         "kvdecode_attend": (I, [P, P, P, F, P]),
         "kvdecode_append_attend": (I, [P, P, P, P, P, F, P]),
         "kvdecode_append_attend_multi": (I, [P, I, P, P, P, P, F, P]),
+        "kvdecode_append_attend_noalloc": (I, [P, P, P, P, P, F, P]),
         "kvdecode_status": (I, [P, P]),
         "kvdecode_reserve": (I, [P, I]),
         "kvdecode_set_num_splits": (I, [P, I]),
@@ -278,6 +281,15 @@ def kvdecode_append_attend(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: 
     _check(library().kvdecode_append_attend(h, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
                                             float(scale), _stream_ptr(stream)),
            "kvdecode_append_attend")
+
+
+def kvdecode_append_attend_noalloc(h: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                                   out: torch.Tensor, scale: float, stream=None) -> None:
+    """kvdecode_append_attend with its workspace in the library's static
+    per-GPU buffer: no device allocation (calls on one GPU must not overlap)."""
+    _check(library().kvdecode_append_attend_noalloc(h, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out),
+                                                    float(scale), _stream_ptr(stream)),
+           "kvdecode_append_attend_noalloc")
 
 
 KVD_MAX_NEW_TOKENS = 16

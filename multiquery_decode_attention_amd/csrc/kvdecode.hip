@@ -35,6 +35,7 @@ struct kvdecode_s {
     // Device resources (allocated on first use, on the then-current device).
     int device = -1;
     int* err = nullptr;
+    int noalloc_device = -1;   // device of this handle's allocation-free steps (scratch error word)
     void* o_part = nullptr;    // partials: bf16 for bf16 outputs, else fp32
     float* lse_part = nullptr;
     int ws_splits = 0;
@@ -139,27 +140,34 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
 // Cost-model choice of the split count (at most s_max) for one kernel
 // shape.  Only the smallest S of each busiest-split size ceil(n_tiles / S)
 // is a candidate (a larger S with the same busiest split costs more rounds),
-// and those are enumerated directly: O(sqrt(n_tiles)) of them.
+// and those are enumerated directly: O(sqrt(n_tiles)) of them, twice (the
+// cheapest cost, then the most splits within 2% of it), with no heap memory.
 long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles, int T_q,
                       long long s_max) {
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * T_q * (h->d.head_dim + 1) * 4 * 2;
-    double best = 0;
-    std::vector<std::pair<long long, double>> cand;
-    for (long long s = 1; s <= n_tiles && s <= s_max;) {
-        const long long per = (n_tiles + s - 1) / s;  // tiles of the busiest split
+    auto cost_of = [&](long long s, long long per) {
         const long long rounds = (sh.units * s + sh.slots - 1) / sh.slots;
-        const double cost = (double)rounds * (per * tile * tok_bytes + fill) * sh.slots +
-                            (double)sh.units * s * part_bytes;
-        cand.emplace_back(s, cost);
+        return (double)rounds * (per * tile * tok_bytes + fill) * sh.slots + (double)sh.units * s * part_bytes;
+    };
+    // visit(s, cost) for every candidate, in increasing s
+    auto each_candidate = [&](auto&& visit) {
+        for (long long s = 1; s <= n_tiles && s <= s_max;) {
+            const long long per = (n_tiles + s - 1) / s;  // tiles of the busiest split
+            visit(s, cost_of(s, per));
+            if (per == 1) break;
+            s = (n_tiles + per - 2) / (per - 1);  // smallest S whose busiest split is smaller
+        }
+    };
+    double best = 0;
+    each_candidate([&](long long, double cost) {
         if (best == 0 || cost < best) best = cost;
-        if (per == 1) break;
-        s = (n_tiles + per - 2) / (per - 1);  // smallest S whose busiest split is smaller
-    }
+    });
     long long pick = 1;
-    for (auto& c : cand)
-        if (c.second <= best * 1.02 && c.first > pick) pick = c.first;
+    each_candidate([&](long long s, double cost) {
+        if (cost <= best * 1.02 && s > pick) pick = s;
+    });
     return pick;
 }
 
@@ -492,6 +500,66 @@ int32_t run_step(kvdecode_s* h, const void* k_new, const void* v_new, const void
     return launch_step(h, p, handle_workspace(h), k_new, v_new, q, out, scale, st, T_q, true);
 }
 
+// --- allocation-free steps --------------------------------------------------
+//
+// kvdecode_append_attend_noalloc takes its workspace from this static device
+// array instead of the handle's: one copy per GPU, loaded with the code
+// object and held until the process ends, shared by every such call on that
+// GPU.  Host code reaches it through the address hipGetSymbolAddress gives
+// for the current device (the array's name is only a host-side stand-in),
+// looked up once per device and kept in scratch_ptr.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)KVD_NOALLOC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array.
+int32_t scratch_of(int dev, char** out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return KVD_EINVAL;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return KVD_EHIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = static_cast<char*>(g_scratch_ptr[dev]);
+    return KVD_OK;
+}
+
+// Layout of one step's workspace in the scratch array: the error word, then
+// [B] attended lengths and [B] appended-row counts, then the partials and
+// their log-sum-exps, each 256-byte aligned.  No dispatch order is kept
+// between calls (the array is shared): steps dispatch in batch order.
+struct ScratchLayout {
+    size_t len_att, n_new, o_part, lse, total;
+};
+ScratchLayout scratch_layout(const kvdecode_s* h, const Plan& p) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t B = (size_t)h->d.batch;
+    const size_t rows = B * h->d.num_q_heads * (size_t)p.splits;
+    const size_t part_elem = h->d.dtype == KVD_F32 ? sizeof(float) : sizeof(uint16_t);
+    ScratchLayout l;
+    l.len_att = 256;
+    l.n_new = l.len_att + up(B * sizeof(int));
+    l.o_part = l.n_new + up(B * sizeof(int));
+    l.lse = l.o_part + up(rows * h->d.head_dim * part_elem);
+    l.total = l.lse + up(rows * sizeof(float));
+    return l;
+}
+
+// Read the sticky error word at `word` on stream st and clear it if set.
+int32_t take_error_word(int* word, hipStream_t st, int* flag) {
+    if (hipMemcpyAsync(flag, word, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess) return KVD_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
+    if (*flag) {
+        if (hipMemsetAsync(word, 0, sizeof(int), st) != hipSuccess) return KVD_EHIP;
+        if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
+    }
+    return KVD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -507,6 +575,7 @@ const char* kvdecode_strerror(int32_t code) {
         case KVD_ENOMEM: return "out of memory";
         case KVD_ELENGTH: return "sequence length outside [0, capacity]";
         case KVD_EPAGE: return "block-table entry outside the page pool";
+        case KVD_ESCRATCH: return "step needs more workspace than the allocation-free entry point's static buffer";
         default: return "unknown status code";
     }
 }
@@ -651,19 +720,43 @@ int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void*
     return run_step(h, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream), n_tokens);
 }
 
+int32_t kvdecode_append_attend_noalloc(kvdecode_t h, const void* k_new, const void* v_new, const void* q,
+                                       void* out, float scale, void* stream) {
+    if (!is_live(h)) return KVD_EINVAL;
+    if (!k_new || !v_new) return KVD_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_EALIGN;
+    Plan p;
+    int32_t rc = check_step(h, q, out, scale, 1, &p);
+    if (rc != KVD_OK) return rc;
+    const ScratchLayout l = scratch_layout(h, p);
+    if (l.total > NOALLOC_SCRATCH_BYTES) return KVD_ESCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KVD_EHIP;
+    char* base = nullptr;
+    if ((rc = scratch_of(dev, &base)) != KVD_OK) return rc;
+    const Workspace ws{reinterpret_cast<int*>(base), reinterpret_cast<int*>(base + l.len_att),
+                       reinterpret_cast<int*>(base + l.n_new), nullptr, base + l.o_part,
+                       reinterpret_cast<float*>(base + l.lse)};
+    h->noalloc_device = dev;
+    return launch_step(h, p, ws, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream), 1, false);
+}
+
 int32_t kvdecode_status(kvdecode_t h, void* stream) {
     if (!is_live(h)) return KVD_EINVAL;
-    if (h->device < 0) return KVD_OK;
+    if (h->device < 0 && h->noalloc_device < 0) return KVD_OK;
     int cur = -1;
-    if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return KVD_EINVAL;
+    if (hipGetDevice(&cur) != hipSuccess) return KVD_EINVAL;
+    if ((h->device >= 0 && cur != h->device) || (h->noalloc_device >= 0 && cur != h->noalloc_device))
+        return KVD_EINVAL;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int flag = 0;
-    if (hipMemcpyAsync(&flag, h->err, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess)
-        return KVD_EHIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
-    if (flag) {
-        if (hipMemsetAsync(h->err, 0, sizeof(int), st) != hipSuccess) return KVD_EHIP;
-        if (hipStreamSynchronize(st) != hipSuccess) return KVD_EHIP;
+    int flag = 0, rc;
+    if (h->device >= 0 && (rc = take_error_word(h->err, st, &flag)) != KVD_OK) return rc;
+    if (h->noalloc_device >= 0) {
+        char* base = nullptr;
+        int scratch_flag = 0;
+        if ((rc = scratch_of(cur, &base)) != KVD_OK) return rc;
+        if ((rc = take_error_word(reinterpret_cast<int*>(base), st, &scratch_flag)) != KVD_OK) return rc;
+        flag |= scratch_flag;
     }
     if (flag & kvd::ERRBIT_CAPACITY) return KVD_ECAPACITY;
     if (flag & kvd::ERRBIT_LENGTH) return KVD_ELENGTH;

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert kvd.kvdecode_strerror(code) != "unknown status code"
     assert kvd.kvdecode_strerror(-99) == "unknown status code"
 
@@ -153,6 +153,29 @@ def test_launch_arithmetic_is_validated(lib):
     kvd.kvdecode_set_num_splits(h, 10**6)
     units = -(-65535 * 64 // 8) * 8
     assert kvd.kvdecode_get_plan(h)["num_splits"] == (2**32 - 1) // (256 * units) == 4
+    lib.kvdecode_destroy(h)
+
+
+def test_noalloc_step_refuses_what_its_buffer_cannot_hold(lib):
+    """The allocation-free step checks its arguments like the allocating
+    one, and refuses (KVD_ESCRATCH) a step whose workspace exceeds the
+    static buffer, all before any HIP call."""
+    rc, h = create(lib, make_desc())
+    assert rc == kvd.KVD_OK
+    f = lib.kvdecode_append_attend_noalloc
+    assert f(h, None, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert f(h, FAKE, FAKE + 8, FAKE, FAKE, 1.0, None) == kvd.KVD_EALIGN
+    assert f(h, FAKE, FAKE, None, FAKE, 1.0, None) == kvd.KVD_EINVAL
+    assert f(h, FAKE, FAKE, FAKE, FAKE + 4, 1.0, None) == kvd.KVD_EALIGN
+    assert f(h, FAKE, FAKE, FAKE, FAKE, float("nan"), None) == kvd.KVD_EINVAL
+    lib.kvdecode_destroy(h)
+    assert f(h, FAKE, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_EINVAL  # destroyed handle
+    # 4096 x 48 heads x 256 columns of bf16 partials at one split already
+    # take 96 MiB, past the 32 MiB buffer
+    rc, h = create(lib, make_desc(batch=4096, num_q_heads=48, num_kv_heads=1, head_dim=256, capacity=2048))
+    assert rc == kvd.KVD_OK
+    kvd.kvdecode_set_num_splits(h, 1)
+    assert f(h, FAKE, FAKE, FAKE, FAKE, 1.0, None) == kvd.KVD_ESCRATCH
     lib.kvdecode_destroy(h)
 
 
