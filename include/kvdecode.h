@@ -269,7 +269,11 @@ int32_t kvdecode_append(kvdecode_t h, const void* k_new, const void* v_new, void
  * time (no host synchronisation); a length outside [0, T_cap] is clamped
  * into range for memory safety and sets the sticky error KVD_ELENGTH.
  * Internally: a split-KV partial pass over (sequence, KV head, split) work
- * units, then a log-sum-exp combine of the splits.
+ * units, then a log-sum-exp combine of the splits.  A plan with one split
+ * on the LDS or VALU kernel has nothing to merge: its partial pass writes
+ * out directly and no combine is launched (the combine exists only to
+ * merge the shards, "All About Transformer Inference", section "Sharding
+ * the KV cache").
  */
 int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, void* stream);
 
@@ -281,8 +285,9 @@ int32_t kvdecode_attend(kvdecode_t h, const void* q, void* out, float scale, voi
  * token's row is read from k_new/v_new directly and written to its cache
  * slot alongside), and with the fp8 WAVE and XCHG kernels the workgroups
  * owning the new token's tile quantize it into its slot before reading
- * that tile; the combine advances lengths.  The MFMA kernel and the fp8
- * LDS kernel run the append kernel first.
+ * that tile; the combine advances lengths (after a one-split pass of the
+ * LDS or VALU kernel, the last of a sequence's workgroups to finish does).
+ * The MFMA kernel and the fp8 LDS kernel run the append kernel first.
  * Same page, section "Implementation: JetStream": generate emits one token
  * per batch item and appends its single-token KV cache.
  */
@@ -318,7 +323,9 @@ int32_t kvdecode_append_attend_multi(kvdecode_t h, int32_t n_tokens, const void*
  * results, cache update and sticky errors as kvdecode_append_attend, and it
  * calls no hipMalloc, hipFree or other allocating routine: the step's
  * workspace (split partials, their log-sum-exps, attended lengths, the
- * error word) is a static device array of KVD_NOALLOC_SCRATCH_MIB MiB that
+ * per-sequence counters of one-split passes -- zero when the array is
+ * loaded and again after every step -- and the error word) is a static
+ * device array of KVD_NOALLOC_SCRATCH_MIB MiB that
  * every GPU the library runs on holds until the process ends.  A step that
  * needs more (about B * Hq * splits * head_dim * 2 bytes of partials,
  * 4 bytes per element for fp32) returns KVD_ESCRATCH and launches nothing.
@@ -397,7 +404,8 @@ int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
 /*
  * Kernel timing with HIP events recorded on the call's stream.  `what` picks
  * the brackets: KVD_TIME_PARTIAL around the partial-pass launch of each
- * attend, KVD_TIME_COMBINE around its combine launch, KVD_TIME_APPEND around
+ * attend, KVD_TIME_COMBINE around its combine launch (an empty bracket
+ * after a one-split pass, which launches none), KVD_TIME_APPEND around
  * a separate append kernel.  Every recorded event costs the stream about
  * 2 us, so ask only for what is read.
  * kvdecode_timing_enable(h, n, what) allocates n event slots (n = 0 or

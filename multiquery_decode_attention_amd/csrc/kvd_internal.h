@@ -98,7 +98,27 @@ struct PartialArgs {
     // see CombineArgs::order).  A hint only: any permutation gives the same
     // results.
     const int* order;
+    // Single-split plans (LDS and VALU kernels; null: a combine follows):
+    // the pass writes the output rows [B, Hq, D] itself, in the output's
+    // precision, and no combine runs.  After a fused append the last
+    // workgroup of a sequence to finish advances lengths_adv[b], counted on
+    // seq_ctr[b] (zero between launches: the last arriver resets it).
+    void* out;
+    int32_t* lengths_adv;
+    int* seq_ctr;
 };
+
+// Single-split plans: each of a sequence's per_seq workgroups calls this
+// once (one lane), after its own read of lengths[b] has been used; the last
+// to arrive sets lengths[b] = new_len.  Every read of the length in the
+// launch precedes that arrival's counter update, so none sees the new
+// value.
+__device__ __forceinline__ void advance_when_last(int* ctr, int per_seq, int32_t* lengths, int b, int new_len) {
+    if (per_seq == 1 || atomicAdd(ctr, 1) == per_seq - 1) {
+        if (per_seq > 1) atomicExch(ctr, 0);
+        lengths[b] = new_len;
+    }
+}
 
 struct CombineArgs {
     int groups;             // split groups per row (set by the launcher)

@@ -94,7 +94,18 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
                                          s == 0 && g == 0 && hg == 0 && threadIdx.x == 0);
     const int len = sl.len;
     const int n_seq_tiles = (len + MFMA_TILE - 1) / MFMA_TILE;
-    if (s >= n_seq_tiles) return;  // whole workgroup, before any barrier
+    if (s >= n_seq_tiles) {
+        // whole workgroup, before any barrier; a single-split pass writes
+        // the zero rows of a sequence with no tokens
+        if (a.out != nullptr && n_seq_tiles == 0) {
+            const size_t r0 = (size_t)b * a.Hq + (size_t)g * a.M + (size_t)hg * 64;
+            const int rows = min(a.M - hg * 64, 64);
+            for (int p = threadIdx.x; p < rows * (D / 8); p += 256)
+                *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + (r0 + p / (D / 8)) * D + (p % (D / 8)) * 8) =
+                    u32x4_t{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
     const int t_end = len;
     // this split owns the sequence's tiles s, s+S, s+2S, ...
     const int n_tiles = (n_seq_tiles - s + a.S - 1) / a.S;
@@ -410,22 +421,28 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
     float l = l_run;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    const size_t row0 = ((size_t)b * a.Hq + (size_t)g * a.M + hw0) * a.S + s;
+    const size_t qrow0 = (size_t)b * a.Hq + (size_t)g * a.M + hw0;  // query row of the wave's first head
+    const size_t row0 = qrow0 * a.S + s;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * gq + i;
         const float li = __shfl(l, r);
         if (r < nh) {
             const float inv = li > 0.f ? 1.f / li : 0.f;  // a row with no token in this split: 0
-            // Non-temporal stores: the partials are read once, by the
-            // combine; kept out of the caches' dirty lines they stream to
-            // memory instead of draining at the end of the launch.
-            store_partial_row<D>(static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D, acc, i, c, inv);
+            // (a single-split pass stores the output rows the same way)
+            uint16_t* dst = a.out != nullptr ? static_cast<uint16_t*>(a.out) + (qrow0 + r) * D
+                                             : static_cast<uint16_t*>(a.o_part) + (row0 + (size_t)r * a.S) * D;
+            store_partial_row<D>(dst, acc, i, c, inv);
         }
     }
-    if (gq == 0 && head_ok)
-        __builtin_nontemporal_store(l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY,
-                                    a.lse_part + row0 + (size_t)c * a.S);
+    if (a.out == nullptr) {
+        if (gq == 0 && head_ok)
+            a.lse_part[row0 + (size_t)c * a.S] = l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY;
+    } else if (sl.appended && a.lengths_adv != nullptr && threadIdx.x == 0) {
+        // Wave 0 always holds heads, so it gets here; every wave of this
+        // workgroup read the length before the ring's first barrier.
+        advance_when_last(a.seq_ctr + b, a.Hkv * head_groups, a.lengths_adv, b, sl.slot + 1);
+    }
 }
 
 template <int D, int NS, int VL>

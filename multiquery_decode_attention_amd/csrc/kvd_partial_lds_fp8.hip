@@ -318,8 +318,7 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
         }
     }
     if (gq == 0 && head_ok)
-        __builtin_nontemporal_store(l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY,
-                                    a.lse_part + row0 + (size_t)c * a.S);
+        a.lse_part[row0 + (size_t)c * a.S] = l > 0.f ? m_ref + __builtin_log2f(l) : -INFINITY;
 }
 
 template <int D>

@@ -69,7 +69,15 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
                                       s == 0 && h == 0 && lane == 0);
     const int len = sl.len;
     const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
-    if (s >= n_seq_tiles) return;  // no tile of this sequence for this split
+    if (s >= n_seq_tiles) {
+        // no tile of this sequence for this split; a single-split pass
+        // writes the zero row of a sequence with no tokens
+        if (a.out != nullptr && n_seq_tiles == 0) {
+            T* orow = static_cast<T*>(a.out) + ((size_t)b * a.Hq + h) * D;
+            for (int d = lane; d < D; d += 64) orow[d] = from_f32<T>(0.f);
+        }
+        return;
+    }
     const int g = h / a.M;  // query row h reads KV head floor(h / M)
     const int row_len = row_limit(len, h, a.T_q, a.n_new, b);  // tokens this row attends
 
@@ -174,11 +182,18 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     const size_t row = ((size_t)b * a.Hq + h) * a.S + s;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     // partials in the output's precision (bf16 rounded to nearest even for
-    // a bf16 cache)
-    T* orow = static_cast<T*>(a.o_part) + row * D;
+    // a bf16 cache); a single-split pass writes the output row itself
+    T* orow = a.out != nullptr ? static_cast<T*>(a.out) + ((size_t)b * a.Hq + h) * D
+                               : static_cast<T*>(a.o_part) + row * D;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) orow[lane + 64 * k] = from_f32<T>(acc[k] * inv);
-    if (lane == 0) a.lse_part[row] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
+    if (a.out == nullptr) {
+        if (lane == 0) a.lse_part[row] = l_run > 0.f ? m_run + log2f(l_run) : -INFINITY;
+    } else if (sl.appended && a.lengths_adv != nullptr && lane == 0) {
+        // the sequence's Hq workgroups have all read its length once the
+        // last of them arrives
+        advance_when_last(a.seq_ctr + b, a.Hq, a.lengths_adv, b, sl.slot + 1);
+    }
 }
 
 template <typename T, bool PAGED>

@@ -465,8 +465,7 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
             }
         }
         if (gq == 0 && r0 + c < mg)
-            __builtin_nontemporal_store(l > 0.f ? m_ref[rb] + __builtin_log2f(l) : -INFINITY,
-                                        a.lse_part + row0 + (size_t)c * a.S);
+            a.lse_part[row0 + (size_t)c * a.S] = l > 0.f ? m_ref[rb] + __builtin_log2f(l) : -INFINITY;
     }
 }
 

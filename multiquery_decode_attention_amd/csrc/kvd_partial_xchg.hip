@@ -523,16 +523,14 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
                 if constexpr (NC == 4) {
                     const u32x2_t w = {pack_bf16x2(acc[rb][0][i] * inv, acc[rb][1][i] * inv),
                                        pack_bf16x2(acc[rb][2][i] * inv, acc[rb][3][i] * inv)};
-                    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(o));
+                    *reinterpret_cast<u32x2_t*>(o) = w;
                 } else {
-                    __builtin_nontemporal_store(pack_bf16x2(acc[rb][0][i] * inv, acc[rb][1][i] * inv),
-                                                reinterpret_cast<uint32_t*>(o));
+                    *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(acc[rb][0][i] * inv, acc[rb][1][i] * inv);
                 }
             }
         }
         if (wave == 0 && gq == 0 && 16 * rb + c < mg)
-            __builtin_nontemporal_store(l > 0.f ? m_ref[rb] + __builtin_log2f(l) : -INFINITY,
-                                        a.lse_part + row0 + (size_t)(16 * rb + c) * a.S);
+            a.lse_part[row0 + (size_t)(16 * rb + c) * a.S] = l > 0.f ? m_ref[rb] + __builtin_log2f(l) : -INFINITY;
     }
 }
 

@@ -91,65 +91,82 @@ int resolve_variant(const kvdecode_s* h, int T_q = 1) {
 // Split planner.  The grid is splits x (sequences, KV heads [, head groups]);
 // lengths live on the device, so the plan is made for full caches and splits
 // with no tile of a sequence exit at once.  For every candidate split count
-// S the cost model charges
-//   rounds(S) * (bytes of the busiest split + a fixed fill cost) * slots
-//     + partial traffic (written by the partial pass, read by the combine),
-//       charged at 4 bytes per value although bf16 outputs keep bf16
-//       partials: the fill constant was tuned with this charge
-// where rounds(S) = ceil(work units * S / resident slots): a launch whose
-// last round is partly empty wastes the rest of that round.  Among plans
-// within 2% of the cheapest, the one with most splits wins (shorter splits
-// balance ragged lengths better).  At d = 256 the LDS kernel has a second
-// configuration with two workgroups per CU; it is planned first and taken
-// when its splits stay long (kvd::LDS_LONG_MIN_TILES tiles of a full cache).
+// S the cost model charges each round of resident workgroups
+//   (bytes of the busiest split + a fixed fill cost) * max(sat, workgroups in the round)
+// plus the partial traffic (written by the partial pass, read by the
+// combine), charged at 4 bytes per value although bf16 outputs keep bf16
+// partials: the fill constant was tuned with this charge.  Full rounds hold
+// `slots` workgroups (all that fit on the GPU at once); the last round may
+// hold fewer.  `sat` is how many resident workgroups of the kernel already
+// stream the cache at the full HBM rate: a round with fewer is bound by the
+// workgroups' own streaming rate (it costs as much as `sat` of them), one
+// with more by HBM (it costs its bytes).  Among plans within 2% of the
+// cheapest whose workgroups take more than one round, the one with most
+// splits wins: there shorter splits balance ragged lengths and the last
+// round better.  A plan whose workgroups all fit at once gains nothing from
+// shorter splits, and the cheapest stands.  At d = 256 the LDS kernel has a second configuration
+// with two workgroups per CU; it is planned first and taken when its splits
+// stay long (kvd::LDS_LONG_MIN_TILES tiles of a full cache).
 constexpr int CUS = 256;
 
 struct Shape {
     long long units;      // workgroups per split
     long long slots;      // workgroups resident on the whole GPU
+    long long sat;        // resident workgroups that saturate HBM (<= slots)
 };
 
 Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
     const long long bkv = (long long)h->d.batch * h->d.num_kv_heads;
     const int rows = h->M * T_q;  // query rows per KV head
+    const int D = h->d.head_dim;
     Shape sh;
     if (variant == KVD_VARIANT_WAVE) {
-        const int rows_per_group = 16 * kvd::wave_fp8_max_row_blocks(h->d.head_dim);
+        const int rows_per_group = 16 * kvd::wave_fp8_max_row_blocks(D);
         sh.units = bkv * ((rows + rows_per_group - 1) / rows_per_group);
-        sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(h->d.head_dim);
+        sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(D);
     } else if (variant == KVD_VARIANT_XCHG) {
-        sh.units = bkv * kvd::xchg_shape(h->d.head_dim, rows).groups;
-        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(h->d.head_dim, is_fp8(h), rows);
+        sh.units = bkv * kvd::xchg_shape(D, rows).groups;
+        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(D, is_fp8(h), rows);
     } else if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((rows + 63) / 64);
-        sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(h->d.head_dim)
-                                               : kvd::lds_groups_per_cu(h->d.head_dim, lds_which));
+        sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(D) : kvd::lds_groups_per_cu(D, lds_which));
     } else if (variant == KVD_VARIANT_MFMA) {
         const int hb = kvd::mfma_head_blocks(h->M);
         const int nw = hb < 4 ? hb : 4;
         sh.units = bkv * ((hb + nw - 1) / nw);
-        const int waves_per_cu = h->d.head_dim == 256 ? 4 : (h->d.head_dim == 128 ? 8 : 16);
+        const int waves_per_cu = D == 256 ? 4 : (D == 128 ? 8 : 16);
         sh.slots = (long long)CUS * (waves_per_cu / nw > 0 ? waves_per_cu / nw : 1);
     } else {
         sh.units = bkv * rows;
         sh.slots = (long long)CUS * 16;
     }
+    // Measured saturation point: the bf16 LDS kernel with two workgroups
+    // per CU at d = 256 streams a long-context step as fast with 384
+    // workgroups (1.5 per CU) as with 512.  Elsewhere every slot is taken
+    // to be needed: the fp8 exchange kernel, for one, ran the same
+    // long-context step 7 us slower on 256 workgroups than on 512.
+    sh.sat = sh.slots;
+    if (variant == KVD_VARIANT_LDS && !is_fp8(h) && D == 256 && lds_which == kvd::LDS_LONG) sh.sat = sh.slots * 3 / 4;
     return sh;
 }
 
 // Cost-model choice of the split count (at most s_max) for one kernel
 // shape.  Only the smallest S of each busiest-split size ceil(n_tiles / S)
-// is a candidate (a larger S with the same busiest split costs more rounds),
-// and those are enumerated directly: O(sqrt(n_tiles)) of them, twice (the
-// cheapest cost, then the most splits within 2% of it), with no heap memory.
+// is a candidate (a larger S with the same busiest split costs more), and
+// those are enumerated directly: O(sqrt(n_tiles)) of them, twice (the
+// cheapest cost, then the most splits of several rounds within 2% of it),
+// with no heap memory.
 long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long n_tiles, int T_q,
                       long long s_max) {
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * T_q * (h->d.head_dim + 1) * 4 * 2;
     auto cost_of = [&](long long s, long long per) {
-        const long long rounds = (sh.units * s + sh.slots - 1) / sh.slots;
-        return (double)rounds * (per * tile * tok_bytes + fill) * sh.slots + (double)sh.units * s * part_bytes;
+        const long long w = sh.units * s;  // workgroups of the launch
+        const long long full = w / sh.slots, rest = w - full * sh.slots;
+        const double split_cost = per * tile * tok_bytes + fill;
+        return split_cost * ((double)full * sh.slots + (rest > 0 ? (double)(rest > sh.sat ? rest : sh.sat) : 0.0)) +
+               (double)w * part_bytes;
     };
     // visit(s, cost) for every candidate, in increasing s
     auto each_candidate = [&](auto&& visit) {
@@ -161,12 +178,15 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
         }
     };
     double best = 0;
-    each_candidate([&](long long, double cost) {
-        if (best == 0 || cost < best) best = cost;
-    });
     long long pick = 1;
     each_candidate([&](long long s, double cost) {
-        if (cost <= best * 1.02 && s > pick) pick = s;
+        if (best == 0 || cost < best) {
+            best = cost;
+            pick = s;
+        }
+    });
+    each_candidate([&](long long s, double cost) {
+        if (cost <= best * 1.02 && s > pick && sh.units * s > sh.slots) pick = s;
     });
     return pick;
 }
@@ -275,8 +295,10 @@ int32_t ensure_device(kvdecode_s* h) {
     if (h->device >= 0) return dev == h->device ? KVD_OK : KVD_EINVAL;
     // err word; per sequence the attended length of the last step and the
     // rows its last append added; then the dispatch order the combine leaves
-    // for the next partial pass (B entries and a flag, zero: not yet valid)
-    const size_t words = 2 + 3 * (size_t)h->d.batch;
+    // for the next partial pass (B entries and a flag, zero: not yet valid);
+    // then the per-sequence arrival counters of single-split passes (zero
+    // between launches)
+    const size_t words = 2 + 4 * (size_t)h->d.batch;
     e = hipMalloc(reinterpret_cast<void**>(&h->err), words * sizeof(int));
     if (e != hipSuccess) return hip_fail(e);
     e = hipMemset(h->err, 0, words * sizeof(int));
@@ -347,13 +369,22 @@ struct Workspace {
     int* len_att;   // [B]
     int* n_new;     // [B]
     int* order;     // [B] + flag, or null
+    int* seq_ctr;   // [B], zero between launches
     void* o_part;
     float* lse_part;
 };
 
 Workspace handle_workspace(const kvdecode_s* h) {
-    return Workspace{h->err, h->err + 1, h->err + 1 + h->d.batch, h->err + 1 + 2 * h->d.batch, h->o_part,
+    const int B = h->d.batch;
+    return Workspace{h->err, h->err + 1, h->err + 1 + B, h->err + 1 + 2 * B, h->err + 2 + 3 * B, h->o_part,
                      h->lse_part};
+}
+
+// A single-split plan of the LDS or VALU kernel writes the output in the
+// partial pass; no combine launch follows (the combine exists only to merge
+// splits).
+bool single_pass(const kvdecode_s* h, const Plan& p) {
+    return p.splits == 1 && ((p.variant == KVD_VARIANT_LDS && !is_fp8(h)) || p.variant == KVD_VARIANT_VALU);
 }
 
 int32_t launch_append_timed(kvdecode_s* h, const Workspace& ws, const void* k_new, const void* v_new,
@@ -445,6 +476,10 @@ int32_t launch_step(kvdecode_s* h, const Plan& p, const Workspace& ws, const voi
     a.v_exp = h->v_exp;
     a.m_init = h->unified ? h->unified_max * kvd::LOG2E : -INFINITY;
     a.tau = h->unified ? 64.f : 8.f;
+    const bool one_pass = single_pass(h, p);
+    a.out = one_pass ? out : nullptr;
+    a.lengths_adv = one_pass && fused ? h->d.lengths : nullptr;
+    a.seq_ctr = one_pass ? ws.seq_ctr : nullptr;
 
     kvd::CombineArgs c;
     c.o_part = ws.o_part;
@@ -477,8 +512,10 @@ int32_t launch_step(kvdecode_s* h, const Plan& p, const Workspace& ws, const voi
                                                    : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
     if (e != hipSuccess) return KVD_EHIP;
     if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
-    e = kvd::launch_combine(c, h->d.dtype != KVD_F32, st);  // fp8 caches give bf16 outputs
-    if (e != hipSuccess) return KVD_EHIP;
+    if (!one_pass) {
+        e = kvd::launch_combine(c, h->d.dtype != KVD_F32, st);  // fp8 caches give bf16 outputs
+        if (e != hipSuccess) return KVD_EHIP;
+    }
     if (timed) {
         if ((what & KVD_TIME_COMBINE) && hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
         ++h->n_attend;
@@ -528,10 +565,15 @@ int32_t scratch_of(int dev, char** out) {
     return KVD_OK;
 }
 
-// Layout of one step's workspace in the scratch array: the error word, then
-// [B] attended lengths and [B] appended-row counts, then the partials and
-// their log-sum-exps, each 256-byte aligned.  No dispatch order is kept
-// between calls (the array is shared): steps dispatch in batch order.
+// Layout of one step's workspace in the scratch array: the error word; the
+// per-sequence arrival counters of single-split passes, in a region of fixed
+// place and size that nothing else uses, so they stay zero between launches
+// whatever step ran before (the array starts zeroed and each launch leaves
+// them zero); then [B] attended lengths and [B] appended-row counts, then
+// the partials and their log-sum-exps, each 256-byte aligned.  No dispatch
+// order is kept between calls (the array is shared): steps dispatch in
+// batch order.
+constexpr size_t NOALLOC_SEQ_CTR = 256;
 struct ScratchLayout {
     size_t len_att, n_new, o_part, lse, total;
 };
@@ -541,7 +583,7 @@ ScratchLayout scratch_layout(const kvdecode_s* h, const Plan& p) {
     const size_t rows = B * h->d.num_q_heads * (size_t)p.splits;
     const size_t part_elem = h->d.dtype == KVD_F32 ? sizeof(float) : sizeof(uint16_t);
     ScratchLayout l;
-    l.len_att = 256;
+    l.len_att = NOALLOC_SEQ_CTR + 65536 * sizeof(int);  // room for the largest batch a handle takes
     l.n_new = l.len_att + up(B * sizeof(int));
     l.o_part = l.n_new + up(B * sizeof(int));
     l.lse = l.o_part + up(rows * h->d.head_dim * part_elem);
@@ -734,8 +776,12 @@ int32_t kvdecode_append_attend_noalloc(kvdecode_t h, const void* k_new, const vo
     if (hipGetDevice(&dev) != hipSuccess) return KVD_EHIP;
     char* base = nullptr;
     if ((rc = scratch_of(dev, &base)) != KVD_OK) return rc;
-    const Workspace ws{reinterpret_cast<int*>(base), reinterpret_cast<int*>(base + l.len_att),
-                       reinterpret_cast<int*>(base + l.n_new), nullptr, base + l.o_part,
+    const Workspace ws{reinterpret_cast<int*>(base),
+                       reinterpret_cast<int*>(base + l.len_att),
+                       reinterpret_cast<int*>(base + l.n_new),
+                       nullptr,
+                       reinterpret_cast<int*>(base + NOALLOC_SEQ_CTR),
+                       base + l.o_part,
                        reinterpret_cast<float*>(base + l.lse)};
     h->noalloc_device = dev;
     return launch_step(h, p, ws, k_new, v_new, q, out, scale, static_cast<hipStream_t>(stream), 1, false);

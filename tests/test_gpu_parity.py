@@ -109,9 +109,11 @@ def test_shapes_and_ragged_lengths(dtype, variant, Hq, Hkv, D):
                    variant=VARIANTS[variant], splits=splits)
 
 
-def test_empty_sequences_and_poisoned_tails():
+@pytest.mark.parametrize("splits", [None, 1])
+def test_empty_sequences_and_poisoned_tails(splits):
     """len 0 gives a zero row; slots past the length hold NaN/Inf and must
-    never reach the output."""
+    never reach the output.  With one split the partial pass writes the
+    output itself, zero rows included."""
     B, Hq, Hkv, D, T_cap = 5, 48, 1, 256, 200
     case = inputs.make_case(B, Hq, Hkv, D, T_cap, [1, 1, 50, 199, 200], "bf16", seed=7)
     L0 = torch.tensor([0, 0, 49, 198, 199], dtype=torch.int32)
@@ -119,14 +121,15 @@ def test_empty_sequences_and_poisoned_tails():
         case.k_cache[b, :, n + 1:] = float("nan")
         case.v_cache[b, :, n + 1:] = float("inf")
     # sequences 0 and 1: attend without appending -> one empty, checked below
-    out, _, _, L, status, _ = gpu_step(case, Hq, append=False, lengths=L0)
+    out, _, _, L, status, _ = gpu_step(case, Hq, append=False, lengths=L0, splits=splits)
     assert status == kvd.KVD_OK
     ref, _, _, _ = oracle_step(case, append=False, lengths=L0)
     o = to_f64(out)
     assert np.all(o[0] == 0) and np.all(o[1] == 0)
     assert rel_err_rows(o, ref) <= TOL_BF16
     # with the append every sequence is non-empty
-    check_case(case, Hq, "poisoned tails + append", lengths=L0)
+    check_case(case, Hq, f"poisoned tails + append, splits={splits}", lengths=L0, splits=splits)
+    check_case(case, Hq, f"poisoned tails + fused append, splits={splits}", lengths=L0, splits=splits, fused=True)
 
 
 @pytest.mark.parametrize("fused,variant", [(False, "auto"), (True, "lds"), (True, "valu"), (True, "mfma")])
@@ -325,14 +328,17 @@ def test_timing_brackets(what):
         assert t["combine_ms"] == 0 and t["append_ms"] == 0 and t["n_append"] == 0
 
 
+@pytest.mark.parametrize("splits", [0, 1])
 @pytest.mark.parametrize("variant", ["lds", "valu"])
 @pytest.mark.parametrize("Hq,Hkv,D", [(16, 2, 128), (96, 1, 256)])
-def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D):
+def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D, splits):
     """Several steps on one handle over a ragged batch.  From the second
     step on, the LDS kernel dispatches the sequences in the length order the
     previous combine sorted (and 96 heads take two head groups); every
     step's output and appended cache must match the oracle run step by
-    step."""
+    step.  With one split there is no combine: the last of each sequence's
+    workgroups advances its length, counted on a per-sequence counter that
+    every step must leave at zero for the next."""
     B, T_cap, steps = 37, 512, 4
     g = torch.Generator().manual_seed(31 + D)
     lengths = torch.randint(1, T_cap - steps, (B,), generator=g).to(torch.int32)
@@ -344,6 +350,8 @@ def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D):
     L = lengths.to(dev, copy=True)
     cache = kvd.KVCache(kc, vc, L, Hq)
     cache.set_variant(VARIANTS[variant])
+    if splits:
+        cache.set_num_splits(splits)
     k_ref, v_ref = inputs.host_array(case.k_cache), inputs.host_array(case.v_cache)
     L_ref = lengths.numpy().copy()
     try:
@@ -352,7 +360,7 @@ def test_consecutive_steps_ragged_batch(variant, Hq, Hkv, D):
             kn = torch.randn(B, Hkv, D, generator=gs).to(torch.bfloat16)
             vn = torch.randn(B, Hkv, D, generator=gs).to(torch.bfloat16)
             q = torch.randn(B, Hq, D, generator=gs).to(torch.bfloat16)
-            say(f"consecutive steps {variant} Hq={Hq} D={D}: step {step}")
+            say(f"consecutive steps {variant} Hq={Hq} D={D} splits={splits}: step {step}")
             out = cache.step(kn.to(dev), vn.to(dev), q.to(dev), scale=D ** -0.5)
             k_ref, v_ref, L_ref, _ = oracle.append(k_ref, v_ref, L_ref, inputs.host_array(kn), inputs.host_array(vn))
             ref = oracle.decode_attention(inputs.host_array(q), k_ref, v_ref, L_ref, D ** -0.5, oracle.BF16)

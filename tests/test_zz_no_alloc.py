@@ -23,9 +23,10 @@ from gpu_helpers import say, to_f64
 pytestmark = pytest.mark.gpu
 
 
-def one_step(case, Hq, noalloc, lengths=None):
+def one_step(case, Hq, noalloc, lengths=None, splits=0):
     """One decode step on fresh device copies of the case, through the C
-    ABI.  Returns (out, k_cache, v_cache, lengths, status)."""
+    ABI (splits > 0: that split count forced).  Returns (out, k_cache,
+    v_cache, lengths, status)."""
     lib = kvd.library()
     dev = torch.device("cuda")
     kc, vc = case.k_cache.to(dev, copy=True), case.v_cache.to(dev, copy=True)
@@ -37,6 +38,8 @@ def one_step(case, Hq, noalloc, lengths=None):
                                kc.data_ptr(), vc.data_ptr(), L.data_ptr())
     h = ctypes.c_void_p()
     assert lib.kvdecode_create(ctypes.byref(desc), ctypes.byref(h)) == kvd.KVD_OK
+    if splits:
+        assert lib.kvdecode_set_num_splits(h, splits) == kvd.KVD_OK
     stream = torch.cuda.current_stream().cuda_stream
     fn = lib.kvdecode_append_attend_noalloc if noalloc else lib.kvdecode_append_attend
     rc = fn(h, kn.data_ptr(), vn.data_ptr(), q.data_ptr(), out.data_ptr(), ctypes.c_float(case.scale), stream)
@@ -47,11 +50,11 @@ def one_step(case, Hq, noalloc, lengths=None):
     return out, kc, vc, L, status
 
 
-def check_against_allocating_step(case, Hq, tol, name):
+def check_against_allocating_step(case, Hq, tol, name, splits=0):
     say(f"noalloc {name}: B={case.q.shape[0]} Hq={Hq} Hkv={case.k_cache.shape[1]} D={case.q.shape[2]} "
-        f"T_cap={case.k_cache.shape[2]} {case.q.dtype}")
-    got = one_step(case, Hq, noalloc=True)
-    want = one_step(case, Hq, noalloc=False)
+        f"T_cap={case.k_cache.shape[2]} {case.q.dtype} splits={splits}")
+    got = one_step(case, Hq, noalloc=True, splits=splits)
+    want = one_step(case, Hq, noalloc=False, splits=splits)
     assert got[4] == kvd.KVD_OK and want[4] == kvd.KVD_OK, (got[4], want[4])
     for a, b, what in zip(got[:4], want[:4], ("output", "K cache", "V cache", "lengths")):
         assert torch.equal(a, b), f"{name}: {what} differs from kvdecode_append_attend's"
@@ -74,6 +77,18 @@ def test_noalloc_matches_allocating_step_twice_second_smaller():
     check_against_allocating_step(small, 16, 2e-2, "smaller GQA")
     tiny = inputs.make_workload_case(inputs.WORKLOADS["tiny_mqa_f32"], device="cpu")
     check_against_allocating_step(tiny, 8, 1e-3, "tiny fp32")
+
+
+def test_noalloc_single_split_steps():
+    """One-split steps (no combine; the last workgroup of each sequence
+    advances its length on a per-sequence counter in the static buffer),
+    three in a row on the LDS and VALU kernels: each bitwise equal to
+    kvdecode_append_attend, so every step found the counters at zero."""
+    small = inputs.make_case(3, 16, 4, 128, 512, [512, 100, 31], "bf16", seed=504, k_scale=3.0)
+    tiny = inputs.make_workload_case(inputs.WORKLOADS["tiny_mqa_f32"], device="cpu")
+    for rep in range(3):
+        check_against_allocating_step(small, 16, 2e-2, f"smaller GQA one split #{rep}", splits=1)
+        check_against_allocating_step(tiny, 8, 1e-3, f"tiny fp32 one split #{rep}", splits=1)
 
 
 def test_noalloc_errors_are_sticky_until_status():
