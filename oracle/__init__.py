@@ -82,10 +82,16 @@ def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
 
 
 def load(path: str | None = None):
-    """Load (building first if absent) an oracle shared library."""
+    """Load (building first if absent) an oracle shared library.
+    KVD_ORACLE_LIBRARY may name another build of oracle.c (the sanitizer
+    run of the CPU tests uses one)."""
     global _lib
     if path is None:
         if _lib is not None:
+            return _lib
+        other = os.environ.get("KVD_ORACLE_LIBRARY")
+        if other:
+            _lib = load(other)
             return _lib
         if not os.path.exists(_LIB_PATH):
             build()
