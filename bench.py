@@ -58,8 +58,6 @@ KERNEL_SOURCES = {
                  "kvd_internal.h"],
     "xchg_fp8": ["kvd_partial_xchg.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
                  "kvd_internal.h"],
-    "xchg_bf16": ["kvd_partial_xchg.hip", "kvd_fp8_common.h", "kvd_lds_common.h", "kvd_mfma_common.h",
-                  "kvd_internal.h"],
     "mfma": ["kvd_partial_mfma.hip", "kvd_mfma_common.h", "kvd_internal.h"],
     "valu": ["kvd_partial_valu.hip", "kvd_internal.h"],
 }
@@ -371,7 +369,7 @@ def measure(w, args, K, W, keep_first_copy=False) -> dict:
         f"({attend_gbps / traffic.MI355X_HBM_PEAK_GBPS:.1%} of peak)")
 
     # kernel name suffix: the fp8 kernels, and the exchange kernel's bf16 instance
-    kvariant = plan["variant"] + ("_fp8" if fp8 else ("_bf16" if plan["variant"] == "xchg" else ""))
+    kvariant = plan["variant"] + ("_fp8" if fp8 else "")
     # The partial pass is HBM-bound unless its arithmetic intensity passes
     # the bf16 matrix-core ridge (peak FLOP/s over peak bytes/s, about 312
     # FLOP/B): with many query rows per KV head (48 heads times several new

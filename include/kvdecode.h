@@ -89,13 +89,11 @@ typedef enum {
  *         of up to 16 (d = 256) or 48 (d = 128) query rows]), each
  *         streaming its own tiles for all of the group's rows, merged in
  *         LDS at the end.
- *   XCHG: fp8 or bf16 caches with d >= 128, for large query groups: four
- *         waves per (split, KV head[, group of up to 48 (d = 256) or 64
- *         (d = 128) query rows]) split every 64-token tile, by tokens for
- *         the scores and by output columns for the values, and exchange the
- *         softmax weights through LDS, so each fp8 code is widened to bf16
- *         once.  Chosen automatically for fp8 only: on bf16 caches it is
- *         correct but slower than LDS on the workloads measured.
+ *   XCHG: fp8 caches with d >= 128, for large query groups: four waves
+ *         per (split, KV head[, group of up to 48 (d = 256) or 64 (d = 128)
+ *         query rows]) split every 64-token tile, by tokens for the scores
+ *         and by output columns for the values, and exchange the softmax
+ *         weights through LDS, so each fp8 code is widened to bf16 once.
  * (Query rows: heads per KV head times the new tokens of the step.) */
 enum { KVD_VARIANT_AUTO = 0, KVD_VARIANT_VALU = 1, KVD_VARIANT_MFMA = 2, KVD_VARIANT_LDS = 3,
        KVD_VARIANT_WAVE = 4, KVD_VARIANT_XCHG = 5 };
@@ -388,8 +386,8 @@ int32_t kvdecode_set_unified_max(kvdecode_t h, int32_t enable, float phi);
  * group -- up to 16 rows per KV head at d = 256, 48 at d = 128 -- else
  * XCHG, and LDS at d = 64), KVD_VARIANT_VALU (fp32 or bf16),
  * KVD_VARIANT_MFMA (bf16), KVD_VARIANT_LDS (bf16 or fp8),
- * KVD_VARIANT_WAVE (fp8, d >= 128) or KVD_VARIANT_XCHG (fp8 or bf16,
- * d >= 128); KVD_EUNSUPPORTED otherwise.
+ * KVD_VARIANT_WAVE or KVD_VARIANT_XCHG (fp8, d >= 128);
+ * KVD_EUNSUPPORTED otherwise.
  */
 int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant);
 

@@ -333,13 +333,12 @@ inline int wave_fp8_groups_per_cu(int D) {
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
 hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
-// Kernel for large query groups (fp8 and bf16 caches) in which the four
-// waves split every 64-token tile by tokens for the scores and by value
-// columns for the output, exchanging the weights through LDS
-// (kvd_partial_xchg.hip).  A workgroup holds up to xchg_max_row_blocks(D)
-// blocks of 16 query rows (queries and accumulators in registers: three at
-// d = 256, four at d = 128); larger groups take several workgroups of equal
-// row blocks.
+// fp8 kernel for large query groups in which the four waves split every
+// 64-token tile by tokens for the scores and by value columns for the
+// output, exchanging the weights through LDS (kvd_partial_xchg.hip).  A
+// workgroup holds up to xchg_max_row_blocks(D) blocks of 16 query rows
+// (queries and accumulators in registers: three at d = 256, four at
+// d = 128); larger groups take several workgroups of equal row blocks.
 constexpr int XCHG_TILE = 64;
 constexpr int xchg_max_row_blocks(int D) { return D == 256 ? 3 : 4; }
 struct XchgShape {
@@ -351,25 +350,22 @@ inline XchgShape xchg_shape(int D, int rows) {
     const int groups = (blocks + mx - 1) / mx;
     return XchgShape{(blocks + groups - 1) / groups, groups};
 }
-// Ring slots (one 64-token tile's K and V rows, and fp8 exponents, each).
-// Two slots keep two fp8 workgroups per CU at d = 256; four slots with one
+// Ring slots (one 64-token tile's K and V codes and exponents, each).  Two
+// slots keep two workgroups per CU at d = 256; four slots with one
 // workgroup per CU measured slower (long context 80 against 67 us).
 constexpr int xchg_slots(int) { return 2; }
 // LDS of one workgroup: the slots, two weight buffers (16 * R rows of 64
 // bf16) and two buffers of row maxima (16 * R rows of 4 floats).
-constexpr int xchg_lds_bytes(int D, bool fp8, int row_blocks) {
-    return xchg_slots(D) * (2 * XCHG_TILE * D * (fp8 ? 1 : 2) + (fp8 ? 1024 : 0)) +
-           2 * 16 * row_blocks * (2 * XCHG_TILE + 16);
+constexpr int xchg_lds_bytes(int D, int row_blocks) {
+    return xchg_slots(D) * (2 * XCHG_TILE * D + 1024) + 2 * 16 * row_blocks * (2 * XCHG_TILE + 16);
 }
-// Workgroups per CU: at most two (the fp8 instances keep to 256 registers
-// per lane), fewer where the LDS of two exceeds the CU's 160 KB (bf16 rows
-// of 512 bytes at d = 256: one, whose three-block instance also takes more
-// than 256 registers, so one wave per SIMD).
-inline int xchg_groups_per_cu(int D, bool fp8, int rows) {
-    const int g = LDS_BYTES_PER_CU / xchg_lds_bytes(D, fp8, xchg_shape(D, rows).row_blocks);
+// Workgroups per CU: at most two (the kernel keeps to 256 registers per
+// lane), fewer where the LDS of two would exceed the CU's 160 KB.
+inline int xchg_groups_per_cu(int D, int rows) {
+    const int g = LDS_BYTES_PER_CU / xchg_lds_bytes(D, xchg_shape(D, rows).row_blocks);
     return g < 1 ? 1 : (g > 2 ? 2 : g);
 }
-hipError_t launch_partial_xchg(const PartialArgs& a, bool fp8, hipStream_t stream);
+hipError_t launch_partial_xchg(const PartialArgs& a, hipStream_t stream);
 // Quantize T_q >= 1 new bf16 K/V rows per (sequence, KV head)
 // (k_new/v_new [B, Hkv, T_q, D]) into slots lengths[b] .. lengths[b] + T_q - 1
 // (contiguous or paged, the exponent at the row's index) and advance

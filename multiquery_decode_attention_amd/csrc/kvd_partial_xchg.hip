@@ -1,7 +1,7 @@
-// kvd_partial_xchg.hip -- split-KV partial pass over an fp8 (or bf16) KV
-// cache for large query groups (many query heads per KV head, as in
-// multiquery attention), in which the four waves of a workgroup split every
-// tile and exchange the softmax weights through LDS.
+// kvd_partial_xchg.hip -- split-KV partial pass over an fp8 KV cache for
+// large query groups (many query heads per KV head, as in multiquery
+// attention), in which the four waves of a workgroup split every tile and
+// exchange the softmax weights through LDS.
 //
 // Work unit: (split s, sequence b, KV head g[, group hg of up to 16*R query
 // rows]) -> one workgroup of four waves, over 64-token tiles.  In the other
@@ -39,15 +39,8 @@
 // for the same reason.  At d = 256 with 48 rows this is 81408 bytes, two
 // workgroups per CU.
 //
-// The same body serves a bf16 cache (FP8 false): rows are twice as long,
-// there are no exponents and no widening, the weights are not scaled.  At
-// d = 256 a slot then holds 64 KB, one workgroup per CU; the LDS kernel,
-// which keeps every K/V tile in LDS for all four waves' row blocks, is the
-// faster choice there and the exchange kernel runs only when asked for.
-//
 // In a decode step the kernel also appends the new token: the workgroups
-// owning its tile quantize (fp8) or copy (bf16) its rows into the cache
-// slot first (below).
+// owning its tile quantize its rows into the cache slot first (below).
 //
 // Sources: quantized KV caches save memory bandwidth ("All About Transformer
 // Inference", section on tricks for generation throughput); bf16 arithmetic
@@ -67,12 +60,10 @@ using namespace fp8;
 // s_waitcnt lgkmcnt(0), then s_barrier: LDS writes of every wave visible.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// The kernel body for an fp8 cache (FP8) or a bf16 cache.
-template <bool FP8, int D, int R, int NS, bool GROUPED, bool PAGED>
-__device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_groups) {
+template <int D, int R, int NS, bool GROUPED, bool PAGED>
+__global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
     constexpr int TT = XCHG_TILE;          // tokens per tile
-    constexpr int EB = FP8 ? 1 : 2;        // bytes per cached value
-    constexpr int ROWB = D * EB;           // bytes per cache row
+    constexpr int ROWB = D;                // bytes per cache row (one code per value)
     constexpr int CH = ROWB / 16;          // 16-byte chunks per row
     constexpr int SWZ = CH - 1;            // K chunk swizzle mask
     constexpr int VKEY = CH / 4;           // V chunk swizzle step per 8-token group
@@ -82,13 +73,13 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
     constexpr int ROWS = 16 * R;           // query rows per workgroup
     constexpr int NKV = 16 * ROWB / 1024;  // 1 KB loads of a wave's 16 K (or V) rows
     constexpr int REGION = TT * ROWB;      // bytes of K (or V) rows per slot
-    constexpr int XBYTES = FP8 ? 4 * 256 : 0;  // exponents per slot: 256 bytes per wave
+    constexpr int XBYTES = 4 * 256;        // exponents per slot: 256 bytes per wave
     constexpr int SLOT = 2 * REGION + XBYTES;
     constexpr int PST = 2 * TT;            // bytes per row of weights
     constexpr int PBUF = ROWS * PST;
     constexpr int MBUF = ROWS * 4 * 4;     // per row, the maxima of the four waves
     constexpr int P_AT = NS * SLOT, M_AT = P_AT + 2 * PBUF;
-    constexpr int KX = NKV + (FP8 ? 1 : 0);  // loads of a wave's K rows (and exponents) per tile
+    constexpr int KX = NKV + 1;            // loads of a wave's K rows and exponents per tile
     constexpr int PERT = NKV + KX;            // loads of a wave per tile
     static_assert(NC == 2 || NC == 4, "d = 128 or 256");
     static_assert(NS >= 2 && (NS - 1) * PERT < 64, "vmcnt range");
@@ -131,14 +122,8 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
                 row = kv_row_contiguous(b, g, a.Hkv, a.T_cap, sl.slot);
             const uint16_t* src = static_cast<const uint16_t*>(wave ? a.v_new : a.k_new) + ((size_t)b * a.Hkv + g) * D;
             uint8_t* cache = static_cast<uint8_t*>(const_cast<void*>(wave ? a.v_cache : a.k_cache));
-            if constexpr (FP8) {
-                int8_t* exps = const_cast<int8_t*>(wave ? a.v_exp : a.k_exp);
-                quantize_row<D>(src, cache + row * D, exps + row, lane);
-            } else {  // a bit copy: lane l copies values l*D/64 .. (l+1)*D/64 - 1
-                uint16_t* dst = reinterpret_cast<uint16_t*>(cache) + row * D;
-#pragma unroll
-                for (int i = 0; i < D / 64; ++i) dst[lane * (D / 64) + i] = src[lane * (D / 64) + i];
-            }
+            int8_t* exps = const_cast<int8_t*>(wave ? a.v_exp : a.k_exp);
+            quantize_row<D>(src, cache + row * D, exps + row, lane);
         }
         __syncthreads();
     }
@@ -230,7 +215,7 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
 #pragma unroll
             for (int n = 0; n < NKV; ++n)
                 __builtin_amdgcn_global_load_lds((const void*)kb, (lds_void_t*)(kd + n * 1024), 16, 0, 0);
-            if constexpr (FP8) __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)xd, 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)ke, (lds_void_t*)xd, 4, 0, 0);
             return;
         }
         const int tb = block_t(k);
@@ -254,11 +239,9 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
         // exponents of rows 4(q-4) ..; lanes 8-63 repeat them.  Bytes 0-15
         // are K, 16-31 V; those of rows past the sequence's end are never
         // used (the 16 rows lie inside the cache row or page).
-        if constexpr (FP8) {
-            const int q = lane & 7;
-            __builtin_amdgcn_global_load_lds((const void*)((q < 4 ? ke : ve) + r0 + 4 * (q & 3)), (lds_void_t*)xd, 4,
-                                             0, 0);
-        }
+        const int q = lane & 7;
+        __builtin_amdgcn_global_load_lds((const void*)((q < 4 ? ke : ve) + r0 + 4 * (q & 3)), (lds_void_t*)xd, 4, 0,
+                                         0);
     };
     auto issue_v = [&](int k) {
         unsigned char* vd = lds + (k % NS) * SLOT + REGION + 16 * wave * ROWB;
@@ -283,22 +266,17 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
     };
 
     // LDS read offsets.  Score operand: K row 16*wave + c, values 32ks + 8gq
-    // .. +7 (half of a swizzled chunk of codes, or a whole chunk of bf16).
+    // .. +7 (half of a swizzled chunk of codes).
     // Value operand: V rows 8gq + j (+32 for the second half of the tile),
     // columns vcol .. vcol+NC-1.
     uint32_t koff[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (FP8) {
-            const int p = 2 * ks + (gq >> 1);
-            koff[ks] = (uint32_t)(16 * wave * ROWB + (c * CH + (p ^ (c & SWZ))) * 16 + 8 * (gq & 1));
-        } else {
-            const int p = 4 * ks + gq;
-            koff[ks] = (uint32_t)(16 * wave * ROWB + (c * CH + (p ^ (c & SWZ))) * 16);
-        }
+        const int p = 2 * ks + (gq >> 1);
+        koff[ks] = (uint32_t)(16 * wave * ROWB + (c * CH + (p ^ (c & SWZ))) * 16 + 8 * (gq & 1));
     }
     const int vcol = wave * DQ + NC * c;
-    const int vbyte = vcol * EB;
+    const int vbyte = vcol;
     const uint32_t voff = (uint32_t)(REGION + 8 * gq * ROWB + (((vbyte >> 4) ^ (gq * VKEY)) << 4) + (vbyte & 15));
 
     f32x4_t acc[R][NC];
@@ -330,20 +308,15 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
         wait_vm<(NS - 1) * PERT>();
 
         // scores of the wave's 16 tokens for every row block: each K row
-        // read once (fp8: widened once, with its own 2^e; a row past the
+        // read and widened once, with its own 2^e (a row past the
         // sequence's end holds the last row's codes and takes its 2^e too)
-        float sk = 1.f;
-        if constexpr (FP8) sk = pow2_scale(X[min(c, len - 1 - block_t(it))]);
+        const float sk = pow2_scale(X[min(c, len - 1 - block_t(it))]);
         f32x4_t sc[R];
 #pragma unroll
         for (int rb = 0; rb < R; ++rb) sc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4_t kop;
-            if constexpr (FP8)
-                kop = widen8(*reinterpret_cast<const u32x2_t*>(slot + koff[ks]), sk);
-            else
-                kop = *reinterpret_cast<const u32x4_t*>(slot + koff[ks]);
+            const u32x4_t kop = widen8(*reinterpret_cast<const u32x2_t*>(slot + koff[ks]), sk);
 #pragma unroll
             for (int rb = 0; rb < R; ++rb) sc[rb] = mfma16x16x32(kop, qop[rb][ks], sc[rb]);
         }
@@ -369,7 +342,7 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
         // 2^(x * scale - m) summed as they are, times the token's 2^e for the
         // value product.  A row with no token yet keeps m_ref = -inf and
         // weighs 0.
-        const uint32_t xv = FP8 ? *reinterpret_cast<const uint32_t*>(X + 16 + 4 * gq) : 0u;
+        const uint32_t xv = *reinterpret_cast<const uint32_t*>(X + 16 + 4 * gq);
         float lt[R];
         // weight row r holds its 16-byte chunk h at position h ^ ((r >> 1) & 7):
         // lane (c, gq) writes tokens 16*wave + 4gq .. +3 (half a chunk)
@@ -385,7 +358,7 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
                 for (int i = 0; i < 4; ++i) {
                     p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[rb][i], sl, -m_sub));
                     sum += p[i];
-                    if constexpr (FP8) p[i] *= pow2_scale((int)(signed char)(xv >> (8 * i)));
+                    p[i] *= pow2_scale((int)(signed char)(xv >> (8 * i)));
                 }
                 lt[rb] = sum;
                 const u32x2_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
@@ -445,42 +418,28 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
         // values: the 64 tokens' weights of every row times this wave's
         // columns of the V rows, each value read (and widened) once for all
         // row blocks.  A lane holds NC values (its columns) of each of tokens
-        // 8gq + j.  fp8: byte permutes pair tokens 2m and 2m+1 column by
-        // column before widening, so each widened dword is dword m of one
-        // column block's operand; bf16: halfword permutes pair them.
+        // 8gq + j; byte permutes pair tokens 2m and 2m+1 column by column
+        // before widening, so each widened dword is dword m of one column
+        // block's operand.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4_t vop[NC];
-            if constexpr (FP8) {
-                uint32_t w[8];
+            uint32_t w[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const unsigned char* vp = slot + voff + (32 * h + j) * ROWB;
-                    w[j] = NC == 4 ? *reinterpret_cast<const uint32_t*>(vp)
-                                   : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
+            for (int j = 0; j < 8; ++j) {
+                const unsigned char* vp = slot + voff + (32 * h + j) * ROWB;
+                w[j] = NC == 4 ? *reinterpret_cast<const uint32_t*>(vp) : (uint32_t)*reinterpret_cast<const uint16_t*>(vp);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t c01 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05010400u);
+                vop[0][m] = widen2<false>(c01, 1.0f);
+                vop[1][m] = widen2<true>(c01, 1.0f);
+                if constexpr (NC == 4) {
+                    const uint32_t c23 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07030602u);
+                    vop[2][m] = widen2<false>(c23, 1.0f);
+                    vop[3][m] = widen2<true>(c23, 1.0f);
                 }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t c01 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x05010400u);
-                    vop[0][m] = widen2<false>(c01, 1.0f);
-                    vop[1][m] = widen2<true>(c01, 1.0f);
-                    if constexpr (NC == 4) {
-                        const uint32_t c23 = __builtin_amdgcn_perm(w[2 * m + 1], w[2 * m], 0x07030602u);
-                        vop[2][m] = widen2<false>(c23, 1.0f);
-                        vop[3][m] = widen2<true>(c23, 1.0f);
-                    }
-                }
-            } else {
-                constexpr int VW = NC / 2;  // dwords of bf16 pairs per token
-                uint32_t v[8][VW];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const unsigned char* vp = slot + voff + (32 * h + j) * ROWB;
-#pragma unroll
-                    for (int i = 0; i < VW; ++i) v[j][i] = reinterpret_cast<const uint32_t*>(vp)[i];
-                }
-#pragma unroll
-                for (int e = 0; e < NC; ++e) vop[e] = v_operand(v, e);
             }
             u32x4_t pop[R];
 #pragma unroll
@@ -534,68 +493,50 @@ __device__ __forceinline__ void partial_xchg(const PartialArgs& a, int head_grou
     }
 }
 
-// One kernel per cache type, so traces and counters name it.
 template <int D, int R, int NS, bool GROUPED, bool PAGED>
-__global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a, int head_groups) {
-    partial_xchg<true, D, R, NS, GROUPED, PAGED>(a, head_groups);
-}
-template <int D, int R, int NS, bool GROUPED, bool PAGED>
-__global__ __launch_bounds__(256, 2) void partial_xchg_bf16_kernel(PartialArgs a, int head_groups) {
-    partial_xchg<false, D, R, NS, GROUPED, PAGED>(a, head_groups);
-}
-
-template <bool FP8, int D, int R, int NS, bool GROUPED, bool PAGED>
 void launch_one(const PartialArgs& a, int groups, hipStream_t stream) {
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
-    if constexpr (FP8)
-        hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
-    else
-        hipLaunchKernelGGL((partial_xchg_bf16_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
+    hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
 }
 
-template <bool FP8, int D, int R>
+template <int D, int R>
 hipError_t launch_r(const PartialArgs& a, int groups, hipStream_t stream) {
     constexpr int NS = xchg_slots(D);
     const bool paged = a.kv.block_table != nullptr;
     if (groups == 1) {
         if (paged)
-            launch_one<FP8, D, R, NS, false, true>(a, 1, stream);
+            launch_one<D, R, NS, false, true>(a, 1, stream);
         else
-            launch_one<FP8, D, R, NS, false, false>(a, 1, stream);
+            launch_one<D, R, NS, false, false>(a, 1, stream);
     } else {
         if (paged)
-            launch_one<FP8, D, R, NS, true, true>(a, groups, stream);
+            launch_one<D, R, NS, true, true>(a, groups, stream);
         else
-            launch_one<FP8, D, R, NS, true, false>(a, groups, stream);
+            launch_one<D, R, NS, true, false>(a, groups, stream);
     }
     return hipGetLastError();
 }
 
-template <bool FP8>
-hipError_t launch_t(const PartialArgs& a, hipStream_t stream) {
+}  // namespace
+
+hipError_t launch_partial_xchg(const PartialArgs& a, hipStream_t stream) {
     const XchgShape x = xchg_shape(a.D, a.M);
     if (a.D == 256) {
         switch (x.row_blocks) {
-            case 1: return launch_r<FP8, 256, 1>(a, x.groups, stream);
-            case 2: return launch_r<FP8, 256, 2>(a, x.groups, stream);
-            default: return launch_r<FP8, 256, 3>(a, x.groups, stream);
+            case 1: return launch_r<256, 1>(a, x.groups, stream);
+            case 2: return launch_r<256, 2>(a, x.groups, stream);
+            default: return launch_r<256, 3>(a, x.groups, stream);
         }
     }
     if (a.D == 128) {
         switch (x.row_blocks) {
-            case 1: return launch_r<FP8, 128, 1>(a, x.groups, stream);
-            case 2: return launch_r<FP8, 128, 2>(a, x.groups, stream);
-            case 3: return launch_r<FP8, 128, 3>(a, x.groups, stream);
-            default: return launch_r<FP8, 128, 4>(a, x.groups, stream);
+            case 1: return launch_r<128, 1>(a, x.groups, stream);
+            case 2: return launch_r<128, 2>(a, x.groups, stream);
+            case 3: return launch_r<128, 3>(a, x.groups, stream);
+            default: return launch_r<128, 4>(a, x.groups, stream);
         }
     }
     return hipErrorInvalidValue;
-}
-
-}  // namespace
-
-hipError_t launch_partial_xchg(const PartialArgs& a, bool fp8, hipStream_t stream) {
-    return fp8 ? launch_t<true>(a, stream) : launch_t<false>(a, stream);
 }
 
 }  // namespace kvd

@@ -126,7 +126,7 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
         sh.slots = (long long)CUS * kvd::wave_fp8_groups_per_cu(D);
     } else if (variant == KVD_VARIANT_XCHG) {
         sh.units = bkv * kvd::xchg_shape(D, rows).groups;
-        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(D, is_fp8(h), rows);
+        sh.slots = (long long)CUS * kvd::xchg_groups_per_cu(D, rows);
     } else if (variant == KVD_VARIANT_LDS) {
         sh.units = bkv * ((rows + 63) / 64);
         sh.slots = (long long)CUS * (is_fp8(h) ? kvd::lds_fp8_groups_per_cu(D) : kvd::lds_groups_per_cu(D, lds_which));
@@ -431,7 +431,8 @@ int32_t check_step(kvdecode_s* h, const void* q, void* out, float scale, int T_q
 
 // One step's launches on a given workspace: optionally the append kernel,
 // the partial pass, the combine.  The LDS and VALU kernels fold a one-token
-// append into the partial pass (the combine then advances lengths), as do
+// append into the partial pass (the combine then advances lengths, or a
+// one-split pass of those kernels does, with no combine), as do
 // the fp8 wave and exchange kernels; the other kernels, and several new
 // tokens, launch the append kernel first.  T_q > 1: a step with T_q new
 // tokens per sequence (append then causal attend of their T_q queries); q
@@ -505,7 +506,7 @@ int32_t launch_step(kvdecode_s* h, const Plan& p, const Workspace& ws, const voi
     hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
     if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
     hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, st)
-                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg(a, is_fp8(h), st)
+                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg(a, st)
                    : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, st)
                    : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
                    : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
@@ -852,8 +853,7 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
         clear_plans(h);
         return KVD_OK;
     }
-    if (variant == KVD_VARIANT_WAVE) return KVD_EUNSUPPORTED;
-    if (variant == KVD_VARIANT_XCHG && (h->d.dtype != KVD_BF16 || h->d.head_dim < 128)) return KVD_EUNSUPPORTED;
+    if (variant == KVD_VARIANT_WAVE || variant == KVD_VARIANT_XCHG) return KVD_EUNSUPPORTED;
     if ((variant == KVD_VARIANT_MFMA || variant == KVD_VARIANT_LDS) && h->d.dtype != KVD_BF16)
         return KVD_EUNSUPPORTED;
     if (variant == KVD_VARIANT_MFMA && h->kv.block_table) return KVD_EUNSUPPORTED;

@@ -19,8 +19,7 @@ from gpu_helpers import gpu_step, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS,
-            "xchg": kvd.KVD_VARIANT_XCHG}
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS}
 
 
 def multi_step(case, Hq, *, variant="auto", splits=None, page_size=0, reserve=0):

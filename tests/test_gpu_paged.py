@@ -20,8 +20,7 @@ from gpu_helpers import gpu_step, say, to_f64
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS,
-            "xchg": kvd.KVD_VARIANT_XCHG}
+VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "lds": kvd.KVD_VARIANT_LDS}
 
 
 def paged_step(case, Hq, page_size, *, seed=11, variant="auto", splits=None, fused=True,
