@@ -47,6 +47,9 @@ __device__ __forceinline__ size_t kv_row_paged(const KvLayout& L, int page, int 
 // Tokens per inner iteration of each partial-pass kernel.
 constexpr int MFMA_TILE = 32;
 constexpr int VALU_TILE = 64;
+// Waves per workgroup of the vector-ALU kernel; each takes every
+// VALU_WAVES-th tile of the workgroup's split.
+constexpr int VALU_WAVES = 4;
 
 // Query heads per MFMA head block (rows of the 16x16 output tile).
 constexpr int MFMA_HEADS = 16;

@@ -1,11 +1,16 @@
 // kvd_partial_valu.hip -- vector-ALU split-KV partial pass (any dtype).
 //
-// One wave per (split, query head, sequence).  Lane t of the wave scores
-// token t0+t of a 64-token tile against the query held in LDS, the wave keeps
-// the running maximum and sum of the split's softmax with cross-lane
-// reductions, and every lane accumulates the probability-weighted values for
-// D/64 of the head's columns.  The split's result is stored normalised,
-// together with its base-2 log-sum-exp, for the combine pass.
+// One workgroup of four waves per (split, query head, sequence); wave w takes
+// the split's tiles w, w+4, ... (of its own tiles s, s+S, ...).  Lane t of a
+// wave scores token t0+t of a 64-token tile against the query held in LDS,
+// the wave keeps the running maximum and sum of its share of the softmax
+// with cross-lane reductions, and every lane accumulates the
+// probability-weighted values for D/64 of the head's columns.  The four
+// waves' states then merge in LDS by the same log-sum-exp rescaling as the
+// combine, and the split's result is stored normalised, with its base-2
+// log-sum-exp, for the combine pass -- or, in a one-split pass, as the
+// output row itself.  Four waves take four tiles at once: a short sequence
+// costs one tile's latency rather than one per tile.
 //
 // With k_new/v_new set (one decode step) the append is folded in: the new
 // token's row is read from k_new/v_new and copied to its cache slot here.
@@ -57,16 +62,17 @@ __device__ inline float wave_sum(float v) {
 }
 
 template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
+__global__ __launch_bounds__(64 * VALU_WAVES) void partial_valu_kernel(PartialArgs a) {
     constexpr int DPL = D / 64;  // value columns per lane
     // unit = (sequence b, query head h), head fastest
     const BlockCoord bc = block_coord(a.B * a.Hq);
     const int s = bc.split;
     const int h = bc.unit % a.Hq;
     const int b = bc.unit / a.Hq;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const SeqLen sl = sequence_length(a.lengths, a.err, a.len_att, b, a.T_cap, a.k_new != nullptr,
-                                      s == 0 && h == 0 && lane == 0);
+                                      s == 0 && h == 0 && threadIdx.x == 0);
     const int len = sl.len;
     const int n_seq_tiles = (len + VALU_TILE - 1) / VALU_TILE;
     if (s >= n_seq_tiles) {
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         // writes the zero row of a sequence with no tokens
         if (a.out != nullptr && n_seq_tiles == 0) {
             T* orow = static_cast<T*>(a.out) + ((size_t)b * a.Hq + h) * D;
-            for (int d = lane; d < D; d += 64) orow[d] = from_f32<T>(0.f);
+            for (int d = threadIdx.x; d < D; d += 64 * VALU_WAVES) orow[d] = from_f32<T>(0.f);
         }
         return;
     }
@@ -83,7 +89,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
 
     __shared__ float qs[D];
     const T* qrow = static_cast<const T*>(a.q) + ((size_t)b * a.Hq + h) * D;
-    for (int d = lane; d < D; d += 64) qs[d] = to_f32(qrow[d]);
+    for (int d = threadIdx.x; d < D; d += 64 * VALU_WAVES) qs[d] = to_f32(qrow[d]);
     __syncthreads();
 
     // Rows are counted from kb/vb: the (b, g) slab of a contiguous cache, or
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     };
 
     // Fused append: the new token (slot sl.slot, the sequence's last) is
-    // read from k_new/v_new, and the wave of the group's first head in the
+    // read from k_new/v_new, and wave 0 of the group's first head in the
     // split owning its tile writes it to the cache slot, which nothing else
     // in this launch reads.
     const T* knew = nullptr;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         const size_t nrow = ((size_t)b * a.Hkv + g) * D;
         knew = static_cast<const T*>(a.k_new) + nrow;
         vnew = static_cast<const T*>(a.v_new) + nrow;
-        if (h % a.M == 0 && s == (slot / VALU_TILE) % a.S) {
+        if (wave == 0 && h % a.M == 0 && s == (slot / VALU_TILE) % a.S) {
             const size_t row = (size_t)row_of(slot);
             T* kw = const_cast<T*>(kb) + row * D;
             T* vw = const_cast<T*>(vb) + row * D;
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
     for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int tile = s; tile < n_seq_tiles; tile += a.S) {
+    for (int tile = s + wave * a.S; tile < n_seq_tiles; tile += VALU_WAVES * a.S) {
         const int t0 = tile * VALU_TILE;
         const int t = t0 + lane;
         // the row of this lane's token (of the sequence's last token past
@@ -179,6 +185,32 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
         }
     }
 
+    // The four waves' states meet in LDS: rescaled to the largest reference
+    // m, the sums and accumulators add (a wave with no token weighs 0).
+    __shared__ float ml[VALU_WAVES][2];
+    __shared__ float accs[VALU_WAVES][D];
+    if (lane == 0) {
+        ml[wave][0] = m_run;
+        ml[wave][1] = l_run;
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) accs[wave][lane + 64 * k] = acc[k];
+    __syncthreads();
+    if (wave != 0) return;
+    float m_all = ml[0][0];
+#pragma unroll
+    for (int w = 1; w < VALU_WAVES; ++w) m_all = fmaxf(m_all, ml[w][0]);
+    l_run = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < VALU_WAVES; ++w) {
+        const float f = ml[w][0] == -INFINITY ? 0.f : exp2f(ml[w][0] - m_all);
+        l_run = fmaf(f, ml[w][1], l_run);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(f, accs[w][lane + 64 * k], acc[k]);
+    }
+    m_run = m_all;
     const size_t row = ((size_t)b * a.Hq + h) * a.S + s;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     // partials in the output's precision (bf16 rounded to nearest even for
@@ -198,7 +230,7 @@ __global__ __launch_bounds__(64) void partial_valu_kernel(PartialArgs a) {
 
 template <typename T, bool PAGED>
 hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
-    dim3 grid((unsigned)a.S * a.B * a.Hq), block(64);
+    dim3 grid((unsigned)a.S * a.B * a.Hq), block(64 * VALU_WAVES);
     switch (a.D) {
         case 64: hipLaunchKernelGGL((partial_valu_kernel<T, 64, PAGED>), grid, block, 0, stream, a); break;
         case 128: hipLaunchKernelGGL((partial_valu_kernel<T, 128, PAGED>), grid, block, 0, stream, a); break;

@@ -113,6 +113,7 @@ struct Shape {
     long long units;      // workgroups per split
     long long slots;      // workgroups resident on the whole GPU
     long long sat;        // resident workgroups that saturate HBM (<= slots)
+    int waves = 1;        // tiles of a split a workgroup streams at once
 };
 
 Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
@@ -137,8 +138,10 @@ Shape shape_for(const kvdecode_s* h, int variant, int lds_which, int T_q) {
         const int waves_per_cu = D == 256 ? 4 : (D == 128 ? 8 : 16);
         sh.slots = (long long)CUS * (waves_per_cu / nw > 0 ? waves_per_cu / nw : 1);
     } else {
+        // vector-ALU kernel: one workgroup of VALU_WAVES waves per query row
         sh.units = bkv * rows;
-        sh.slots = (long long)CUS * 16;
+        sh.slots = (long long)CUS * 16 / kvd::VALU_WAVES;
+        sh.waves = kvd::VALU_WAVES;
     }
     // Measured saturation point: the bf16 LDS kernel with two workgroups
     // per CU at d = 256 streams a long-context step as fast with 384
@@ -161,10 +164,12 @@ long long plan_splits(const kvdecode_s* h, const Shape& sh, int tile, long long 
     const double tok_bytes = 2.0 * h->d.head_dim * h->elem + (is_fp8(h) ? 2 : 0);  // K+V of one token
     const double fill = 32.0 * 1024;                              // pipeline fill per split
     const double part_bytes = (double)h->M * T_q * (h->d.head_dim + 1) * 4 * 2;
+    // the vector-ALU kernel's waves take a split's tiles VALU_WAVES at a time
+    const int waves = sh.waves;
     auto cost_of = [&](long long s, long long per) {
         const long long w = sh.units * s;  // workgroups of the launch
         const long long full = w / sh.slots, rest = w - full * sh.slots;
-        const double split_cost = per * tile * tok_bytes + fill;
+        const double split_cost = (double)((per + waves - 1) / waves) * tile * tok_bytes + fill;
         return split_cost * ((double)full * sh.slots + (rest > 0 ? (double)(rest > sh.sat ? rest : sh.sat) : 0.0)) +
                (double)w * part_bytes;
     };
@@ -219,7 +224,7 @@ GridShape partial_grid(const kvdecode_s* h, int variant, int T_q) {
         g.threads = 64 * nw;
     } else {
         g.blocks_per_split = (long long)h->d.batch * h->d.num_q_heads * T_q;
-        g.threads = 64;
+        g.threads = 64 * kvd::VALU_WAVES;
     }
     return g;
 }
