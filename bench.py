@@ -368,7 +368,7 @@ def measure(w, args, K, W, keep_first_copy=False) -> dict:
         f"{statistics.median(part_us):.1f}); attend median {attend_med:.1f} us, {attend_gbps:.0f} GB/s "
         f"({attend_gbps / traffic.MI355X_HBM_PEAK_GBPS:.1%} of peak)")
 
-    # kernel name suffix: the fp8 kernels, and the exchange kernel's bf16 instance
+    # kernel name suffix of the fp8 kernels
     kvariant = plan["variant"] + ("_fp8" if fp8 else "")
     # The partial pass is HBM-bound unless its arithmetic intensity passes
     # the bf16 matrix-core ridge (peak FLOP/s over peak bytes/s, about 312

@@ -79,7 +79,8 @@ typedef enum {
 } kvd_status_t;
 
 /* Kernel variants for the partial pass (kvdecode_set_variant).
- *   VALU: vector-ALU kernel, fp32 or bf16, one wave per (split, query head).
+ *   VALU: vector-ALU kernel, fp32 or bf16, one four-wave workgroup per
+ *         (split, query head), each wave taking every fourth tile.
  *   MFMA: bf16 matrix-core kernel, one wave per 16 query heads, each wave
  *         loading K/V straight into registers.
  *   LDS:  bf16 matrix-core kernel, four waves per (split, KV head) sharing

@@ -69,9 +69,10 @@ struct PartialArgs {
     float* lse_part;        // [B, Hq, S]    base-2 log-sum-exp of each split
     int* err;               // sticky error word
     int* len_att;           // [B] attended length of each sequence, for the combine
-    // Fused append (LDS kernel only; null otherwise): the new token's K/V,
-    // [B, Hkv, D].  Slot lengths[b] of the cache receives them and the pass
-    // attends lengths[b] + 1 tokens; lengths itself is advanced by the combine.
+    // Fused append (null otherwise): the new token's K/V, [B, Hkv, D].  Slot
+    // lengths[b] of the cache receives them and the pass attends
+    // lengths[b] + 1 tokens; lengths itself is advanced by the combine (or,
+    // in a one-split pass, by the pass: see lengths_adv below).
     const void* k_new;
     const void* v_new;
     KvLayout kv;            // contiguous or paged cache rows
