@@ -11,8 +11,10 @@ independent cache copies are cycled so that no step finds its cache in the
 between).
 
 Each workload runs W warm-up steps, then K steps with nothing recorded on the
-stream (the value pass), then K more steps with HIP events around the partial
-pass and the combine, read after every step (the kernel-time pass).
+stream (the value pass), then K more steps with HIP events on the partial pass
+and the combine, read after every step (the kernel-time pass).  The events
+ride on the launches (the dispatch stamps each kernel's start and end), so
+they add no command to the stream and time the kernels alone.
 
 Prints one JSON line:
   value        value pass: step throughput in algorithmic GB/s (K/V of the
@@ -204,7 +206,7 @@ def main():
 def measure(w, args, K, W, keep_first_copy=False) -> dict:
     """One workload: build cache copies, run W warm-up steps, K timed steps
     with nothing recorded on the stream (the `value` pass), then K more steps
-    with HIP events around the partial pass and the combine, read after every
+    with HIP events on the partial pass and the combine, read after every
     step (the kernel-time pass).  Returns the figures of both passes."""
     import statistics
     import torch
@@ -336,8 +338,8 @@ def measure(w, args, K, W, keep_first_copy=False) -> dict:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # kernel-time pass: K more steps, each bracketed by HIP events around
-    # the partial pass and the combine and read at once (per-step durations)
+    # kernel-time pass: K more steps whose partial and combine launches carry
+    # HIP events, read at once (per-step kernel durations)
     for c in copies:
         kvd.kvdecode_timing_enable(c["cache"].handle, 1, kvd.KVD_TIME_PARTIAL | kvd.KVD_TIME_COMBINE)
     part_us, comb_us = [], []

@@ -401,12 +401,13 @@ int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
                           int32_t* split_tokens);
 
 /*
- * Kernel timing with HIP events recorded on the call's stream.  `what` picks
- * the brackets: KVD_TIME_PARTIAL around the partial-pass launch of each
- * attend, KVD_TIME_COMBINE around its combine launch (an empty bracket
- * after a one-split pass, which launches none), KVD_TIME_APPEND around
- * a separate append kernel.  Every recorded event costs the stream about
- * 2 us, so ask only for what is read.
+ * Kernel timing with HIP events.  `what` picks the brackets: KVD_TIME_PARTIAL
+ * the partial-pass kernel of each attend, KVD_TIME_COMBINE its combine
+ * kernel (zero for a one-split pass, which launches none), KVD_TIME_APPEND
+ * a separate append kernel.  The events ride on the timed launches (HIP's
+ * extended launch stamps them with the kernel's start and end), so timing
+ * adds no command to the stream and a bracket holds its kernel alone, not
+ * the gaps between launches.
  * kvdecode_timing_enable(h, n, what) allocates n event slots (n = 0 or
  * what = 0 disables and frees them); at most n attends (and n appends) are
  * timed before the slots are full.  KVD_EINVAL for n < 0 or unknown bits.

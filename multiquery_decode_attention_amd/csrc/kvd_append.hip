@@ -116,9 +116,9 @@ __global__ __launch_bounds__(64 * APPEND_FP8_WAVES) void append_fp8_kernel(const
 
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                              int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
-                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, hipStream_t stream) {
+                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, const Launch& on) {
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, dim3(B), dim3(64 * APPEND_FP8_WAVES), 0, stream, static_cast<const uint16_t*>(k_new),
+        KVD_LAUNCH(kernel, dim3(B), dim3(64 * APPEND_FP8_WAVES), 0, on, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), static_cast<uint8_t*>(k_cache),
                            static_cast<uint8_t*>(v_cache), k_exp, v_exp, kv, lengths, err, n_new, Hkv, T_cap, T_q);
     };
@@ -133,9 +133,9 @@ hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache
 
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const KvLayout& kv, int32_t* lengths, int* err, int* n_new, int B, int Hkv,
-                         int D, int T_cap, int T_q, int elem_bytes, hipStream_t stream) {
+                         int D, int T_cap, int T_q, int elem_bytes, const Launch& on) {
     const int vec_per_row = D * elem_bytes / 16;
-    hipLaunchKernelGGL(append_kernel, dim3(B), dim3(256), 0, stream,
+    KVD_LAUNCH(append_kernel, dim3(B), dim3(256), 0, on,
                        static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                        static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), kv, lengths,
                        err, n_new, Hkv, vec_per_row, T_cap, T_q);

@@ -220,20 +220,20 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
 }
 
 template <typename T>
-hipError_t launch_t(const CombineArgs& a, int U, dim3 grid, hipStream_t stream) {
+hipError_t launch_t(const CombineArgs& a, int U, dim3 grid, const Launch& on) {
     switch (U) {
-        case 1: hipLaunchKernelGGL((combine_kernel<T, 1>), grid, dim3(THREADS), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((combine_kernel<T, 2>), grid, dim3(THREADS), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((combine_kernel<T, 4>), grid, dim3(THREADS), 0, stream, a); break;
-        case 8: hipLaunchKernelGGL((combine_kernel<T, 8>), grid, dim3(THREADS), 0, stream, a); break;
-        default: hipLaunchKernelGGL((combine_kernel<T, MAX_UNROLL>), grid, dim3(THREADS), 0, stream, a); break;
+        case 1: KVD_LAUNCH((combine_kernel<T, 1>), grid, dim3(THREADS), 0, on, a); break;
+        case 2: KVD_LAUNCH((combine_kernel<T, 2>), grid, dim3(THREADS), 0, on, a); break;
+        case 4: KVD_LAUNCH((combine_kernel<T, 4>), grid, dim3(THREADS), 0, on, a); break;
+        case 8: KVD_LAUNCH((combine_kernel<T, 8>), grid, dim3(THREADS), 0, on, a); break;
+        default: KVD_LAUNCH((combine_kernel<T, MAX_UNROLL>), grid, dim3(THREADS), 0, on, a); break;
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_combine(const CombineArgs& args, bool bf16, hipStream_t stream) {
+hipError_t launch_combine(const CombineArgs& args, bool bf16, const Launch& on) {
     // split groups per row: enough that MAX_UNROLL loads per thread cover
     // the splits in one round, and a row no wider than a workgroup; then
     // the smallest power-of-two unroll that covers them
@@ -248,7 +248,7 @@ hipError_t launch_combine(const CombineArgs& args, bool bf16, hipStream_t stream
     const int rows = a.B * a.Hq;
     const int per_block = THREADS / (nvec * G);
     dim3 grid((rows + per_block - 1) / per_block + (a.order != nullptr ? 1 : 0));
-    return bf16 ? launch_t<uint16_t>(a, U, grid, stream) : launch_t<float>(a, U, grid, stream);
+    return bf16 ? launch_t<uint16_t>(a, U, grid, on) : launch_t<float>(a, U, grid, on);
 }
 
 }  // namespace kvd

@@ -2,6 +2,7 @@
 // library (internal; the public ABI is include/kvdecode.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -269,6 +270,23 @@ inline unsigned lds_grid_blocks(int S, int groups, int Hkv, int B) {
     return (unsigned)(((long long)B * Hkv + 7) / 8 * 8 * S * groups);
 }
 
+// Where a launcher puts its kernel: the stream and, optionally, events that
+// the dispatch itself stamps with the kernel's start and end times (HIP's
+// extended launch).  A timed launch then adds no command to the stream, and
+// the events bracket the kernel alone, as a kernel trace does.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start, stop;
+    Launch(hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) : stream(s), start(t0), stop(t1) {}
+};
+#define KVD_LAUNCH(kernel, grid, block, shmem, on, ...)                                                        \
+    do {                                                                                                     \
+        if ((on).start || (on).stop)                                                                         \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, (on).stream, (on).start, (on).stop, 0u, __VA_ARGS__); \
+        else                                                                                                 \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, (on).stream, __VA_ARGS__);                        \
+    } while (0)
+
 // Each launcher returns the hipError_t of its launch.
 // Append T_q >= 1 new rows per (sequence, KV head) at slots lengths[b] ..
 // lengths[b] + T_q - 1 (k_new/v_new [B, Hkv, T_q, D]); a sequence they do
@@ -276,10 +294,10 @@ inline unsigned lds_grid_blocks(int S, int groups, int Hkv, int B) {
 // rows appended per sequence.
 hipError_t launch_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                          const KvLayout& kv, int32_t* lengths, int* err, int* n_new, int B, int Hkv,
-                         int D, int T_cap, int T_q, int elem_bytes, hipStream_t stream);
-hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream);
-hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream);
+                         int D, int T_cap, int T_q, int elem_bytes, const Launch& on);
+hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, const Launch& on);
+hipError_t launch_partial_mfma(const PartialArgs& a, const Launch& on);
+hipError_t launch_partial_lds(const PartialArgs& a, const Launch& on);
 
 // Configurations of the LDS-staged kernel: ring depth (stages of K and V of
 // 32 tokens, 128*D bytes each) and how many of the split's tiles the V loads
@@ -307,7 +325,7 @@ inline int lds_groups_per_cu(int D, int which) {
     const int g = LDS_BYTES_PER_CU / (lds_config(D, which).stages * 128 * D);
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
-hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, bool bf16, const Launch& on);
 
 // fp8 (OCP E4M3 codes with a power-of-two exponent per row) cache.
 // Ring depth of the fp8 LDS kernel; a stage holds K and V codes of 32
@@ -317,7 +335,7 @@ inline int lds_fp8_groups_per_cu(int D) {
     const int g = LDS_BYTES_PER_CU / (lds_fp8_stages(D) * (64 * D + 1024));
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
-hipError_t launch_partial_lds_fp8(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_partial_lds_fp8(const PartialArgs& a, const Launch& on);
 
 // fp8 cache, kernel in which each wave streams its own tiles for all rows of
 // a group (kvd_partial_wave_fp8.hip): 16-row blocks per group (each wave
@@ -336,7 +354,7 @@ inline int wave_fp8_groups_per_cu(int D) {
     const int g = LDS_BYTES_PER_CU / (4 * wave_fp8_stages(D) * (64 * D + 1024));
     return g < 1 ? 1 : (g > 8 ? 8 : g);
 }
-hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_partial_wave_fp8(const PartialArgs& a, const Launch& on);
 // fp8 kernel for large query groups in which the four waves split every
 // 64-token tile by tokens for the scores and by value columns for the
 // output, exchanging the weights through LDS (kvd_partial_xchg.hip).  A
@@ -369,7 +387,7 @@ inline int xchg_groups_per_cu(int D, int rows) {
     const int g = LDS_BYTES_PER_CU / xchg_lds_bytes(D, xchg_shape(D, rows).row_blocks);
     return g < 1 ? 1 : (g > 2 ? 2 : g);
 }
-hipError_t launch_partial_xchg(const PartialArgs& a, hipStream_t stream);
+hipError_t launch_partial_xchg(const PartialArgs& a, const Launch& on);
 // Quantize T_q >= 1 new bf16 K/V rows per (sequence, KV head)
 // (k_new/v_new [B, Hkv, T_q, D]) into slots lengths[b] .. lengths[b] + T_q - 1
 // (contiguous or paged, the exponent at the row's index) and advance
@@ -377,7 +395,7 @@ hipError_t launch_partial_xchg(const PartialArgs& a, hipStream_t stream);
 // (may be null) receives the rows appended per sequence.
 hipError_t launch_append_fp8(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                              int8_t* k_exp, int8_t* v_exp, const KvLayout& kv, int32_t* lengths, int* err,
-                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, hipStream_t stream);
+                             int* n_new, int B, int Hkv, int D, int T_cap, int T_q, const Launch& on);
 
 
 // Waves per work unit of the MFMA partial pass for group size M.

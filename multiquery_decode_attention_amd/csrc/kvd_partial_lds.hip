@@ -446,38 +446,38 @@ __global__ __launch_bounds__(256) void partial_lds_kernel(PartialArgs a, int hea
 }
 
 template <int D, int NS, int VL>
-hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_d(const PartialArgs& a, const Launch& on) {
     const int groups = (a.M + 63) / 64;
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
     if (groups == 1) {
         if (a.kv.block_table)
-            hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, true, false>), grid, block, 0, stream, a, 1);
+            KVD_LAUNCH((partial_lds_kernel<D, NS, VL, true, false>), grid, block, 0, on, a, 1);
         else
-            hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, false, false>), grid, block, 0, stream, a, 1);
+            KVD_LAUNCH((partial_lds_kernel<D, NS, VL, false, false>), grid, block, 0, on, a, 1);
     } else {
         if (a.kv.block_table)
-            hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, true, true>), grid, block, 0, stream, a, groups);
+            KVD_LAUNCH((partial_lds_kernel<D, NS, VL, true, true>), grid, block, 0, on, a, groups);
         else
-            hipLaunchKernelGGL((partial_lds_kernel<D, NS, VL, false, true>), grid, block, 0, stream, a, groups);
+            KVD_LAUNCH((partial_lds_kernel<D, NS, VL, false, true>), grid, block, 0, on, a, groups);
     }
     return hipGetLastError();
 }
 
 template <int D, int WHICH>
-hipError_t launch_cfg(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_cfg(const PartialArgs& a, const Launch& on) {
     constexpr LdsConfig c = lds_config(D, WHICH);
-    return launch_d<D, c.stages, c.v_lag>(a, stream);
+    return launch_d<D, c.stages, c.v_lag>(a, on);
 }
 
 }  // namespace
 
-hipError_t launch_partial_lds(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_partial_lds(const PartialArgs& a, const Launch& on) {
     switch (a.D) {
-        case 64: return launch_cfg<64, LDS_SHORT>(a, stream);
-        case 128: return launch_cfg<128, LDS_SHORT>(a, stream);
+        case 64: return launch_cfg<64, LDS_SHORT>(a, on);
+        case 128: return launch_cfg<128, LDS_SHORT>(a, on);
         case 256:
-            return a.lds_config == LDS_LONG ? launch_cfg<256, LDS_LONG>(a, stream)
-                                            : launch_cfg<256, LDS_SHORT>(a, stream);
+            return a.lds_config == LDS_LONG ? launch_cfg<256, LDS_LONG>(a, on)
+                                            : launch_cfg<256, LDS_SHORT>(a, on);
         default: return hipErrorInvalidValue;
     }
 }

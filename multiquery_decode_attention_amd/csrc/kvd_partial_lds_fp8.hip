@@ -322,25 +322,25 @@ __global__ __launch_bounds__(256) void partial_lds_fp8_kernel(PartialArgs a, int
 }
 
 template <int D>
-hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_d(const PartialArgs& a, const Launch& on) {
     const int groups = (a.M + 63) / 64;
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B));
     if (a.kv.block_table)
-        hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D), true>), grid, dim3(256), 0, stream, a,
+        KVD_LAUNCH((partial_lds_fp8_kernel<D, lds_fp8_stages(D), true>), grid, dim3(256), 0, on, a,
                            groups);
     else
-        hipLaunchKernelGGL((partial_lds_fp8_kernel<D, lds_fp8_stages(D), false>), grid, dim3(256), 0, stream, a,
+        KVD_LAUNCH((partial_lds_fp8_kernel<D, lds_fp8_stages(D), false>), grid, dim3(256), 0, on, a,
                            groups);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_partial_lds_fp8(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_partial_lds_fp8(const PartialArgs& a, const Launch& on) {
     switch (a.D) {
-        case 64: return launch_d<64>(a, stream);
-        case 128: return launch_d<128>(a, stream);
-        case 256: return launch_d<256>(a, stream);
+        case 64: return launch_d<64>(a, on);
+        case 128: return launch_d<128>(a, on);
+        case 256: return launch_d<256>(a, on);
         default: return hipErrorInvalidValue;
     }
 }

@@ -225,27 +225,27 @@ __global__ __launch_bounds__(64 * NW) void partial_mfma_kernel(PartialArgs a, in
 }
 
 template <int D>
-hipError_t launch_d(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_d(const PartialArgs& a, const Launch& on) {
     const int hbs = mfma_head_blocks(a.M);
     const int nw = hbs < 4 ? hbs : 4;
     const int groups = (hbs + nw - 1) / nw;
     dim3 grid((unsigned)a.S * a.B * a.Hkv * groups);
     switch (nw) {
-        case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1>), grid, dim3(64), 0, stream, a, groups); break;
-        case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2>), grid, dim3(128), 0, stream, a, groups); break;
-        case 3: hipLaunchKernelGGL((partial_mfma_kernel<D, 3>), grid, dim3(192), 0, stream, a, groups); break;
-        default: hipLaunchKernelGGL((partial_mfma_kernel<D, 4>), grid, dim3(256), 0, stream, a, groups); break;
+        case 1: KVD_LAUNCH((partial_mfma_kernel<D, 1>), grid, dim3(64), 0, on, a, groups); break;
+        case 2: KVD_LAUNCH((partial_mfma_kernel<D, 2>), grid, dim3(128), 0, on, a, groups); break;
+        case 3: KVD_LAUNCH((partial_mfma_kernel<D, 3>), grid, dim3(192), 0, on, a, groups); break;
+        default: KVD_LAUNCH((partial_mfma_kernel<D, 4>), grid, dim3(256), 0, on, a, groups); break;
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_partial_mfma(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_partial_mfma(const PartialArgs& a, const Launch& on) {
     switch (a.D) {
-        case 64: return launch_d<64>(a, stream);
-        case 128: return launch_d<128>(a, stream);
-        case 256: return launch_d<256>(a, stream);
+        case 64: return launch_d<64>(a, on);
+        case 128: return launch_d<128>(a, on);
+        case 256: return launch_d<256>(a, on);
         default: return hipErrorInvalidValue;
     }
 }

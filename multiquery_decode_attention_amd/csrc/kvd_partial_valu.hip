@@ -229,12 +229,12 @@ __global__ __launch_bounds__(64 * VALU_WAVES) void partial_valu_kernel(PartialAr
 }
 
 template <typename T, bool PAGED>
-hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_typed(const PartialArgs& a, const Launch& on) {
     dim3 grid((unsigned)a.S * a.B * a.Hq), block(64 * VALU_WAVES);
     switch (a.D) {
-        case 64: hipLaunchKernelGGL((partial_valu_kernel<T, 64, PAGED>), grid, block, 0, stream, a); break;
-        case 128: hipLaunchKernelGGL((partial_valu_kernel<T, 128, PAGED>), grid, block, 0, stream, a); break;
-        case 256: hipLaunchKernelGGL((partial_valu_kernel<T, 256, PAGED>), grid, block, 0, stream, a); break;
+        case 64: KVD_LAUNCH((partial_valu_kernel<T, 64, PAGED>), grid, block, 0, on, a); break;
+        case 128: KVD_LAUNCH((partial_valu_kernel<T, 128, PAGED>), grid, block, 0, on, a); break;
+        case 256: KVD_LAUNCH((partial_valu_kernel<T, 256, PAGED>), grid, block, 0, on, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -242,10 +242,10 @@ hipError_t launch_typed(const PartialArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, hipStream_t stream) {
+hipError_t launch_partial_valu(const PartialArgs& a, bool bf16, const Launch& on) {
     if (a.kv.block_table)
-        return bf16 ? launch_typed<uint16_t, true>(a, stream) : launch_typed<float, true>(a, stream);
-    return bf16 ? launch_typed<uint16_t, false>(a, stream) : launch_typed<float, false>(a, stream);
+        return bf16 ? launch_typed<uint16_t, true>(a, on) : launch_typed<float, true>(a, on);
+    return bf16 ? launch_typed<uint16_t, false>(a, on) : launch_typed<float, false>(a, on);
 }
 
 }  // namespace kvd

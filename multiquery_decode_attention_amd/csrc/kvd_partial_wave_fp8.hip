@@ -470,20 +470,20 @@ __global__ __launch_bounds__(256) void partial_wave_fp8_kernel(PartialArgs a, in
 }
 
 template <int D, int RB, int NSW>
-hipError_t launch_rb(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_rb(const PartialArgs& a, const Launch& on) {
     const int groups = (a.M + 16 * RB - 1) / (16 * RB);
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
     const bool paged = a.kv.block_table != nullptr;
     if (groups == 1) {
         if (paged)
-            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false, true>), grid, block, 0, stream, a, 1);
+            KVD_LAUNCH((partial_wave_fp8_kernel<D, RB, NSW, false, true>), grid, block, 0, on, a, 1);
         else
-            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, false, false>), grid, block, 0, stream, a, 1);
+            KVD_LAUNCH((partial_wave_fp8_kernel<D, RB, NSW, false, false>), grid, block, 0, on, a, 1);
     } else {
         if (paged)
-            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true, true>), grid, block, 0, stream, a, groups);
+            KVD_LAUNCH((partial_wave_fp8_kernel<D, RB, NSW, true, true>), grid, block, 0, on, a, groups);
         else
-            hipLaunchKernelGGL((partial_wave_fp8_kernel<D, RB, NSW, true, false>), grid, block, 0, stream, a,
+            KVD_LAUNCH((partial_wave_fp8_kernel<D, RB, NSW, true, false>), grid, block, 0, on, a,
                                groups);
     }
     return hipGetLastError();
@@ -491,14 +491,14 @@ hipError_t launch_rb(const PartialArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_partial_wave_fp8(const PartialArgs& a, hipStream_t stream) {
-    if (a.D == 256) return launch_rb<256, 1, wave_fp8_stages(256)>(a, stream);
+hipError_t launch_partial_wave_fp8(const PartialArgs& a, const Launch& on) {
+    if (a.D == 256) return launch_rb<256, 1, wave_fp8_stages(256)>(a, on);
     if (a.D == 128) {
         constexpr int NSW = wave_fp8_stages(128);
         switch (wave_fp8_row_blocks(128, a.M)) {
-            case 1: return launch_rb<128, 1, NSW>(a, stream);
-            case 2: return launch_rb<128, 2, NSW>(a, stream);
-            default: return launch_rb<128, 3, NSW>(a, stream);
+            case 1: return launch_rb<128, 1, NSW>(a, on);
+            case 2: return launch_rb<128, 2, NSW>(a, on);
+            default: return launch_rb<128, 3, NSW>(a, on);
         }
     }
     return hipErrorInvalidValue;

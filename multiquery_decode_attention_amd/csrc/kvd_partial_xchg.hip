@@ -494,46 +494,46 @@ __global__ __launch_bounds__(256, 2) void partial_xchg_fp8_kernel(PartialArgs a,
 }
 
 template <int D, int R, int NS, bool GROUPED, bool PAGED>
-void launch_one(const PartialArgs& a, int groups, hipStream_t stream) {
+void launch_one(const PartialArgs& a, int groups, const Launch& on) {
     const dim3 grid(lds_grid_blocks(a.S, groups, a.Hkv, a.B)), block(256);
-    hipLaunchKernelGGL((partial_xchg_fp8_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, stream, a, groups);
+    KVD_LAUNCH((partial_xchg_fp8_kernel<D, R, NS, GROUPED, PAGED>), grid, block, 0, on, a, groups);
 }
 
 template <int D, int R>
-hipError_t launch_r(const PartialArgs& a, int groups, hipStream_t stream) {
+hipError_t launch_r(const PartialArgs& a, int groups, const Launch& on) {
     constexpr int NS = xchg_slots(D);
     const bool paged = a.kv.block_table != nullptr;
     if (groups == 1) {
         if (paged)
-            launch_one<D, R, NS, false, true>(a, 1, stream);
+            launch_one<D, R, NS, false, true>(a, 1, on);
         else
-            launch_one<D, R, NS, false, false>(a, 1, stream);
+            launch_one<D, R, NS, false, false>(a, 1, on);
     } else {
         if (paged)
-            launch_one<D, R, NS, true, true>(a, groups, stream);
+            launch_one<D, R, NS, true, true>(a, groups, on);
         else
-            launch_one<D, R, NS, true, false>(a, groups, stream);
+            launch_one<D, R, NS, true, false>(a, groups, on);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_partial_xchg(const PartialArgs& a, hipStream_t stream) {
+hipError_t launch_partial_xchg(const PartialArgs& a, const Launch& on) {
     const XchgShape x = xchg_shape(a.D, a.M);
     if (a.D == 256) {
         switch (x.row_blocks) {
-            case 1: return launch_r<256, 1>(a, x.groups, stream);
-            case 2: return launch_r<256, 2>(a, x.groups, stream);
-            default: return launch_r<256, 3>(a, x.groups, stream);
+            case 1: return launch_r<256, 1>(a, x.groups, on);
+            case 2: return launch_r<256, 2>(a, x.groups, on);
+            default: return launch_r<256, 3>(a, x.groups, on);
         }
     }
     if (a.D == 128) {
         switch (x.row_blocks) {
-            case 1: return launch_r<128, 1>(a, x.groups, stream);
-            case 2: return launch_r<128, 2>(a, x.groups, stream);
-            case 3: return launch_r<128, 3>(a, x.groups, stream);
-            default: return launch_r<128, 4>(a, x.groups, stream);
+            case 1: return launch_r<128, 1>(a, x.groups, on);
+            case 2: return launch_r<128, 2>(a, x.groups, on);
+            case 3: return launch_r<128, 3>(a, x.groups, on);
+            default: return launch_r<128, 4>(a, x.groups, on);
         }
     }
     return hipErrorInvalidValue;

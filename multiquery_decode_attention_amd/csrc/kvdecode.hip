@@ -43,8 +43,13 @@ struct kvdecode_s {
     // Event timing.
     int timing_cap = 0;
     int timing_what = 0;                // KVD_TIME_* bits
-    std::vector<hipEvent_t> ev_attend;  // 3 per timed attend
+    // Events stamped by the timed launches themselves: per timed attend the
+    // partial pass's start and end, then the combine's; per timed append
+    // the append kernel's.  comb_timed: whether attend i timed a combine
+    // (a one-split pass launches none).
+    std::vector<hipEvent_t> ev_attend;  // 4 per timed attend
     std::vector<hipEvent_t> ev_append;  // 2 per timed append
+    std::vector<char> comb_timed;
     int n_attend = 0, n_append = 0;
 };
 
@@ -345,13 +350,15 @@ void free_events(kvdecode_s* h) {
     for (hipEvent_t ev : h->ev_append) (void)hipEventDestroy(ev);
     h->ev_attend.clear();
     h->ev_append.clear();
+    h->comb_timed.clear();
     h->n_attend = h->n_append = 0;
 }
 
 int32_t ensure_events(kvdecode_s* h) {
     if (h->timing_cap <= 0 || !h->ev_attend.empty()) return KVD_OK;
-    h->ev_attend.resize(3 * (size_t)h->timing_cap, nullptr);
+    h->ev_attend.resize(4 * (size_t)h->timing_cap, nullptr);
     h->ev_append.resize(2 * (size_t)h->timing_cap, nullptr);
+    h->comb_timed.assign((size_t)h->timing_cap, 0);
     for (auto* vec : {&h->ev_attend, &h->ev_append}) {
         for (hipEvent_t& ev : *vec) {
             // timing only: no system-scope fence (cache writeback) at record
@@ -396,19 +403,17 @@ int32_t launch_append_timed(kvdecode_s* h, const Workspace& ws, const void* k_ne
                             hipStream_t st, int T_q = 1, bool may_time = true) {
     const bool timed = may_time && (h->timing_what & KVD_TIME_APPEND) && h->timing_cap > 0 &&
                        h->n_append < h->timing_cap;
-    if (timed && hipEventRecord(h->ev_append[2 * h->n_append], st) != hipSuccess) return KVD_EHIP;
+    const kvd::Launch on = timed ? kvd::Launch(st, h->ev_append[2 * h->n_append], h->ev_append[2 * h->n_append + 1])
+                                 : kvd::Launch(st);
     hipError_t e =
         is_fp8(h) ? kvd::launch_append_fp8(k_new, v_new, h->d.k_cache, h->d.v_cache, h->k_exp, h->v_exp, h->kv,
                                            h->d.lengths, ws.err, ws.n_new, h->d.batch, h->d.num_kv_heads,
-                                           h->d.head_dim, h->d.capacity, T_q, st)
+                                           h->d.head_dim, h->d.capacity, T_q, on)
                   : kvd::launch_append(k_new, v_new, h->d.k_cache, h->d.v_cache, h->kv, h->d.lengths, ws.err,
                                        ws.n_new, h->d.batch, h->d.num_kv_heads, h->d.head_dim, h->d.capacity,
-                                       T_q, h->elem, st);
+                                       T_q, h->elem, on);
     if (e != hipSuccess) return KVD_EHIP;
-    if (timed) {
-        if (hipEventRecord(h->ev_append[2 * h->n_append + 1], st) != hipSuccess) return KVD_EHIP;
-        ++h->n_append;
-    }
+    if (timed) ++h->n_append;
     return KVD_OK;
 }
 
@@ -501,31 +506,28 @@ int32_t launch_step(kvdecode_s* h, const Plan& p, const Workspace& ws, const voi
     c.T_cap = a.T_cap;
     c.tile = p.tile;
     c.S = p.splits;
-    // Each recorded event is one more command-processor round trip on the
-    // stream (about 2 us), so only the brackets asked for are recorded:
-    // ev[0] before the partial pass, ev[1] between the two launches, ev[2]
-    // after the combine.
+    // Timed launches carry their events (the dispatch stamps them), so a
+    // bracket asked for adds no command to the stream and measures the
+    // kernel alone: ev[0], ev[1] the partial pass, ev[2], ev[3] the combine.
     const int what = h->timing_what;
     const bool timed = may_time && (what & (KVD_TIME_PARTIAL | KVD_TIME_COMBINE)) && h->timing_cap > 0 &&
                        h->n_attend < h->timing_cap;
-    hipEvent_t* ev = timed ? &h->ev_attend[3 * h->n_attend] : nullptr;
-    if (timed && (what & KVD_TIME_PARTIAL) && hipEventRecord(ev[0], st) != hipSuccess) return KVD_EHIP;
-    hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, st)
-                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg(a, st)
-                   : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, st)
-                   : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, st)
-                   : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, st)
-                                                   : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, st);
+    hipEvent_t* ev = timed ? &h->ev_attend[4 * h->n_attend] : nullptr;
+    const kvd::Launch on_part = timed && (what & KVD_TIME_PARTIAL) ? kvd::Launch(st, ev[0], ev[1]) : kvd::Launch(st);
+    const bool comb_timed = timed && (what & KVD_TIME_COMBINE) && !one_pass;
+    const kvd::Launch on_comb = comb_timed ? kvd::Launch(st, ev[2], ev[3]) : kvd::Launch(st);
+    hipError_t e = p.variant == KVD_VARIANT_WAVE   ? kvd::launch_partial_wave_fp8(a, on_part)
+                   : p.variant == KVD_VARIANT_XCHG ? kvd::launch_partial_xchg(a, on_part)
+                   : is_fp8(h)                     ? kvd::launch_partial_lds_fp8(a, on_part)
+                   : p.variant == KVD_VARIANT_LDS  ? kvd::launch_partial_lds(a, on_part)
+                   : p.variant == KVD_VARIANT_MFMA ? kvd::launch_partial_mfma(a, on_part)
+                                                   : kvd::launch_partial_valu(a, h->d.dtype == KVD_BF16, on_part);
     if (e != hipSuccess) return KVD_EHIP;
-    if (timed && hipEventRecord(ev[1], st) != hipSuccess) return KVD_EHIP;
     if (!one_pass) {
-        e = kvd::launch_combine(c, h->d.dtype != KVD_F32, st);  // fp8 caches give bf16 outputs
+        e = kvd::launch_combine(c, h->d.dtype != KVD_F32, on_comb);  // fp8 caches give bf16 outputs
         if (e != hipSuccess) return KVD_EHIP;
     }
-    if (timed) {
-        if ((what & KVD_TIME_COMBINE) && hipEventRecord(ev[2], st) != hipSuccess) return KVD_EHIP;
-        ++h->n_attend;
-    }
+    if (timed) h->comb_timed[h->n_attend++] = comb_timed;
     return KVD_OK;
 }
 
@@ -891,11 +893,16 @@ int32_t kvdecode_timing_read(kvdecode_t h, double* partial_ms, double* combine_m
     double tp = 0, tc = 0, ta = 0;
     const int what = h->timing_what;
     for (int i = 0; i < h->n_attend; ++i) {
-        hipEvent_t* ev = &h->ev_attend[3 * i];
+        hipEvent_t* ev = &h->ev_attend[4 * i];
         float a = 0, b = 0;
-        if (hipEventSynchronize(ev[(what & KVD_TIME_COMBINE) ? 2 : 1]) != hipSuccess) return KVD_EHIP;
-        if ((what & KVD_TIME_PARTIAL) && hipEventElapsedTime(&a, ev[0], ev[1]) != hipSuccess) return KVD_EHIP;
-        if ((what & KVD_TIME_COMBINE) && hipEventElapsedTime(&b, ev[1], ev[2]) != hipSuccess) return KVD_EHIP;
+        if (what & KVD_TIME_PARTIAL) {
+            if (hipEventSynchronize(ev[1]) != hipSuccess || hipEventElapsedTime(&a, ev[0], ev[1]) != hipSuccess)
+                return KVD_EHIP;
+        }
+        if (h->comb_timed[i]) {
+            if (hipEventSynchronize(ev[3]) != hipSuccess || hipEventElapsedTime(&b, ev[2], ev[3]) != hipSuccess)
+                return KVD_EHIP;
+        }
         tp += a;
         tc += b;
     }

@@ -293,10 +293,13 @@ def test_unified_max_any_bound_same_result(name, B, phi):
     check_case(case, w.Hq, f"{name} unified max {phi}", fused=True, unified_max=phi)
 
 
+@pytest.mark.parametrize("splits", [4, 1])
 @pytest.mark.parametrize("what", ["all", "partial"])
-def test_timing_brackets(what):
+def test_timing_brackets(what, splits):
     """Event timing records only the brackets asked for and leaves results
-    unchanged: timed steps equal untimed ones bit for bit."""
+    unchanged: timed steps equal untimed ones bit for bit.  The timed
+    launches stamp their own events: a one-split pass launches no combine,
+    so its combine bracket is exactly zero."""
     case = inputs.make_case(2, 16, 2, 128, 300, [100, 250], "bf16", seed=41)
     dev = torch.device("cuda")
     mask = kvd.KVD_TIME_ALL if what == "all" else kvd.KVD_TIME_PARTIAL
@@ -306,6 +309,8 @@ def test_timing_brackets(what):
         L = case.lengths0.to(dev, torch.int32, copy=True)
         cache = kvd.KVCache(kc, vc, L, 16)
         try:
+            cache.set_variant(VARIANTS["lds"])
+            cache.set_num_splits(splits)
             if timed:
                 kvd.kvdecode_timing_enable(cache.handle, 3, mask)
             kn, vn, q = (t.to(dev) for t in (case.k_new, case.v_new, case.q))
@@ -323,7 +328,7 @@ def test_timing_brackets(what):
     t = timings[0]
     assert t["n_attend"] == 2 and t["partial_ms"] > 0
     if what == "all":
-        assert t["combine_ms"] > 0 and t["append_ms"] > 0 and t["n_append"] == 1
+        assert (t["combine_ms"] > 0) == (splits > 1) and t["append_ms"] > 0 and t["n_append"] == 1
     else:
         assert t["combine_ms"] == 0 and t["append_ms"] == 0 and t["n_append"] == 0
 
