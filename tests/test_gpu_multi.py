@@ -123,6 +123,16 @@ def test_multi_token_empty_splits(variant, splits):
     check_multi(case, 16, f"multi edges {variant} S={splits}", variant=variant, splits=splits)
 
 
+@pytest.mark.parametrize("splits", [20, 40])
+def test_multi_token_many_splits_d256(splits):
+    """d = 256 with more than 16 splits (several split groups per row in the
+    combine): early queries whose last tokens end before later splits
+    (empty splits, log-sum-exp -inf) must weigh those splits 0."""
+    L0 = [31, 700, 95, 1, 1200]
+    case = inputs.make_multi_case(len(L0), 48, 1, 256, 1280, L0, 4, "bf16", seed=60 + splits)
+    check_multi(case, 48, f"multi d256 S={splits}", variant="lds", splits=splits)
+
+
 def test_multi_token_fp32_and_paged():
     case = inputs.make_multi_case(2, 8, 1, 64, 256, [100, 3], 5, "f32", seed=61)
     check_multi(case, 8, "multi fp32 valu")

@@ -77,6 +77,18 @@ def test_split_invariance(name, B, splits):
     check_case(case, w.Hq, f"{name}/splits={splits}", splits=splits)
 
 
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("splits", [17, 24, 33, 50, 64])
+def test_many_splits_d256(splits, fused):
+    """d = 256 bf16 rows over 17..64 splits (the combine's split groups meet
+    in LDS): ragged lengths with a sequence of one token, one shorter than
+    the split count in tiles, and a full one, every row against the
+    oracle."""
+    lengths = [1, 20 * 32 + 5, 2048, 1500]
+    case = inputs.make_case(len(lengths), 48, 1, 256, 2048, lengths, "bf16", seed=300 + splits)
+    check_case(case, 48, f"many splits {splits} fused={fused}", splits=splits, fused=fused)
+
+
 VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}
 
 
