@@ -89,6 +89,38 @@ def test_many_splits_d256(splits, fused):
     check_case(case, 48, f"many splits {splits} fused={fused}", splits=splits, fused=fused)
 
 
+@pytest.mark.parametrize("variant", ["valu"])
+def test_bf16_cache_past_4_gib(variant):
+    """test_cache_past_4_gib on the vector-ALU kernel: a bf16 MHA cache of
+    5.4 GB per tensor (64 sequences, 40 KV heads, 8192 tokens, d = 128),
+    whose later sequences' byte offsets pass 2^32 in the fused append, the
+    partial pass and the combine; the first, a middle and the last sequence
+    against the oracle on their own slices (the append bit for bit)."""
+    B, H, T, D = 64, 40, 8192, 128
+    L_att = torch.full((B,), T, dtype=torch.int32)
+    L_att[1::2] = T - 100
+    case = inputs.make_case(B, H, H, D, T, L_att, "bf16", seed=4323, device="cuda")
+    assert case.k_cache.numel() * 2 > 2 ** 32
+    picks = [0, B // 2, B - 1]
+    sl = lambda t, b: inputs.host_array(t[b:b + 1])
+    before = {b: (sl(case.k_cache, b), sl(case.v_cache, b)) for b in picks}
+    say(f"bf16 cache past 4 GiB ({variant}): B={B} H={H} T={T} D={D}")
+    out, kc, vc, L, status, plan = gpu_step(case, H, variant=VARIANTS[variant], fused=True)
+    say(f"bf16 cache past 4 GiB ({variant}): gpu done, plan={plan}, status={status}")
+    assert status == kvd.KVD_OK
+    L0 = case.lengths0.cpu().numpy().astype(np.int32)
+    assert np.array_equal(L.cpu().numpy(), L0 + 1)
+    for b in picks:
+        k2, v2, L2, _ = oracle.append(*before[b], L0[b:b + 1], sl(case.k_new, b), sl(case.v_new, b))
+        assert np.array_equal(sl(kc, b), k2) and np.array_equal(sl(vc, b), v2), b
+        ref = oracle.decode_attention(sl(case.q, b), k2, v2, L2, case.scale, oracle.BF16)
+        err = rel_err_rows(to_f64(out[b:b + 1]), ref)
+        say(f"bf16 cache past 4 GiB ({variant}): sequence {b} max row-relative error {err:.3e}")
+        assert err <= TOL_BF16, err
+    del case, out, kc, vc
+    torch.cuda.empty_cache()
+
+
 VARIANTS = {"auto": kvd.KVD_VARIANT_AUTO, "valu": kvd.KVD_VARIANT_VALU, "mfma": kvd.KVD_VARIANT_MFMA, "lds": kvd.KVD_VARIANT_LDS}
 
 
