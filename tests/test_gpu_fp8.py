@@ -570,6 +570,34 @@ def test_fp8_multi_token_paged_and_overflow():
     fp8_multi_check(3, 16, 2, 128, 128, [126, 124, 10], 4, "overflow", expect=kvd.KVD_ECAPACITY)
 
 
+def test_fp8_maximum_capacity():
+    """The largest fp8 cache the header accepts, 2^24 tokens (one sequence,
+    8 heads, d = 64, 1 GiB of codes per tensor): one fused step appends
+    slot 2^24 - 1 and attends every token; codes, exponents and lengths
+    bit for bit, all heads against the oracle."""
+    T = 1 << 24
+    case = inputs.make_fp8_case(1, 8, 1, 64, T, torch.tensor([T], dtype=torch.int32), seed=2424, device="cuda")
+    say("fp8 maximum capacity: B=1 Hq=8 Hkv=1 D=64 T=2^24")
+    out, kc, ke, vc, ve, L, status, plan = fp8_step(case, 8)
+    say(f"fp8 maximum capacity: gpu done, plan={plan}, status={status}")
+    assert status == kvd.KVD_OK
+    host = lambda t: t.cpu().numpy()
+    f32 = lambda t: t.float().cpu().numpy()
+    L0 = case.lengths0.cpu().numpy().astype(np.int32)
+    kc2, ke2, vc2, ve2, L2, _ = oracle.append_fp8(host(case.k_codes), host(case.k_exp), host(case.v_codes),
+                                                  host(case.v_exp), L0, f32(case.k_new), f32(case.v_new))
+    assert np.array_equal(L.cpu().numpy(), L2)
+    for got, want, what in ((kc, kc2, "K codes"), (ke, ke2, "K exponents"), (vc, vc2, "V codes"),
+                            (ve, ve2, "V exponents")):
+        assert np.array_equal(host(got), want), what
+    del kc, vc
+    ref = oracle.decode_attention_fp8(f32(case.q), kc2, ke2, vc2, ve2, L2, case.scale)
+    err = rel_err_rows(to_f64(out), ref)
+    say(f"fp8 maximum capacity: max row-relative error {err:.3e}")
+    assert err <= TOL_BF16, err
+    torch.cuda.empty_cache()
+
+
 def test_fp8_cache_past_4_gib():
     """An fp8 MHA cache of 5.4 GB of codes per tensor (128 sequences, 40 KV
     heads, 8192 tokens, d = 128): code offsets of the later sequences pass

@@ -153,6 +153,20 @@ def test_shapes_and_ragged_lengths(dtype, variant, Hq, Hkv, D):
                    variant=VARIANTS[variant], splits=splits)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_maximum_capacity(dtype):
+    """The largest cache the header accepts, 2^24 tokens (one sequence,
+    d = 64; 2 GiB per tensor in bf16, 4 GiB in fp32): the fused step
+    appends slot 2^24 - 1 and attends every token; all 8 heads against the
+    oracle, the append bit for bit on the whole cache."""
+    T = 1 << 24
+    case = inputs.make_case(1, 8, 1, 64, T, [T], dtype, seed=24, device="cuda")
+    _, _, plan = check_case(case, 8, f"maximum capacity {dtype}", fused=True)
+    assert plan["num_splits"] * plan["split_tokens"] >= T
+    del case
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("splits", [None, 1])
 def test_empty_sequences_and_poisoned_tails(splits):
     """len 0 gives a zero row; slots past the length hold NaN/Inf and must
