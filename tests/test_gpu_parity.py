@@ -153,6 +153,22 @@ def test_shapes_and_ragged_lengths(dtype, variant, Hq, Hkv, D):
                    variant=VARIANTS[variant], splits=splits)
 
 
+@pytest.mark.parametrize("splits", [0, 2])
+@pytest.mark.parametrize("variant", ["lds", "valu"])
+def test_maximum_batch(variant, splits):
+    """The largest batch the header accepts, 65535 sequences (8 heads, one
+    KV head, d = 64, capacity 128, ragged lengths 1..128 after the append):
+    the automatic one-split plan (per-sequence arrival counters for every
+    sequence) and two splits (the combine over all of them, past its
+    2048-sequence sort).  Fused step; every row against the oracle, the
+    append bit for bit."""
+    B, T = 65535, 128
+    lengths = torch.randint(1, T + 1, (B,), generator=torch.Generator().manual_seed(65535), dtype=torch.int32)
+    case = inputs.make_case(B, 8, 1, 64, T, lengths, "bf16", seed=65535)
+    check_case(case, 8, f"maximum batch {variant} splits={splits}", fused=True,
+               variant=VARIANTS[variant], splits=splits)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_maximum_capacity(dtype):
     """The largest cache the header accepts, 2^24 tokens (one sequence,
