@@ -104,6 +104,15 @@ def test_paged_long_context_long_splits():
     check_paged(case, w.Hq, 512, "longctx/paged512")
 
 
+@pytest.mark.parametrize("fused", [True, False])
+def test_paged_largest_pages(fused):
+    """Pages of 65536 tokens, the largest size the header accepts (two
+    blocks per sequence, shuffled; the second sequence ends inside its
+    second page)."""
+    case = inputs.make_case(2, 8, 1, 64, 2 * 65536, [2 * 65536, 70001], "bf16", seed=65536)
+    check_paged(case, 8, 65536, "paged65536", fused=fused)
+
+
 def test_paged_ragged_full_size():
     w = inputs.WORKLOADS["ragged_gqa_bf16"]
     case = inputs.make_workload_case(w, device="cpu")
