@@ -273,7 +273,7 @@ def measure(w, args, K, W, keep_first_copy=False) -> dict:
         cache.reserve(tq)  # device workspace allocated now, not inside the timed steps
         copies.append({"case": case, "cache": cache, "out": torch.empty_like(case.q),
                        "len": case.lengths0.cpu().tolist(), "keep": keep})
-    plan = copies[0]["cache"].plan()
+    plan = copies[0]["cache"].plan(tq)  # the plan of a step with tq new tokens
     log(f"plan {plan}")
     torch.cuda.synchronize()
 

@@ -401,6 +401,19 @@ int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits,
                           int32_t* split_tokens);
 
 /*
+ * The plan of a step with n_tokens new tokens per sequence
+ * (kvdecode_append_attend_multi; n_tokens = 1 is kvdecode_get_plan's):
+ * variant, splits per (sequence, KV head) and the most tokens any split
+ * holds when the cache is full.  A step's query rows grow with n_tokens,
+ * so its plan can differ from the one-token plan.  KVD_EINVAL for
+ * n_tokens outside 1..KVD_MAX_NEW_TOKENS, KVD_EUNSUPPORTED when the chosen
+ * kernel takes one token per step (KVD_VARIANT_MFMA with n_tokens > 1).
+ * Makes no device call.  Any output pointer may be NULL.
+ */
+int32_t kvdecode_get_plan_multi(kvdecode_t h, int32_t n_tokens, int32_t* variant, int32_t* num_splits,
+                                int32_t* split_tokens);
+
+/*
  * Kernel timing with HIP events.  `what` picks the brackets: KVD_TIME_PARTIAL
  * the partial-pass kernel of each attend, KVD_TIME_COMBINE its combine
  * kernel (zero for a one-split pass, which launches none), KVD_TIME_APPEND

@@ -28,8 +28,8 @@ __all__ = [
     "kvdecode_append_attend_noalloc", "kvdecode_status", "KVD_MAX_NEW_TOKENS", "KVD_TIME_PARTIAL", "KVD_TIME_COMBINE",
     "KVD_TIME_APPEND", "KVD_TIME_ALL",
     "kvdecode_reserve", "kvdecode_set_num_splits",
-    "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan", "kvdecode_timing_enable",
-    "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
+    "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan", "kvdecode_get_plan_multi",
+    "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror", "KVCache", "library",
     "LIB_PATH",
 ]
 
@@ -51,7 +51,8 @@ EXPORTS = (
     "kvdecode_append_attend", "kvdecode_append_attend_multi", "kvdecode_append_attend_noalloc",
     "kvdecode_status", "kvdecode_reserve",
     "kvdecode_set_num_splits", "kvdecode_set_variant", "kvdecode_set_unified_max", "kvdecode_get_plan",
-    "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy", "kvdecode_strerror",
+    "kvdecode_get_plan_multi", "kvdecode_timing_enable", "kvdecode_timing_read", "kvdecode_destroy",
+    "kvdecode_strerror",
 )
 
 
@@ -123,6 +124,7 @@ def library():
         "kvdecode_set_variant": (I, [P, I]),
         "kvdecode_set_unified_max": (I, [P, I, F]),
         "kvdecode_get_plan": (I, [P, IP, IP, IP]),
+        "kvdecode_get_plan_multi": (I, [P, I, IP, IP, IP]),
         "kvdecode_timing_enable": (I, [P, I, I]),
         "kvdecode_timing_read": (I, [P, D, D, D, IP, IP]),
         "kvdecode_destroy": (I, [P]),
@@ -327,12 +329,23 @@ def kvdecode_set_variant(h: int, variant: int) -> None:
     _check(library().kvdecode_set_variant(h, variant), "kvdecode_set_variant")
 
 
+def _plan_dict(v, s, c) -> dict:
+    return {"variant": {1: "valu", 2: "mfma", 3: "lds", 4: "wave", 5: "xchg"}.get(v.value, str(v.value)),
+            "num_splits": s.value, "split_tokens": c.value}
+
+
 def kvdecode_get_plan(h: int) -> dict:
     v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     _check(library().kvdecode_get_plan(h, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)),
            "kvdecode_get_plan")
-    return {"variant": {1: "valu", 2: "mfma", 3: "lds", 4: "wave", 5: "xchg"}.get(v.value, str(v.value)),
-            "num_splits": s.value, "split_tokens": c.value}
+    return _plan_dict(v, s, c)
+
+
+def kvdecode_get_plan_multi(h: int, n_tokens: int) -> dict:
+    v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(library().kvdecode_get_plan_multi(h, n_tokens, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)),
+           "kvdecode_get_plan_multi")
+    return _plan_dict(v, s, c)
 
 
 def kvdecode_timing_enable(h: int, max_calls: int, what: int = None) -> None:
@@ -466,8 +479,9 @@ class KVCache:
     def set_variant(self, variant: int):
         kvdecode_set_variant(self.handle, variant)
 
-    def plan(self) -> dict:
-        return kvdecode_get_plan(self.handle)
+    def plan(self, n_tokens: int = 1) -> dict:
+        """The plan of a step with n_tokens new tokens per sequence."""
+        return kvdecode_get_plan(self.handle) if n_tokens == 1 else kvdecode_get_plan_multi(self.handle, n_tokens)
 
     def close(self):
         if self.handle is not None:

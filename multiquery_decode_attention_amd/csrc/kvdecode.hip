@@ -870,8 +870,14 @@ int32_t kvdecode_set_variant(kvdecode_t h, int32_t variant) {
 }
 
 int32_t kvdecode_get_plan(kvdecode_t h, int32_t* variant, int32_t* num_splits, int32_t* split_tokens) {
-    if (!is_live(h)) return KVD_EINVAL;
-    const Plan p = make_plan(h);
+    return kvdecode_get_plan_multi(h, 1, variant, num_splits, split_tokens);
+}
+
+int32_t kvdecode_get_plan_multi(kvdecode_t h, int32_t n_tokens, int32_t* variant, int32_t* num_splits,
+                                int32_t* split_tokens) {
+    if (!is_live(h) || n_tokens < 1 || n_tokens > KVD_MAX_NEW_TOKENS) return KVD_EINVAL;
+    const Plan p = make_plan(h, n_tokens);
+    if (n_tokens > 1 && p.variant == KVD_VARIANT_MFMA) return KVD_EUNSUPPORTED;
     if (variant) *variant = p.variant;
     if (num_splits) *num_splits = p.splits;
     if (split_tokens) *split_tokens = p.chunk;

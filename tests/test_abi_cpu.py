@@ -369,3 +369,26 @@ def test_fp8_paged_handle(lib):
     rc, h2 = create_paged(lib, make_paged_desc(dtype=kvd.KVD_FP8_E4M3))
     assert rc == kvd.KVD_EUNSUPPORTED and not h2
     assert lib.kvdecode_create_fp8_paged(None, ctypes.byref(ctypes.c_void_p())) == kvd.KVD_EINVAL
+
+
+def test_plan_of_several_new_tokens(lib):
+    """kvdecode_get_plan_multi: one token reports kvdecode_get_plan's plan;
+    a step's query rows grow with n_tokens, and the plan may change with
+    them (the PaLM-like batch: 4 splits for one token, 2 for four); counts
+    outside 1..KVD_MAX_NEW_TOKENS and the one-token MFMA kernel are refused."""
+    rc, h = create(lib, make_desc(batch=64, num_q_heads=48, num_kv_heads=1, head_dim=256, capacity=2048))
+    assert rc == kvd.KVD_OK
+    try:
+        assert kvd.kvdecode_get_plan_multi(h, 1) == kvd.kvdecode_get_plan(h)
+        assert kvd.kvdecode_get_plan(h)["num_splits"] == 4
+        assert kvd.kvdecode_get_plan_multi(h, 4)["num_splits"] == 2
+        v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        for n in (0, -1, kvd.KVD_MAX_NEW_TOKENS + 1):
+            assert lib.kvdecode_get_plan_multi(h, n, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)) == kvd.KVD_EINVAL
+        assert lib.kvdecode_get_plan_multi(h, 2, None, None, None) == kvd.KVD_OK
+        assert lib.kvdecode_set_variant(h, kvd.KVD_VARIANT_MFMA) == kvd.KVD_OK
+        assert lib.kvdecode_get_plan_multi(h, 1, None, None, None) == kvd.KVD_OK
+        assert lib.kvdecode_get_plan_multi(h, 2, None, None, None) == kvd.KVD_EUNSUPPORTED
+    finally:
+        lib.kvdecode_destroy(h)
+    assert lib.kvdecode_get_plan_multi(None, 1, None, None, None) == kvd.KVD_EINVAL

@@ -38,9 +38,13 @@ def create(lib, B, Hq, Hkv, D, T_cap, dtype):
     return rc, h.value
 
 
-def plan(lib, h):
+def plan(lib, h, T_q=1):
     v, s, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    assert lib.kvdecode_get_plan(h, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)) == kvd.KVD_OK
+    assert lib.kvdecode_get_plan_multi(h, T_q, ctypes.byref(v), ctypes.byref(s), ctypes.byref(c)) == kvd.KVD_OK
+    if T_q == 1:
+        v1, s1, c1 = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        assert lib.kvdecode_get_plan(h, ctypes.byref(v1), ctypes.byref(s1), ctypes.byref(c1)) == kvd.KVD_OK
+        assert (v1.value, s1.value, c1.value) == (v.value, s.value, c.value)
     return VARIANT_NAMES[v.value], s.value, c.value
 
 
@@ -57,17 +61,19 @@ def caches(draw):
 
 
 @SETTINGS
-@given(caches(), st.integers(0, 5000))
-def test_plan_properties(lib, cache, forced):
+@given(caches(), st.integers(0, 5000), st.integers(1, kvd.KVD_MAX_NEW_TOKENS))
+def test_plan_properties(lib, cache, forced, T_q):
+    """Plans of steps with T_q new tokens (the query rows per KV head grow
+    with T_q)."""
     B, Hq, Hkv, D, T_cap, dtype = cache
     rc, h = create(lib, B, Hq, Hkv, D, T_cap, dtype)
     assert rc == kvd.KVD_OK and h
     try:
         assert lib.kvdecode_set_num_splits(h, forced) == kvd.KVD_OK
-        variant, S, C = plan(lib, h)
-        assert plan(lib, h) == (variant, S, C)  # cached, stable
+        variant, S, C = plan(lib, h, T_q)
+        assert plan(lib, h, T_q) == (variant, S, C)  # cached, stable
         # the automatic kernel choice the header documents
-        M = Hq // Hkv
+        rows = Hq // Hkv * T_q
         if dtype == kvd.KVD_F32:
             assert variant == "valu"
         elif dtype == kvd.KVD_BF16:
@@ -75,7 +81,7 @@ def test_plan_properties(lib, cache, forced):
         elif D < 128:
             assert variant == "lds"
         else:
-            assert variant == ("wave" if M <= (16 if D == 256 else 48) else "xchg")
+            assert variant == ("wave" if rows <= (16 if D == 256 else 48) else "xchg")
         tile = {"valu": 64, "xchg": 64}.get(variant, 32)
         n_tiles = -(-T_cap // tile)
         # whole tiles dealt round-robin: S splits, at most one per tile, the
