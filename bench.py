@@ -115,7 +115,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip measuring the other workloads (the 'extra' field)")
-    ap.add_argument("--extra-steps", type=int, default=30, help="steps per pass for each other workload")
+    ap.add_argument("--extra-steps", type=int, default=50, help="steps per pass for each other workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args(argv)
