@@ -357,8 +357,9 @@ int32_t kvdecode_status(kvdecode_t h, void* stream);
 /*
  * Force the split count of the attend pass (0 restores the automatic plan).
  * Each sequence's cache is cut into tiles of the partial kernel (32 tokens,
- * or 64 for the vector-ALU kernel) dealt round-robin to the splits: split s
- * owns tiles s, s+S, s+2S, ...  n is clamped to [1, ceil(T_cap / tile)].
+ * or 64 for the vector-ALU and fp8 exchange kernels) dealt round-robin to
+ * the splits: split s owns tiles s, s+S, s+2S, ...  n is clamped to
+ * [1, ceil(T_cap / tile)].
  * Used to check that results do not depend on the split.
  */
 int32_t kvdecode_set_num_splits(kvdecode_t h, int32_t n);
